@@ -1,0 +1,292 @@
+"""Plain, slow, fp64 CPU oracle of one MoE layer's forward pass.
+
+TEST INFRASTRUCTURE ONLY: imported by tests/, __graft_entry__.smoke() and the
+cpu_baseline leg of bench.py, never by the HIP product path, and it shares no
+code with it.  Every function works in float64 on the exact values that the
+device receives (bf16 inputs are widened, never re-rounded).
+
+Sources, cited by page title and section:
+  [RM]  "MoE routing math" (jerryiiii.gitbook.io, llm-review math dictionary)
+  [SA]  "Mixture of Experts architecture: how sparse activation reshapes the
+        efficiency and scale of LLMs" (x7peeps.com); its listings are named
+        by their function names (moe_forward, load_balancing_loss,
+        router_z_loss)
+  [DD]  "MoE deep dive: routing mechanisms and load balancing" (guijiagi.com)
+  [L17] "CMU 11-868 Lecture 17: Systems for Mixture-of-Experts Models"
+        (semidirectx.com notes)
+  [INF] "MoE inference optimisation, deep dive" (jerryiiii.gitbook.io notes)
+
+Readings where the pages are silent or disagree (each is listed in the design doc):
+  * top-k order: larger first; equal values go to the lower expert index.
+  * capacity: ceil(CF * T * k / E) evaluated exactly on the given CF value,
+    clamped to T; CF None or <= 0 means no limit (cap = T).
+  * overflow: within each expert the lowest token indices are kept.
+  * a dropped (token, choice) contributes zero and the surviving weights are
+    not renormalised.
+  * f_i is counted before the drop (sum_i f_i = k); N = T.
+  * SiLU(z) = z * sigmoid(z); W1 is the gated branch, W3 the linear one.
+"""
+from fractions import Fraction
+import math
+
+import numpy as np
+
+__all__ = [
+    "router_logits", "softmax", "logsumexp", "topk_experts",
+    "renormalise", "topk_softmax_weights", "route", "expert_counts",
+    "capacity", "dispatch", "silu", "swiglu_expert", "combine_grouped",
+    "combine_per_token", "load_balance_loss", "aux_stats", "layer_forward",
+]
+
+
+def _f64(a):
+    return np.asarray(a, dtype=np.float64)
+
+
+# ---------------------------------------------------------------- routing --
+
+def router_logits(x, w_gate):
+    """g = x . W_gate, W_gate in R^{d x E}, no bias.  [RM] section 2.1."""
+    return _f64(x) @ _f64(w_gate)
+
+
+def softmax(g):
+    """p = softmax(g) over the E routed experts.  [RM] section 2.1."""
+    g = _f64(g)
+    m = g.max(axis=-1, keepdims=True)
+    e = np.exp(g - m)
+    return e / e.sum(axis=-1, keepdims=True)
+
+
+def logsumexp(g):
+    """log sum_i exp(g_i), the quantity the z-loss squares.  [SA]
+    router_z_loss; [DD] section 3.2."""
+    g = _f64(g)
+    m = g.max(axis=-1)
+    return m + np.log(np.exp(g - m[..., None]).sum(axis=-1))
+
+
+def topk_experts(scores, k):
+    """S = TopK(scores, k) per row: indices of the k largest, larger first,
+    ties to the lower expert index.  [RM] section 2.1 (TopK over p)."""
+    scores = _f64(scores)
+    order = np.argsort(-scores, axis=-1, kind="stable")
+    return order[..., :k].astype(np.int64)
+
+
+def renormalise(p, idx):
+    """p~_i = p_i / sum_{j in S} p_j for i in S.  [RM] section 2.1."""
+    sel = np.take_along_axis(_f64(p), idx, axis=-1)
+    return sel / sel.sum(axis=-1, keepdims=True)
+
+
+def topk_softmax_weights(g, k):
+    """Second form of the same weights: take the k largest logits first, then
+    softmax over only those.  [SA] moe_forward steps 2-3; [DD] section 2.1
+    (TopKRouter); called top-k-softmax (Mixtral) in [L17] section 6."""
+    idx = topk_experts(g, k)
+    return idx, softmax(np.take_along_axis(_f64(g), idx, axis=-1))
+
+
+def route(x, w_gate, k):
+    """Router: logits, probabilities, top-k indices, renormalised weights and
+    the per-token log-sum-exp.  The top-k is taken over p as [RM] section 2.1
+    writes it."""
+    g = router_logits(x, w_gate)
+    p = softmax(g)
+    idx = topk_experts(p, k)
+    w = renormalise(p, idx)
+    return {"logits": g, "probs": p, "idx": idx, "weights": w,
+            "lse": logsumexp(g)}
+
+
+# --------------------------------------------------------------- dispatch --
+
+def expert_counts(idx, E):
+    """Number of (token, choice) pairs that picked each expert, before any
+    drop.  [SA] load_balancing_loss (the one-hot mask summed over tokens)."""
+    return np.bincount(np.asarray(idx).ravel(), minlength=E).astype(np.int64)
+
+
+def capacity(T, E, k, CF):
+    """capacity = ceil(cf * k * n / E), [L17] section 2.4, with n = T tokens,
+    evaluated exactly on the float value given.  A token picks an expert at
+    most once, so the result is clamped to T.  CF None or <= 0: no limit."""
+    if CF is None or CF <= 0:
+        return int(T)
+    c = Fraction(CF) * T * k / E
+    return int(min(T, math.ceil(c)))
+
+
+def dispatch(idx, E, cap):
+    """Group (token, choice) pairs by expert in token order and drop what
+    exceeds the capacity.  [L17] section 2.2 (group by expert), section 2.4
+    (overflow is dropped); [RM] section 4.3 (drop rate over pairs).
+
+    Returns slot (rank inside the expert's kept rows, -1 if dropped), the
+    drop mask, kept rows per expert, offsets (exclusive scan of kept),
+    row_of_pair (offsets[e] + slot, -1 if dropped) and token_of_row (the
+    inverse map, -1 past the last kept row; rows run over T*k slots)."""
+    idx = np.asarray(idx)
+    T, k = idx.shape
+    fill = [0] * E
+    slot = np.full((T, k), -1, dtype=np.int64)
+    drop = np.zeros((T, k), dtype=np.uint8)
+    for t in range(T):
+        for j in range(k):
+            e = int(idx[t, j])
+            if fill[e] < cap:
+                slot[t, j] = fill[e]
+                fill[e] += 1
+            else:
+                drop[t, j] = 1
+    kept = np.array(fill, dtype=np.int64)
+    offsets = np.zeros(E + 1, dtype=np.int64)
+    offsets[1:] = np.cumsum(kept)
+    row_of_pair = np.full((T, k), -1, dtype=np.int64)
+    token_of_row = np.full(T * k, -1, dtype=np.int64)
+    for t in range(T):
+        for j in range(k):
+            if not drop[t, j]:
+                r = offsets[idx[t, j]] + slot[t, j]
+                row_of_pair[t, j] = r
+                token_of_row[r] = t
+    return {"slot": slot, "drop": drop, "kept": kept, "offsets": offsets,
+            "row_of_pair": row_of_pair, "token_of_row": token_of_row}
+
+
+# ------------------------------------------------------------------ experts --
+
+def silu(z):
+    """SiLU(z) = z * sigmoid(z) = z / (1 + exp(-z))."""
+    z = _f64(z)
+    with np.errstate(over="ignore"):
+        return z / (1.0 + np.exp(-z))
+
+
+def swiglu_expert(xr, w1, w3, w2):
+    """FFN(x) = (SiLU(x W1) (*) x W3) W2, [L17] section 5.2.
+
+    Weights come in storage layout: w1, w3 [F, d] hold W1, W3 transposed and
+    w2 [d, F] holds W2 transposed."""
+    xr = _f64(xr)
+    a = xr @ _f64(w1).T
+    b = xr @ _f64(w3).T
+    return (silu(a) * b) @ _f64(w2).T
+
+
+def combine_grouped(x, weights, idx, disp, load_expert, E, tokens=None,
+                    shared_out=None):
+    """Grouped form: per expert, gather the kept rows, run the expert once on
+    all of them, and add p~-weighted results back in token order.
+    [L17] section 2.2 (group, one product per expert, index_add back).
+
+    tokens restricts the output to those token indices (others are not
+    computed); load_expert(e) -> (w1, w3, w2) in storage layout;
+    shared_out, if given, is added first (always-on shared experts,
+    [RM] section 2.2)."""
+    x = _f64(x)
+    T = x.shape[0]
+    tok = np.arange(T) if tokens is None else np.asarray(tokens)
+    pos = {int(t): i for i, t in enumerate(tok)}
+    y = np.zeros((len(tok), x.shape[1]))
+    if shared_out is not None:
+        y += _f64(shared_out)
+    kept = disp["drop"] == 0
+    for e in range(E):
+        sel = [(int(t), j) for t, j in zip(*np.nonzero((np.asarray(idx) == e) & kept))
+               if int(t) in pos]
+        if not sel:
+            continue
+        w1, w3, w2 = load_expert(e)
+        rows = np.array([t for t, _ in sel])
+        out = swiglu_expert(x[rows], w1, w3, w2)
+        for r, (t, j) in enumerate(sel):
+            y[pos[t]] += weights[t, j] * out[r]
+    return y
+
+
+def combine_per_token(x, weights, idx, disp, load_expert, tokens,
+                      shared_out=None):
+    """Per-token form: for each token, for each of its k choices, add
+    p~ * Expert(x) unless that pair was dropped.  [SA] moe_forward step 4;
+    [DD] section 4.3 (MoEWithSharedExpert: shared sum plus routed sum);
+    [L17] section 2.4 (a dropped pair adds nothing)."""
+    x = _f64(x)
+    tok = np.asarray(tokens)
+    y = np.zeros((len(tok), x.shape[1]))
+    if shared_out is not None:
+        y += _f64(shared_out)
+    for i, t in enumerate(tok):
+        for j in range(idx.shape[1]):
+            if disp["drop"][t, j]:
+                continue
+            w1, w3, w2 = load_expert(int(idx[t, j]))
+            y[i] += weights[t, j] * swiglu_expert(x[t:t + 1], w1, w3, w2)[0]
+    return y
+
+
+# --------------------------------------------------------------- statistics --
+
+def load_balance_loss(f, P):
+    """L_balance = E * sum_i f_i * P_i (alpha = 1).  [RM] section 3.2."""
+    f = _f64(f)
+    return float(f.shape[-1] * np.sum(f * _f64(P)))
+
+
+def aux_stats(logits, counts, T, k, cap):
+    """f_i, P_i, L_balance, z-loss and drop rate of one routed batch.
+
+    f_i = (1/N) sum_t 1[t routed to i] with N = T, counted before the drop
+    ([RM] section 3.2, so sum_i f_i = k); P_i = (1/N) sum_t p_{t,i};
+    z = mean_t (logsumexp_i g_{t,i})^2 ([SA] router_z_loss, [DD] section 3.2,
+    beta = 1); drop rate = dropped pairs / (T k) ([RM] section 4.3), where
+    expert i drops max(0, counts_i - cap)."""
+    g = _f64(logits)
+    counts = np.asarray(counts, dtype=np.int64)
+    f = counts / float(T)
+    P = softmax(g).sum(axis=0) / float(T)
+    lse = logsumexp(g)
+    z = float(np.mean(lse * lse))
+    dropped = int(np.maximum(counts - cap, 0).sum())
+    return {"f": f, "P": P, "L_balance": load_balance_loss(f, P),
+            "z_loss": z, "drop_rate": dropped / float(T * k)}
+
+
+# ---------------------------------------------------------------- the layer --
+
+def layer_forward(x, w_gate, k, CF, load_expert, E, E_shared=0,
+                  load_shared=None, tokens=None, mode="grouped"):
+    """Whole forward of one MoE layer, the order the pages give:
+    route ([RM] 2.1) -> count and capacity-clip ([L17] 2.2, 2.4) ->
+    experts and weighted sum plus always-on shared experts ([RM] 2.2,
+    [L17] 5.2) -> statistics ([RM] 3.2, 4.3; [SA] router_z_loss).
+
+    tokens: optional subset of token indices whose outputs are computed
+    (routing, dispatch and statistics always cover all T tokens)."""
+    x = _f64(x)
+    T = x.shape[0]
+    r = route(x, w_gate, k)
+    counts = expert_counts(r["idx"], E)
+    cap = capacity(T, E, k, CF)
+    disp = dispatch(r["idx"], E, cap)
+    tok = np.arange(T) if tokens is None else np.asarray(tokens)
+    shared = None
+    if E_shared:
+        shared = np.zeros((len(tok), x.shape[1]))
+        for s in range(E_shared):
+            w1, w3, w2 = load_shared(s)
+            shared += swiglu_expert(x[tok], w1, w3, w2)
+    if mode == "grouped":
+        y = combine_grouped(x, r["weights"], r["idx"], disp, load_expert, E,
+                            tokens=tok, shared_out=shared)
+    elif mode == "per_token":
+        y = combine_per_token(x, r["weights"], r["idx"], disp, load_expert,
+                              tok, shared_out=shared)
+    else:
+        raise ValueError(mode)
+    stats = aux_stats(r["logits"], counts, T, k, cap)
+    out = dict(r)
+    out.update(counts=counts, cap=cap, y=y, tokens=tok, **disp)
+    out.update(stats)
+    return out
