@@ -1,0 +1,221 @@
+"""Throughput of the MoE-layer forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+One step is one pass of the whole layer (moe_route, moe_permute,
+moe_expert_ffn, moe_combine, moe_aux_stats) over one batch of seeded
+synthetic input already resident in HBM.  Prints one JSON line with the
+whole-job tokens/s, the roofline of the grouped expert GEMM call (timed
+with HIP events on the launch stream) and the CPU oracle timed on a
+bounded token sample of the same workload.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import top_routing_expert_softmax_amd as M  # noqa: E402
+from workloads import CONFIGS, expert_stack, router_inputs, storage_bits  # noqa: E402
+
+METRIC = "MoE-layer fwd tokens/s; % MFMA peak (prefill) / % HBM BW (decode)"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3        # MI355X fp32 vector
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def to_dev(a):
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).to("cuda").view(torch.bfloat16)
+    return torch.from_numpy(a).to("cuda")
+
+
+def build_inputs(cfg):
+    """Generate on the host, upload; the host copies of the expert stacks are
+    kept for the CPU baseline."""
+    x, wg = router_inputs(cfg)
+    dev = {"x": to_dev(storage_bits(cfg, x)), "wg": to_dev(storage_bits(cfg, wg))}
+    host = {}
+    kinds = ["w1", "w3", "w2"] + (["ws1", "ws3", "ws2"] if cfg.E_shared else [])
+    for kind in kinds:
+        host[kind] = expert_stack(cfg, kind, bits=True)
+        dev[kind] = to_dev(host[kind])
+    return x, wg, dev, host
+
+
+def gemm_work(cfg, counts_np, cap):
+    """Algorithmic work of one moe_expert_ffn call: flop = 6 d F per kept
+    routed row + 6 d F T per shared expert; bytes = weights of touched
+    experts (routed with >=1 kept row, plus shared) read once + activations
+    in/out."""
+    kept = np.minimum(counts_np, cap)
+    rows = int(kept.sum()) + cfg.E_shared * cfg.T
+    flop = 6.0 * cfg.d_model * cfg.d_ff * rows
+    eb = cfg.bytes_per_el
+    touched = int((kept > 0).sum()) + cfg.E_shared
+    wbytes = touched * 3.0 * cfg.d_model * cfg.d_ff * eb
+    abytes = rows * cfg.d_model * eb * 2           # rows in, rows out
+    return flop, wbytes + abytes, touched, rows
+
+
+def cpu_baseline(cfg, x, wg, host, sample_tokens):
+    """The oracle, as it stands, on a bounded sample: routing, dispatch and
+    statistics over all T tokens plus the expert outputs of the sampled
+    tokens.  Returns tokens/s of the sample and the thread count."""
+    from oracle import moe_oracle as O
+    from workloads import bf16_bits_to_f32
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    rng = np.random.default_rng(0)
+    tokens = np.sort(rng.choice(cfg.T, size=min(sample_tokens, cfg.T), replace=False))
+
+    def vals(a):
+        return bf16_bits_to_f32(a) if a.dtype == np.uint16 else a
+
+    def load(e):
+        return tuple(vals(host[kk][e]) for kk in ("w1", "w3", "w2"))
+
+    def load_s(s):
+        return tuple(vals(host[kk][s]) for kk in ("ws1", "ws3", "ws2"))
+    # the weight values (the same bits the GPU holds) are prepared outside
+    # the timed region
+    r = O.route(x, wg, cfg.k)
+    need = sorted(set(int(e) for e in r["idx"][tokens].ravel()))
+    cache = {e: load(e) for e in need}
+    cache_s = {s: load_s(s) for s in range(cfg.E_shared)}
+    t0 = time.perf_counter()
+    O.layer_forward(x, wg, cfg.k, cfg.CF, lambda e: cache[e], cfg.E, cfg.E_shared,
+                    lambda s: cache_s[s], tokens=tokens)
+    dt = time.perf_counter() - t0
+    return len(tokens) / dt, threads, len(tokens), dt
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="mixtral_prefill", choices=sorted(CONFIGS))
+    ap.add_argument("--cpu-sample", type=int, default=48,
+                    help="tokens whose expert outputs the oracle computes")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(see DESIGN.md for how the layer would shard).", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    M.lib()
+    cfg = CONFIGS[args.workload]
+    t = time.time()
+    x, wg, dev, host = build_inputs(cfg)
+    log(f"inputs for {cfg.name} on the device in {time.time() - t:.1f}s")
+    T, d, E, Es, k, F = cfg.T, cfg.d_model, cfg.E, cfg.E_shared, cfg.k, cfg.d_ff
+    dtype = dev["x"].dtype
+    b = M.MoELayerBuffers(T, d, E, Es, k, F, dtype)
+    stream = torch.cuda.current_stream()
+    names = ["route", "permute", "expert_ffn", "combine", "aux_stats"]
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+
+    def step(timed):
+        if timed:
+            ev[0].record(stream)
+        M.moe_route(dev["x"], dev["wg"], k, b.logits, b.topk_idx, b.topk_w, stream)
+        if timed:
+            ev[1].record(stream)
+        M.moe_permute(b.topk_idx, dev["x"], E, cfg.CF, b.counts, b.offsets, b.token_of_row,
+                      b.row_of_pair, b.drop_mask, b.x_perm, b.ws, stream)
+        if timed:
+            ev[2].record(stream)
+        M.moe_expert_ffn(T, k, b.x_perm, b.offsets, dev["x"], dev["w1"], dev["w3"], dev["w2"],
+                         dev.get("ws1"), dev.get("ws3"), dev.get("ws2"), b.y_perm, b.y_shared,
+                         b.ws, stream)
+        if timed:
+            ev[3].record(stream)
+        M.moe_combine(b.y_perm, b.y_shared, b.row_of_pair, b.topk_w, b.y, stream)
+        if timed:
+            ev[4].record(stream)
+        M.moe_aux_stats(b.logits, b.counts, k, cfg.CF, b.f, b.P, b.scalars, b.ws, stream)
+        if timed:
+            ev[5].record(stream)
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    # Per-call durations: events on the launch stream, one timed pass each.
+    per_call = np.zeros(len(names))
+    for _ in range(args.steps):
+        step(True)
+        torch.cuda.synchronize()
+        per_call += np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(len(names))])
+    per_call /= args.steps
+    # Whole-job timing: K back-to-back steps bracketed by synchronisation.
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(False)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms = elapsed * 1e3 / args.steps
+    tokens_per_s = T / (ms / 1e3)
+
+    counts = b.counts.cpu().numpy()
+    cap = M.moe_capacity(T, E, k, cfg.CF)
+    flop, bytes_alg, touched, rows = gemm_work(cfg, counts, cap)
+    ffn_ms = float(per_call[names.index("expert_ffn")])
+    if cfg.T <= 256:      # decode-shaped: weight streaming, HBM-bound
+        achieved = bytes_alg / (ffn_ms / 1e3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None}
+    else:
+        peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
+        achieved = flop / (ffn_ms / 1e3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak,
+                "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None}
+    roof["kernel"] = "moe_expert_ffn (grouped GEMM phase 1 + phase 2 + tile table)"
+    roof["kernel_ms"] = round(ffn_ms, 4)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a token sample")
+        v, threads, n, dt = cpu_baseline(cfg, x, wg, host, args.cpu_sample)
+        cpu = {"value": round(v, 3), "unit": "tokens/s", "cores": int(threads),
+               "kind": "oracle",
+               "sample": f"{n} of {T} tokens' expert outputs (routing, dispatch and "
+                         f"statistics over all {T}); {dt:.1f}s"}
+
+    out = {
+        "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16" if cfg.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded; inputs resident in HBM)",
+        "config": {"workload": cfg.name, "T": T, "d_model": d, "E": E, "E_shared": Es,
+                   "k": k, "d_ff": F, "CF": cfg.CF, "kept_rows": rows,
+                   "experts_touched": touched},
+        "breakdown_ms": {n: round(float(v), 4) for n, v in zip(names, per_call)},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,192 @@
+/*
+ * moe.h - C ABI of the MI355X (gfx950) forward pass of one Mixture-of-Experts
+ * layer with softmax top-k routing.
+ *
+ * The layer, in the notation of the pages it follows:
+ *   g = x W_gate                                  ("MoE routing math", sec. 2.1)
+ *   p = softmax(g);  S = TopK(p, k);  p~_i = p_i / sum_{j in S} p_j   (sec. 2.1)
+ *   capacity = ceil(CF * k * T / E), overflow dropped
+ *                         ("CMU 11-868 Lecture 17: Systems for MoE Models", 2.4)
+ *   group (token, choice) pairs by expert, one product per expert     (L17, 2.2)
+ *   Expert(x) = (SiLU(x W1) (*) x W3) W2                              (L17, 5.2)
+ *   y = sum_s Shared_s(x) + sum_{i in S, kept} p~_i Expert_i(x)
+ *                                            ("MoE routing math", sec. 2.2)
+ *   f_i, P_i, L_balance = E sum_i f_i P_i    ("MoE routing math", sec. 3.2)
+ *   z = mean_t (logsumexp_i g_ti)^2          ("MoE deep dive: routing and
+ *                                              load balancing", sec. 3.2)
+ *
+ * Notation: T tokens, d = d_model, E routed experts, E_shared always-on
+ * shared experts, k experts per token, F = d_ff, CF capacity factor.
+ *
+ * Conventions for every entry point
+ *   - All tensor arguments are DEVICE pointers, row-major and contiguous,
+ *     16-byte aligned.  The caller owns every buffer; the library never
+ *     allocates, frees or keeps a pointer after the call returns, and it has
+ *     no mutable global state: calls are re-entrant.
+ *   - dtype selects activations AND weights: MOE_F32 (fp32) or MOE_BF16
+ *     (bf16 storage).  Accumulation is always fp32.  Router logits,
+ *     weights and statistics are fp32 (scalars fp64) for both dtypes.
+ *   - stream is a hipStream_t passed as void* (NULL = the null stream).  All
+ *     device work is enqueued on it; outputs are valid once the caller has
+ *     synchronised the stream.  No call waits on the device.
+ *   - Arguments are checked on the host before anything is launched.  On
+ *     error nothing is launched and a negative MOE_E* code is returned;
+ *     moe_last_error() then describes it (per calling thread).  A device
+ *     fault surfaces at the caller's next synchronisation as a HIP error.
+ *   - Limits: 1 <= k <= E <= 256; 0 <= E_shared <= 16; 1 <= T; T*k < 2^31;
+ *     d_model and d_ff multiples of 64 (bf16) or of 4 (fp32).
+ *
+ * Weight layouts (each stored row is one output feature's weights along
+ * the contracted dimension, the [out, in] layout of a linear layer):
+ *   w_gate [d, E]          the pages' W_gate in R^{d x E}
+ *   w1, w3 [E, F, d]       w1[e][f][i] = W1_e[i][f]  (W1_e in R^{d x F})
+ *   w2     [E, d, F]       w2[e][i][f] = W2_e[f][i]  (W2_e in R^{F x d})
+ *   ws1, ws3 [E_shared, F, d];  ws2 [E_shared, d, F]   same, shared experts
+ */
+#ifndef MOE_H_
+#define MOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  MOE_OK = 0,
+  MOE_EINVAL = -1,       /* bad argument: null, misaligned, out of range */
+  MOE_EUNSUPPORTED = -2, /* a dtype or shape with no kernel */
+  MOE_EHIP = -3,         /* a HIP launch or query failed (message kept) */
+  MOE_EWORKSPACE = -4    /* workspace smaller than moe_workspace_size() */
+};
+
+enum { MOE_F32 = 0, MOE_BF16 = 1 };
+
+/* Static description of a status code. */
+const char* moe_strerror(int status);
+
+/* Message of the last failing call made by this thread ("" if none). */
+const char* moe_last_error(void);
+
+/*
+ * Expert capacity, "CMU 11-868 Lecture 17", section 2.4:
+ *   cap = min(T, ceil(CF * k * T / E)),
+ * evaluated exactly on the double value CF (no rounding of the product).
+ * A token picks an expert at most once, hence the clamp to T.  CF <= 0
+ * means no capacity limit (cap = T).  Host only.  Returns MOE_OK and
+ * writes *cap, or MOE_EINVAL.
+ */
+int moe_capacity(int64_t T, int32_t E, int32_t k, double CF, int64_t* cap);
+
+/*
+ * Bytes of device workspace that moe_permute, moe_expert_ffn and
+ * moe_aux_stats need for this shape (one buffer serves all three; calls on
+ * one stream may share it).  Host only.
+ */
+int moe_workspace_size(int64_t T, int64_t d_model, int32_t E, int32_t E_shared,
+                       int32_t k, int64_t d_ff, int32_t dtype, size_t* bytes);
+
+/*
+ * Router, "MoE routing math" section 2.1: logits g = x W_gate, softmax,
+ * top-k and renormalisation.  (The pages also write the weights as a
+ * softmax over only the k largest logits; the two are equal.)
+ *   x       [T, d]  dtype            in
+ *   w_gate  [d, E]  dtype            in
+ *   logits  [T, E]  fp32             out  exact when x and W_gate lie on a
+ *                                         common dyadic grid whose integer
+ *                                         partial sums stay below 2^24
+ *   topk_idx[T, k]  int32            out  expert ids, larger logit first,
+ *                                         ties to the lower expert id
+ *   topk_w  [T, k]  fp32             out  renormalised weights p~ (sum 1)
+ */
+int moe_route(int64_t T, int64_t d_model, int32_t E, int32_t k, int32_t dtype,
+              const void* x, const void* w_gate, float* logits,
+              int32_t* topk_idx, float* topk_w, void* stream);
+
+/*
+ * Counting, capacity, drop and permutation, "CMU 11-868 Lecture 17"
+ * sections 2.2 (group by expert) and 2.4 (capacity, overflow dropped).
+ * Pairs (t, j) are ranked inside their expert in token order; a pair is
+ * kept iff its rank < cap = moe_capacity(T, E, k, CF).
+ *   topk_idx     [T, k]     int32   in
+ *   x            [T, d]     dtype   in
+ *   counts       [E]        int32   out  pairs per expert before the drop
+ *   offsets      [E + 1]    int32   out  exclusive scan of min(counts, cap);
+ *                                        offsets[E] = R, the kept rows
+ *   token_of_row [T * k]    int32   out  token of each kept row, -1 past R
+ *   row_of_pair  [T, k]     int32   out  row of pair (t, j), -1 if dropped
+ *   drop_mask    [T, k]     uint8   out  1 if pair (t, j) was dropped
+ *   x_perm       [T * k, d] dtype   out  rows 0..R-1 = x[token_of_row[r]];
+ *                                        rows >= R are not written
+ * Rows are sorted by (expert, token).  Needs ws of moe_workspace_size().
+ */
+int moe_permute(int64_t T, int64_t d_model, int32_t E, int32_t k, double CF,
+                int32_t dtype, const int32_t* topk_idx, const void* x,
+                int32_t* counts, int32_t* offsets, int32_t* token_of_row,
+                int32_t* row_of_pair, uint8_t* drop_mask, void* x_perm,
+                void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Grouped expert FFN, "CMU 11-868 Lecture 17" sections 2.2 and 5.2: for
+ * each routed expert e, its kept rows x_perm[offsets[e] .. offsets[e+1])
+ * go through (SiLU(X W1_e) (*) X W3_e) W2_e; each shared expert s
+ * ("MoE routing math" section 2.2) takes all T rows of x.
+ *   x_perm   [T * k, d]        dtype  in   (rows past offsets[E] unread)
+ *   offsets  [E + 1]           int32  in   (from moe_permute)
+ *   x        [T, d]            dtype  in   (read only if E_shared > 0)
+ *   w1, w3   [E, F, d]; w2 [E, d, F]              dtype in
+ *   ws1, ws3 [E_shared, F, d]; ws2 [E_shared, d, F] dtype in (NULL if
+ *                                                  E_shared == 0)
+ *   y_perm   [T * k, d]        dtype  out  row r = Expert(x_perm[r]) for
+ *                                          r < offsets[E]; others unwritten
+ *   y_shared [E_shared, T, d]  dtype  out  (NULL if E_shared == 0)
+ * The SiLU-gated intermediate is kept in ws, rounded to dtype.
+ */
+int moe_expert_ffn(int64_t T, int64_t d_model, int32_t E, int32_t E_shared,
+                   int32_t k, int64_t d_ff, int32_t dtype, const void* x_perm,
+                   const int32_t* offsets, const void* x, const void* w1,
+                   const void* w3, const void* w2, const void* ws1,
+                   const void* ws3, const void* ws2, void* y_perm,
+                   void* y_shared, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Weighted combine back to token order, "CMU 11-868 Lecture 17" section 2.2
+ * (add back with the weights) and "MoE routing math" section 2.2 (shared
+ * experts with weight 1):
+ *   y[t] = sum_s y_shared[s][t] + sum_{j : row_of_pair[t][j] >= 0}
+ *          topk_w[t][j] * y_perm[row_of_pair[t][j]]
+ * A dropped pair adds nothing; the surviving weights are not renormalised.
+ * Summation in fp32: shared experts first, then j = 0..k-1.
+ *   y_perm [T*k, d] dtype in; y_shared [E_shared, T, d] dtype in (NULL if
+ *   E_shared == 0); row_of_pair [T, k] int32 in; topk_w [T, k] fp32 in;
+ *   y [T, d] dtype out.
+ */
+int moe_combine(int64_t T, int64_t d_model, int32_t E_shared, int32_t k,
+                int32_t dtype, const void* y_perm, const void* y_shared,
+                const int32_t* row_of_pair, const float* topk_w, void* y,
+                void* stream);
+
+/*
+ * Load-balance statistics, "MoE routing math" sections 3.2 and 4.3, and the
+ * router z-loss ("MoE deep dive" section 3.2), unscaled (alpha = beta = 1):
+ *   f[i] = counts[i] / T   (before the drop, so sum_i f_i = k)
+ *   P[i] = (1/T) sum_t softmax(logits[t])[i]
+ *   scalars[0] = L_balance = E * sum_i f_i * P_i
+ *   scalars[1] = z_loss    = (1/T) sum_t (logsumexp_i logits[t][i])^2
+ *   scalars[2] = drop_rate = sum_i max(0, counts[i] - cap) / (T * k)
+ * with cap = moe_capacity(T, E, k, CF).  Sums run in a fixed order (the
+ * result is deterministic) and in fp64.
+ *   logits [T, E] fp32 in; counts [E] int32 in; f, P [E] fp32 out;
+ *   scalars [3] fp64 out (device memory).  Needs ws.
+ */
+int moe_aux_stats(int64_t T, int32_t E, int32_t k, double CF,
+                  const float* logits, const int32_t* counts, float* f,
+                  float* P, double* scalars, void* ws, size_t ws_bytes,
+                  void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H_ */

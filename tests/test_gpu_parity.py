@@ -1,0 +1,132 @@
+"""GPU parity: the HIP layer (through the C ABI) against the fp64 oracle.
+
+Integer outputs (top-k ids, counts, offsets, permutation, drop mask) and the
+logits must match bit for bit; weights within 2e-6; y within the bounds the
+layer promises (fp32: max error <= 1e-4 max|ref|; bf16: max error <= 2e-2
+max|ref| and sum|err|/sum|ref| <= 5e-3); statistics within 1e-5 relative.
+"""
+import numpy as np
+import pytest
+import torch
+
+from workloads import get_config
+
+pytestmark = pytest.mark.gpu
+
+import gpu_harness as H  # noqa: E402
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import top_routing_expert_softmax_amd as M
+    M.lib()      # raises if the HIP library is missing: no silent fallback
+
+
+def _full_check(cfg, label):
+    H.log(f"case {label}: {cfg}")
+    inp = H.LayerInputs(cfg)
+    g = H.host(H.run_gpu(inp))
+    r, counts, cap, disp, stats = H.oracle_routing(inp)
+    H.check_routing(g, r, counts, disp)
+    ref = H.oracle_y(inp, r, disp, np.arange(cfg.T))
+    mx, mr = H.check_y(cfg, g["y"], ref)
+    H.check_stats(g, stats)
+    H.log(f"case {label}: R={g['R']} drop={stats['drop_rate']:.4f} max_err={mx:.2e} mean_rel={mr:.2e}")
+
+
+SMALL_CASES = {
+    # name: (base config, overrides)
+    "tiny_f32": ("tiny_f32", {}),
+    "f32_ragged": ("tiny_f32", dict(T=200, d_model=192, E=5, k=2, d_ff=320, CF=1.0, E_shared=1)),
+    "bf16_ragged_shared": ("dsmoe16b_prefill", dict(T=300, d_model=192, E=6, E_shared=1, k=2,
+                                                     d_ff=320, CF=1.0)),
+    "bf16_multi_tile": ("mixtral_prefill", dict(T=700, d_model=256, E=4, k=2, d_ff=512,
+                                                CF=1.25)),
+    "bf16_two_shared_k6": ("dsmoe16b_prefill", dict(T=260, d_model=128, E=16, E_shared=2, k=6,
+                                                    d_ff=192, CF=1.25)),
+    "bf16_T1": ("dsv3_decode", dict(T=1, d_model=256, E=32, E_shared=1, k=8, d_ff=128)),
+    "bf16_E1_k1": ("mixtral_prefill", dict(T=150, d_model=128, E=1, k=1, d_ff=128, CF=None)),
+    "bf16_empty_experts": ("dsv3_decode", dict(T=5, d_model=128, E=64, E_shared=0, k=2,
+                                               d_ff=128)),
+    "bf16_skew_drop": ("skewed_train", dict(T=1024, d_model=256, E=8, k=2, d_ff=256, CF=1.0,
+                                            zipf_tau=1.0)),
+    "bf16_E256_decode_small": ("dsv3_decode", dict(T=64, d_model=512, d_ff=256)),
+}
+
+
+@pytest.mark.parametrize("label", list(SMALL_CASES))
+def test_small_layer_matches_oracle(label):
+    base, over = SMALL_CASES[label]
+    _full_check(get_config(base, **over), label)
+
+
+def test_all_equal_logits_route_to_the_first_k_and_drop():
+    """W_gate = 0: every logit is 0, so every token picks experts 0..k-1 and
+    capacity drops all but the first cap tokens of each."""
+    import top_routing_expert_softmax_amd as M
+    from oracle import moe_oracle as O
+    cfg = get_config("mixtral_prefill", T=256, d_model=128, E=8, k=2, d_ff=128, CF=1.0)
+    inp = H.LayerInputs(cfg)
+    inp.wg[:] = 0.0
+    inp.wg_dev.zero_()
+    g = H.host(H.run_gpu(inp))
+    r, counts, cap, disp, stats = H.oracle_routing(inp)
+    assert np.all(g["topk_idx"] == np.arange(2)[None, :])
+    H.check_routing(g, r, counts, disp)
+    assert g["drop_mask"][:cap].sum() == 0 and g["drop_mask"][cap:].all()
+    H.check_stats(g, stats)
+    ref = H.oracle_y(inp, r, disp, np.arange(cfg.T))
+    H.check_y(cfg, g["y"], ref)
+    assert M  # loaded
+
+
+def test_x_perm_is_exact_copy_and_runs_are_deterministic():
+    cfg = get_config("dsmoe16b_prefill", T=512, d_model=256, E=16, E_shared=2, k=4, d_ff=256,
+                     CF=1.0)
+    inp = H.LayerInputs(cfg)
+    b = H.run_gpu(inp)
+    R = int(b.offsets[-1].item())
+    tor = b.token_of_row[:R].long()
+    assert torch.equal(b.x_perm[:R], inp.x_dev[tor])
+    first = {n: getattr(b, n).clone() for n in ("logits", "topk_idx", "topk_w", "row_of_pair",
+                                                "y", "y_perm", "f", "P", "scalars")}
+    b2 = H.run_gpu(inp, bufs=b)
+    for n, v in first.items():
+        assert torch.equal(getattr(b2, n), v), f"{n} differs between runs"
+
+
+FULL = ["mixtral_prefill", "dsv3_decode", "dsmoe16b_prefill", "skewed_train"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_config(name):
+    """Full configuration in the launch configuration the benchmark times:
+    routing, permutation and statistics checked in full, y on sampled tokens
+    (all tokens for the 64-token decode step), including dropped ones."""
+    cfg = get_config(name)
+    H.log(f"full config {name}")
+    inp = H.LayerInputs(cfg)
+    b = H.run_gpu(inp)
+    g = H.host(b)
+    r, counts, cap, disp, stats = H.oracle_routing(inp)
+    H.check_routing(g, r, counts, disp)
+    H.check_stats(g, stats)
+    R = g["R"]
+    tor = b.token_of_row[:R].long()
+    assert torch.equal(b.x_perm[:R], inp.x_dev[tor])
+    del b
+    if cfg.T <= 64:
+        tokens = np.arange(cfg.T)
+    else:
+        rng = np.random.default_rng(cfg.seed)
+        dropped = np.nonzero(disp["drop"].any(axis=1))[0]
+        pick = list(rng.choice(cfg.T, size=24, replace=False))
+        if len(dropped):
+            pick += list(rng.choice(dropped, size=min(8, len(dropped)), replace=False))
+        tokens = np.unique(np.array(pick + [0, cfg.T - 1]))
+    H.log(f"oracle on {len(tokens)} tokens")
+    ref = H.oracle_y(inp, r, disp, tokens)
+    mx, mr = H.check_y(cfg, g["y"][tokens], ref)
+    H.log(f"{name}: R={R} drop={stats['drop_rate']:.4f} max_err={mx:.2e} mean_rel={mr:.2e}")

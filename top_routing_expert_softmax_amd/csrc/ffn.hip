@@ -1,0 +1,402 @@
+// Grouped expert FFN over ragged expert segments: "CMU 11-868 Lecture 17"
+// section 2.2 (one product per expert on its gathered rows) and section 5.2
+// (SwiGLU expert: (SiLU(x W1) (*) x W3) W2), plus the always-on shared
+// experts of "MoE routing math" section 2.2, which run as full-T segments.
+//
+// Segments: routed expert e owns rows offsets[e] .. offsets[e+1] of x_perm
+// (and of H and y_perm); shared expert s owns rows 0..T-1 of x, rows
+// T*k + s*T + m of H and rows s*T + m of y_shared.  A one-block prep kernel
+// cuts every segment into BM-row tiles on the device (no host sync: grids
+// are sized for the worst case and idle blocks exit).
+//
+// Phase 1: H = SiLU(A W1^T) (*) (A W3^T), both products of one column tile
+//          in the same block so the gate epilogue is fused; H rounded to
+//          the layer dtype.
+// Phase 2: Y = H W2^T.
+// Both operands are K-contiguous in memory ([rows][K] activations and
+// [out][in] weights), which is the layout bf16 MFMA operands want.
+//
+// bf16: v_mfma_f32_32x32x16_bf16, fp32 accumulators.  Block = 256 threads
+// (4 wavefronts as 2 x 2), tile BM x 128 B-rows x BK=64, LDS rows padded by
+// 16 bytes so the 16-byte fragment reads of 8 consecutive rows fall in
+// distinct banks.  fp32 (small configs): VALU tiles, correctness path.
+#include <math.h>
+
+#include "moe_device.h"
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+constexpr int kBM = 128;        // rows per tile (bf16 path)
+constexpr int kBMf = 64;        // rows per tile (fp32 path)
+constexpr int kBK = 64;
+constexpr int kLdsStride = kBK + 8;   // bf16 elements per LDS row
+constexpr int kThreads = 256;
+
+struct FfnArgs {
+  const void* x_perm;
+  const void* x;
+  const int32_t* offsets;
+  const void* w1;
+  const void* w3;
+  const void* w2;
+  const void* ws1;
+  const void* ws3;
+  const void* ws2;
+  void* H;
+  void* y_perm;
+  void* y_shared;
+  const int4* tiles;     // (segment, A row, rows, H row)
+  const int* ntiles;
+  int T, d, E, Es, k, F;
+};
+
+// ---------------------------------------------------------------- tiling --
+
+__global__ __launch_bounds__(kWave) void tile_table_kernel(const int32_t* __restrict__ offsets,
+                                                          int4* __restrict__ tiles,
+                                                          int* __restrict__ ntiles, int E,
+                                                          int Es, int T, int k, int BM) {
+  // One wavefront; each lane owns up to 5 segments (E + Es <= 272 < 320).
+  const int lane = threadIdx.x;
+  const int nseg = E + Es;
+  int cnt[5];
+  int tot = 0;
+#pragma unroll
+  for (int q = 0; q < 5; ++q) {
+    const int s = lane * 5 + q;
+    int rows = 0;
+    if (s < E) rows = offsets[s + 1] - offsets[s];
+    else if (s < nseg) rows = T;
+    cnt[q] = (rows + BM - 1) / BM;
+    tot += cnt[q];
+  }
+  int incl = tot;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int n = __shfl_up(incl, off, kWave);
+    if (lane >= off) incl += n;
+  }
+  int base = incl - tot;
+#pragma unroll
+  for (int q = 0; q < 5; ++q) {
+    const int s = lane * 5 + q;
+    for (int i = 0; i < cnt[q]; ++i) {
+      int4 t;
+      t.x = s;
+      if (s < E) {
+        const int r0 = offsets[s] + i * BM;
+        t.y = r0;
+        t.z = min(BM, offsets[s + 1] - r0);
+        t.w = r0;
+      } else {
+        const int m0 = i * BM;
+        t.y = m0;
+        t.z = min(BM, T - m0);
+        t.w = T * k + (s - E) * T + m0;
+      }
+      tiles[base + i] = t;
+    }
+    base += cnt[q];
+  }
+  if (lane == kWave - 1) *ntiles = incl;
+}
+
+// ------------------------------------------------------------- bf16 MFMA --
+
+__device__ __forceinline__ float silu_f(float g) { return g / (1.0f + __expf(-g)); }
+
+template <int PHASE>
+__global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(FfnArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t As[kBM * kLdsStride];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[128 * kLdsStride];
+
+  if (static_cast<int>(blockIdx.x) >= *a.ntiles) return;
+  const int4 tl = a.tiles[blockIdx.x];
+  const int seg = tl.x, arow0 = tl.y, mrows = tl.z, hrow0 = tl.w;
+  const bool routed = seg < a.E;
+  const int e = routed ? seg : seg - a.E;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const int wm = wave >> 1, wn = wave & 1;
+
+  // Problem geometry of this phase.
+  const int K = PHASE == 1 ? a.d : a.F;
+  const int N = PHASE == 1 ? a.F : a.d;          // output columns
+  const int n0 = blockIdx.y * (PHASE == 1 ? 64 : 128);
+  const uint16_t* A;
+  if (PHASE == 1) {
+    A = static_cast<const uint16_t*>(routed ? a.x_perm : a.x) + static_cast<int64_t>(arow0) * K;
+  } else {
+    A = static_cast<const uint16_t*>(a.H) + static_cast<int64_t>(hrow0) * K;
+  }
+  const int64_t wstride = static_cast<int64_t>(a.F) * a.d;   // elements per expert matrix
+
+  // Each thread moves 4 A chunks and 4 B chunks of 16 bytes per K step.
+  // Rows outside the segment (A) or past N (B) read a clamped, valid row
+  // and are zeroed by the mask, so every load is unconditional.
+  const int kc = tid & 7;
+  const uint16_t* a_src[4];
+  const uint16_t* b_src[4];
+  uint32_t valid = 0;     // bit q: A row valid; bit 4+q: B row valid
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int r = (tid >> 3) + 32 * q;      // tile row 0..127
+    const bool av = r < mrows;
+    a_src[q] = A + static_cast<int64_t>(av ? r : 0) * K + kc * 8;
+    int col;
+    const uint16_t* W;
+    if (PHASE == 1) {
+      col = n0 + (r & 63);
+      W = static_cast<const uint16_t*>(r < 64 ? (routed ? a.w1 : a.ws1) : (routed ? a.w3 : a.ws3));
+    } else {
+      col = n0 + r;
+      W = static_cast<const uint16_t*>(routed ? a.w2 : a.ws2);
+    }
+    const bool bv = col < N;
+    b_src[q] = W + e * wstride + static_cast<int64_t>(bv ? col : N - 1) * K + kc * 8;
+    valid |= (av ? 1u : 0u) << q;
+    valid |= (bv ? 1u : 0u) << (4 + q);
+  }
+
+  f32x16_t acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+
+  u32x4_t ra[4], rb[4];
+  const u32x4_t zero = {0u, 0u, 0u, 0u};
+#define MOE_LOAD_TILE(k0)                                                          \
+  _Pragma("unroll") for (int q = 0; q < 4; ++q) {                                  \
+    const u32x4_t va = *reinterpret_cast<const u32x4_t*>(a_src[q] + (k0));        \
+    const u32x4_t vb = *reinterpret_cast<const u32x4_t*>(b_src[q] + (k0));        \
+    ra[q] = ((valid >> q) & 1u) ? va : zero;                                       \
+    rb[q] = ((valid >> (4 + q)) & 1u) ? vb : zero;                                 \
+  }
+
+  const int nk = K / kBK;
+  MOE_LOAD_TILE(0);
+  for (int kt = 0; kt < nk; ++kt) {
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int r = (tid >> 3) + 32 * q;
+      *reinterpret_cast<u32x4_t*>(&As[r * kLdsStride + kc * 8]) = ra[q];
+      *reinterpret_cast<u32x4_t*>(&Bs[r * kLdsStride + kc * 8]) = rb[q];
+    }
+    __syncthreads();
+    if (kt + 1 < nk) { MOE_LOAD_TILE((kt + 1) * kBK); }
+#pragma unroll
+    for (int ks = 0; ks < kBK / 16; ++ks) {
+      const int kk = ks * 16 + (lane >> 5) * 8;
+      bf16x8_t fa[2], fb[2];
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi) {
+        const int r = wm * 64 + mi * 32 + (lane & 31);
+        fa[mi] = *reinterpret_cast<const bf16x8_t*>(&As[r * kLdsStride + kk]);
+      }
+#pragma unroll
+      for (int ni = 0; ni < 2; ++ni) {
+        const int r = PHASE == 1 ? (ni * 64 + wn * 32 + (lane & 31)) : (wn * 64 + ni * 32 + (lane & 31));
+        fb[ni] = *reinterpret_cast<const bf16x8_t*>(&Bs[r * kLdsStride + kk]);
+      }
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni)
+          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[mi], fb[ni], acc[mi][ni], 0, 0, 0);
+    }
+  }
+
+#undef MOE_LOAD_TILE
+  // Epilogue.  32x32 accumulator layout: element v of lane l is row
+  // 8*(v/4) + 4*(l/32) + v%4, column l%32.
+  if (PHASE == 1) {
+    uint16_t* Hout = static_cast<uint16_t*>(a.H) + static_cast<int64_t>(hrow0) * a.F;
+    const int col = n0 + wn * 32 + (lane & 31);
+    if (col < N) {
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int row = wm * 64 + mi * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+          if (row < mrows) {
+            const float h = silu_f(acc[mi][0][v]) * acc[mi][1][v];
+            Hout[static_cast<int64_t>(row) * a.F + col] = f32_to_bf16(h);
+          }
+        }
+    }
+  } else {
+    uint16_t* Yout = routed ? static_cast<uint16_t*>(a.y_perm) + static_cast<int64_t>(arow0) * a.d
+                            : static_cast<uint16_t*>(a.y_shared) +
+                                  static_cast<int64_t>(hrow0 - a.T * a.k) * a.d;
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni) {
+      const int col = n0 + wn * 64 + ni * 32 + (lane & 31);
+      if (col >= N) continue;
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int row = wm * 64 + mi * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+          if (row < mrows) Yout[static_cast<int64_t>(row) * a.d + col] = f32_to_bf16(acc[mi][ni][v]);
+        }
+    }
+  }
+}
+
+// ------------------------------------------------------------- fp32 VALU --
+
+// Tile: 64 rows x 64 B-rows, K step 16; thread (ty, tx) = (tid / 16,
+// tid % 16) owns rows ty*4 .. ty*4+3.  Phase 1: B-rows 0..31 are W1
+// columns n0..n0+31 and 32..63 the same W3 columns; the thread owns H
+// columns tx*2, tx*2+1 (gate and up).  Phase 2: columns tx*4 .. tx*4+3.
+template <int PHASE>
+__global__ __launch_bounds__(kThreads) void gemm_f32_kernel(FfnArgs a) {
+  constexpr int BKf = 16;
+  __shared__ float As[kBMf][BKf + 1];
+  __shared__ float Bs[64][BKf + 1];
+  if (static_cast<int>(blockIdx.x) >= *a.ntiles) return;
+  const int4 tl = a.tiles[blockIdx.x];
+  const int seg = tl.x, arow0 = tl.y, mrows = tl.z, hrow0 = tl.w;
+  const bool routed = seg < a.E;
+  const int e = routed ? seg : seg - a.E;
+  const int tid = threadIdx.x;
+  const int ty = tid / 16, tx = tid % 16;
+  const int K = PHASE == 1 ? a.d : a.F;
+  const int N = PHASE == 1 ? a.F : a.d;
+  const int n0 = blockIdx.y * (PHASE == 1 ? 32 : 64);
+  const float* A = PHASE == 1
+      ? static_cast<const float*>(routed ? a.x_perm : a.x) + static_cast<int64_t>(arow0) * K
+      : static_cast<const float*>(a.H) + static_cast<int64_t>(hrow0) * K;
+  const int64_t wstride = static_cast<int64_t>(a.F) * a.d;
+  float acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = 0.f;
+
+  for (int k0 = 0; k0 < K; k0 += BKf) {
+    // 64 x 16 of A and of B: 1024 values each, 4 per thread.
+    for (int q = tid; q < 64 * BKf; q += kThreads) {
+      const int r = q / BKf, c = q % BKf;
+      As[r][c] = (r < mrows && k0 + c < K) ? A[static_cast<int64_t>(r) * K + k0 + c] : 0.f;
+      float bv = 0.f;
+      int col;
+      const float* W;
+      if (PHASE == 1) {
+        col = n0 + (r & 31);
+        W = static_cast<const float*>(r < 32 ? (routed ? a.w1 : a.ws1) : (routed ? a.w3 : a.ws3));
+      } else {
+        col = n0 + r;
+        W = static_cast<const float*>(routed ? a.w2 : a.ws2);
+      }
+      if (col < N && k0 + c < K) bv = W[e * wstride + static_cast<int64_t>(col) * K + k0 + c];
+      Bs[r][c] = bv;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int c = 0; c < BKf; ++c) {
+      float av[4], bv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) av[i] = As[ty * 4 + i][c];
+      if (PHASE == 1) {
+        bv[0] = Bs[tx * 2][c];      bv[1] = Bs[tx * 2 + 1][c];
+        bv[2] = Bs[32 + tx * 2][c]; bv[3] = Bs[32 + tx * 2 + 1][c];
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) bv[j] = Bs[tx * 4 + j][c];
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(av[i], bv[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+  if (PHASE == 1) {
+    float* Hout = static_cast<float*>(a.H) + static_cast<int64_t>(hrow0) * a.F;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = ty * 4 + i;
+      if (row >= mrows) continue;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int col = n0 + tx * 2 + j;
+        if (col < N) {
+          const float g = acc[i][j];
+          Hout[static_cast<int64_t>(row) * a.F + col] = (g / (1.0f + expf(-g))) * acc[i][2 + j];
+        }
+      }
+    }
+  } else {
+    float* Yout = routed ? static_cast<float*>(a.y_perm) + static_cast<int64_t>(arow0) * a.d
+                         : static_cast<float*>(a.y_shared) +
+                               static_cast<int64_t>(hrow0 - a.T * a.k) * a.d;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = ty * 4 + i;
+      if (row >= mrows) continue;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int col = n0 + tx * 4 + j;
+        if (col < N) Yout[static_cast<int64_t>(row) * a.d + col] = acc[i][j];
+      }
+    }
+  }
+}
+
+int64_t max_tiles(int64_t T, int E, int Es, int k, int BM) {
+  return (T * k + BM - 1) / BM + E + static_cast<int64_t>(Es) * ((T + BM - 1) / BM);
+}
+
+size_t align256(size_t b) { return (b + 255) & ~static_cast<size_t>(255); }
+
+}  // namespace
+
+size_t ffn_workspace_bytes(int64_t T, int E, int E_shared, int k, int64_t d_ff,
+                           int elem_bytes) {
+  const int64_t tiles = max_tiles(T, E, E_shared, k, kBMf);   // the smaller BM bounds both
+  const int64_t hrows = T * k + static_cast<int64_t>(E_shared) * T;
+  return 256 + align256(static_cast<size_t>(tiles) * sizeof(int4)) +
+         static_cast<size_t>(hrows) * d_ff * elem_bytes;
+}
+
+hipError_t launch_expert_ffn(int64_t T, int64_t d, int E, int E_shared, int k, int64_t F,
+                             bool bf16, const void* x_perm, const int32_t* offsets,
+                             const void* x, const void* w1, const void* w3, const void* w2,
+                             const void* ws1, const void* ws3, const void* ws2, void* y_perm,
+                             void* y_shared, void* ws, hipStream_t s) {
+  char* base = static_cast<char*>(ws);
+  int* ntiles = reinterpret_cast<int*>(base);
+  int4* tiles = reinterpret_cast<int4*>(base + 256);
+  const int64_t tiles_cap = max_tiles(T, E, E_shared, k, kBMf);
+  void* H = base + 256 + align256(static_cast<size_t>(tiles_cap) * sizeof(int4));
+
+  const int BM = bf16 ? kBM : kBMf;
+  hipLaunchKernelGGL(tile_table_kernel, dim3(1), dim3(kWave), 0, s, offsets, tiles, ntiles, E,
+                     E_shared, static_cast<int>(T), k, BM);
+  FfnArgs a{x_perm, x, offsets, w1, w3, w2, ws1, ws3, ws2, H, y_perm, y_shared, tiles, ntiles,
+            static_cast<int>(T), static_cast<int>(d), E, E_shared, k, static_cast<int>(F)};
+  const unsigned gx = static_cast<unsigned>(max_tiles(T, E, E_shared, k, BM));
+  if (bf16) {
+    hipLaunchKernelGGL(gemm_bf16_kernel<1>, dim3(gx, static_cast<unsigned>((F + 63) / 64)),
+                       dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL(gemm_bf16_kernel<2>, dim3(gx, static_cast<unsigned>((d + 127) / 128)),
+                       dim3(kThreads), 0, s, a);
+  } else {
+    hipLaunchKernelGGL(gemm_f32_kernel<1>, dim3(gx, static_cast<unsigned>((F + 31) / 32)),
+                       dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL(gemm_f32_kernel<2>, dim3(gx, static_cast<unsigned>((d + 63) / 64)),
+                       dim3(kThreads), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace moe

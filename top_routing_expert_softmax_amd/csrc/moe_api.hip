@@ -1,0 +1,267 @@
+// C ABI of the MoE-layer forward (include/moe.h): argument checks, exact
+// capacity, workspace sizing and error reporting around the launchers.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+
+#include "moe.h"
+#include "moe_internal.h"
+
+namespace {
+
+thread_local char g_msg[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_msg, sizeof(g_msg), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_msg[0] = '\0';
+  return MOE_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+#define REQUIRE(cond, ...)                          \
+  do {                                              \
+    if (!(cond)) return fail(MOE_EINVAL, __VA_ARGS__); \
+  } while (0)
+
+#define REQUIRE_PTR(p)                                                         \
+  do {                                                                         \
+    if ((p) == nullptr) return fail(MOE_EINVAL, "%s is NULL", #p);              \
+    if (!aligned16(p)) return fail(MOE_EINVAL, "%s is not 16-byte aligned", #p); \
+  } while (0)
+
+int check_common(int64_t T, int32_t E, int32_t k) {
+  REQUIRE(T >= 1, "T must be >= 1 (got %lld)", static_cast<long long>(T));
+  REQUIRE(E >= 1 && E <= 256, "E must be in [1, 256] (got %d)", E);
+  REQUIRE(k >= 1 && k <= E && k <= 64, "k must be in [1, min(E, 64)] (got k=%d, E=%d)", k, E);
+  REQUIRE(T * k < (int64_t(1) << 31), "T*k must be < 2^31");
+  return MOE_OK;
+}
+
+int check_dtype(int32_t dtype) {
+  if (dtype != MOE_F32 && dtype != MOE_BF16)
+    return fail(MOE_EUNSUPPORTED, "dtype %d has no kernel (MOE_F32=0, MOE_BF16=1)", dtype);
+  return MOE_OK;
+}
+
+int check_dim(const char* name, int64_t v) {
+  REQUIRE(v >= 64 && v % 64 == 0 && v < (int64_t(1) << 24),
+          "%s must be a positive multiple of 64 below 2^24 (got %lld)", name,
+          static_cast<long long>(v));
+  return MOE_OK;
+}
+
+int launched(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(MOE_EHIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+// ceil(CF * T * k / E) on the exact value of CF, clamped to T; CF <= 0: T.
+int64_t exact_capacity(int64_t T, int32_t E, int32_t k, double CF) {
+  if (!(CF > 0.0)) return T;
+  int ex = 0;
+  const double fr = frexp(CF, &ex);                            // CF = fr * 2^ex, fr in [0.5, 1)
+  const int64_t m = static_cast<int64_t>(ldexp(fr, 53));       // CF = m * 2^(ex - 53) exactly
+  ex -= 53;
+  __int128 num = static_cast<__int128>(m) * T * k;             // < 2^84
+  int64_t c;
+  if (ex >= 0) {
+    if (ex >= 40) return T;                                    // the product is >= 2^40 > T
+    num <<= ex;
+    c = static_cast<int64_t>(std::min<__int128>((num + E - 1) / E, static_cast<__int128>(T)));
+  } else {
+    const int s = -ex;
+    if (s >= 96) return std::min<int64_t>(T, 1);               // 0 < value < 1
+    const __int128 den = static_cast<__int128>(E) << s;
+    c = static_cast<int64_t>(std::min<__int128>((num + den - 1) / den, static_cast<__int128>(T)));
+  }
+  return std::min<int64_t>(c, T);
+}
+
+size_t align256(size_t b) { return (b + 255) & ~static_cast<size_t>(255); }
+
+size_t workspace_bytes(int64_t T, int64_t /*d*/, int32_t E, int32_t Es, int32_t k, int64_t F,
+                       int32_t dtype) {
+  const int elem = dtype == MOE_BF16 ? 2 : 4;
+  size_t b = moe::permute_workspace_bytes(T, E);
+  b = std::max(b, moe::stats_workspace_bytes(T, E));
+  b = std::max(b, moe::ffn_workspace_bytes(T, E, Es, k, F, elem));
+  return align256(b);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_strerror(int status) {
+  switch (status) {
+    case MOE_OK: return "success";
+    case MOE_EINVAL: return "invalid argument";
+    case MOE_EUNSUPPORTED: return "unsupported dtype or shape";
+    case MOE_EHIP: return "HIP error";
+    case MOE_EWORKSPACE: return "workspace too small";
+    default: return "unknown status";
+  }
+}
+
+const char* moe_last_error(void) { return g_msg; }
+
+int moe_capacity(int64_t T, int32_t E, int32_t k, double CF, int64_t* cap) {
+  if (int r = check_common(T, E, k)) return r;
+  REQUIRE(cap != nullptr, "cap is NULL");
+  REQUIRE(!isnan(CF) && !isinf(CF), "CF must be finite");
+  *cap = exact_capacity(T, E, k, CF);
+  return ok();
+}
+
+int moe_workspace_size(int64_t T, int64_t d_model, int32_t E, int32_t E_shared, int32_t k,
+                       int64_t d_ff, int32_t dtype, size_t* bytes) {
+  if (int r = check_common(T, E, k)) return r;
+  if (int r = check_dtype(dtype)) return r;
+  if (int r = check_dim("d_model", d_model)) return r;
+  if (int r = check_dim("d_ff", d_ff)) return r;
+  REQUIRE(E_shared >= 0 && E_shared <= 16, "E_shared must be in [0, 16]");
+  REQUIRE(T * k + static_cast<int64_t>(E_shared) * T < (int64_t(1) << 31),
+          "T*k + E_shared*T must be < 2^31");
+  REQUIRE(bytes != nullptr, "bytes is NULL");
+  *bytes = workspace_bytes(T, d_model, E, E_shared, k, d_ff, dtype);
+  return ok();
+}
+
+int moe_route(int64_t T, int64_t d_model, int32_t E, int32_t k, int32_t dtype, const void* x,
+              const void* w_gate, float* logits, int32_t* topk_idx, float* topk_w,
+              void* stream) {
+  if (int r = check_common(T, E, k)) return r;
+  if (int r = check_dtype(dtype)) return r;
+  if (int r = check_dim("d_model", d_model)) return r;
+  REQUIRE_PTR(x);
+  REQUIRE_PTR(w_gate);
+  REQUIRE_PTR(logits);
+  REQUIRE_PTR(topk_idx);
+  REQUIRE_PTR(topk_w);
+  (void)hipGetLastError();
+  return launched(moe::launch_route(T, d_model, E, k, dtype == MOE_BF16, x, w_gate, logits,
+                                    topk_idx, topk_w, static_cast<hipStream_t>(stream)),
+                  "moe_route");
+}
+
+int moe_permute(int64_t T, int64_t d_model, int32_t E, int32_t k, double CF, int32_t dtype,
+                const int32_t* topk_idx, const void* x, int32_t* counts, int32_t* offsets,
+                int32_t* token_of_row, int32_t* row_of_pair, uint8_t* drop_mask, void* x_perm,
+                void* ws, size_t ws_bytes, void* stream) {
+  if (int r = check_common(T, E, k)) return r;
+  if (int r = check_dtype(dtype)) return r;
+  if (int r = check_dim("d_model", d_model)) return r;
+  REQUIRE(!isnan(CF) && !isinf(CF), "CF must be finite");
+  REQUIRE_PTR(topk_idx);
+  REQUIRE_PTR(x);
+  REQUIRE_PTR(counts);
+  REQUIRE_PTR(offsets);
+  REQUIRE_PTR(token_of_row);
+  REQUIRE_PTR(row_of_pair);
+  REQUIRE_PTR(drop_mask);
+  REQUIRE_PTR(x_perm);
+  REQUIRE_PTR(ws);
+  const size_t need = moe::permute_workspace_bytes(T, E);
+  if (ws_bytes < need)
+    return fail(MOE_EWORKSPACE, "moe_permute needs %zu workspace bytes, got %zu", need, ws_bytes);
+  const int64_t cap = exact_capacity(T, E, k, CF);
+  (void)hipGetLastError();
+  return launched(moe::launch_permute(T, d_model, E, k, cap, dtype == MOE_BF16, topk_idx, x,
+                                      counts, offsets, token_of_row, row_of_pair, drop_mask,
+                                      x_perm, ws, static_cast<hipStream_t>(stream)),
+                  "moe_permute");
+}
+
+int moe_expert_ffn(int64_t T, int64_t d_model, int32_t E, int32_t E_shared, int32_t k,
+                   int64_t d_ff, int32_t dtype, const void* x_perm, const int32_t* offsets,
+                   const void* x, const void* w1, const void* w3, const void* w2,
+                   const void* ws1, const void* ws3, const void* ws2, void* y_perm,
+                   void* y_shared, void* ws, size_t ws_bytes, void* stream) {
+  if (int r = check_common(T, E, k)) return r;
+  if (int r = check_dtype(dtype)) return r;
+  if (int r = check_dim("d_model", d_model)) return r;
+  if (int r = check_dim("d_ff", d_ff)) return r;
+  REQUIRE(E_shared >= 0 && E_shared <= 16, "E_shared must be in [0, 16]");
+  REQUIRE(T * k + static_cast<int64_t>(E_shared) * T < (int64_t(1) << 31),
+          "T*k + E_shared*T must be < 2^31");
+  REQUIRE_PTR(x_perm);
+  REQUIRE_PTR(offsets);
+  REQUIRE_PTR(w1);
+  REQUIRE_PTR(w3);
+  REQUIRE_PTR(w2);
+  REQUIRE_PTR(y_perm);
+  REQUIRE_PTR(ws);
+  if (E_shared > 0) {
+    REQUIRE_PTR(x);
+    REQUIRE_PTR(ws1);
+    REQUIRE_PTR(ws3);
+    REQUIRE_PTR(ws2);
+    REQUIRE_PTR(y_shared);
+  }
+  const size_t need = moe::ffn_workspace_bytes(T, E, E_shared, k, d_ff, dtype == MOE_BF16 ? 2 : 4);
+  if (ws_bytes < need)
+    return fail(MOE_EWORKSPACE, "moe_expert_ffn needs %zu workspace bytes, got %zu", need,
+                ws_bytes);
+  (void)hipGetLastError();
+  return launched(moe::launch_expert_ffn(T, d_model, E, E_shared, k, d_ff, dtype == MOE_BF16,
+                                         x_perm, offsets, x, w1, w3, w2, ws1, ws3, ws2, y_perm,
+                                         y_shared, ws, static_cast<hipStream_t>(stream)),
+                  "moe_expert_ffn");
+}
+
+int moe_combine(int64_t T, int64_t d_model, int32_t E_shared, int32_t k, int32_t dtype,
+                const void* y_perm, const void* y_shared, const int32_t* row_of_pair,
+                const float* topk_w, void* y, void* stream) {
+  REQUIRE(T >= 1, "T must be >= 1");
+  REQUIRE(k >= 1 && k <= 64, "k must be in [1, 64]");
+  REQUIRE(T * k < (int64_t(1) << 31), "T*k must be < 2^31");
+  if (int r = check_dtype(dtype)) return r;
+  if (int r = check_dim("d_model", d_model)) return r;
+  REQUIRE(E_shared >= 0 && E_shared <= 16, "E_shared must be in [0, 16]");
+  REQUIRE_PTR(y_perm);
+  REQUIRE_PTR(row_of_pair);
+  REQUIRE_PTR(topk_w);
+  REQUIRE_PTR(y);
+  if (E_shared > 0) REQUIRE_PTR(y_shared);
+  (void)hipGetLastError();
+  return launched(moe::launch_combine(T, d_model, E_shared, k, dtype == MOE_BF16, y_perm,
+                                      y_shared, row_of_pair, topk_w, y,
+                                      static_cast<hipStream_t>(stream)),
+                  "moe_combine");
+}
+
+int moe_aux_stats(int64_t T, int32_t E, int32_t k, double CF, const float* logits,
+                  const int32_t* counts, float* f, float* P, double* scalars, void* ws,
+                  size_t ws_bytes, void* stream) {
+  if (int r = check_common(T, E, k)) return r;
+  REQUIRE(!isnan(CF) && !isinf(CF), "CF must be finite");
+  REQUIRE_PTR(logits);
+  REQUIRE_PTR(counts);
+  REQUIRE_PTR(f);
+  REQUIRE_PTR(P);
+  REQUIRE(scalars != nullptr && (reinterpret_cast<uintptr_t>(scalars) & 7u) == 0,
+          "scalars must be a non-NULL 8-byte aligned pointer");
+  REQUIRE_PTR(ws);
+  const size_t need = moe::stats_workspace_bytes(T, E);
+  if (ws_bytes < need)
+    return fail(MOE_EWORKSPACE, "moe_aux_stats needs %zu workspace bytes, got %zu", need,
+                ws_bytes);
+  const int64_t cap = exact_capacity(T, E, k, CF);
+  (void)hipGetLastError();
+  return launched(moe::launch_aux_stats(T, E, k, cap, logits, counts, f, P, scalars, ws,
+                                        static_cast<hipStream_t>(stream)),
+                  "moe_aux_stats");
+}
+
+}  // extern "C"

@@ -1,0 +1,69 @@
+// Device-side helpers shared by the gfx950 kernels of the MoE forward.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int kWave = 64;  // CDNA wavefront width
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+// Native 128-bit vector (HIP's uint4 is a struct; selects on it go through
+// memory).
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// bf16 storage is handled as raw 16-bit patterns.
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+  return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+
+// Round to nearest even; inputs here are finite.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return static_cast<uint32_t>(f32_to_bf16(lo)) |
+         (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+}
+
+// Low / high bf16 of a 32-bit word, widened to fp32.
+__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+template <typename T>
+__device__ __forceinline__ T wave_sum(T v) {
+#pragma unroll
+  for (int off = kWave / 2; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int off = kWave / 2; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
+  return v;
+}
+
+// Total order on fp32 as unsigned keys (no NaNs expected).
+__device__ __forceinline__ uint32_t f32_order_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+  for (int off = kWave / 2; off > 0; off >>= 1) {
+    uint32_t lo = __shfl_xor(static_cast<uint32_t>(v), off, kWave);
+    uint32_t hi = __shfl_xor(static_cast<uint32_t>(v >> 32), off, kWave);
+    uint64_t o = (static_cast<uint64_t>(hi) << 32) | lo;
+    v = o > v ? o : v;
+  }
+  return v;
+}
+
+}  // namespace moe

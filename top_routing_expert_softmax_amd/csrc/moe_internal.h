@@ -1,0 +1,54 @@
+// Host-side launchers behind the C ABI.  Arguments are validated by the
+// caller (moe_api.hip); these only size grids and enqueue kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+// Token chunking shared by the dispatch kernels: blocks of kDispatchThreads
+// threads, at most kMaxDispatchBlocks blocks (so the per-expert scan over
+// blocks fits one wavefront).
+constexpr int kDispatchThreads = 256;
+constexpr int kMaxDispatchBlocks = 64;
+
+// Statistics: at most this many partial blocks.
+constexpr int kStatsBlocks = 256;
+
+size_t permute_workspace_bytes(int64_t T, int E);
+size_t stats_workspace_bytes(int64_t T, int E);
+size_t ffn_workspace_bytes(int64_t T, int E, int E_shared, int k, int64_t d_ff,
+                           int elem_bytes);
+
+hipError_t launch_route(int64_t T, int64_t d, int E, int k, bool bf16,
+                        const void* x, const void* w_gate, float* logits,
+                        int32_t* topk_idx, float* topk_w, hipStream_t s);
+
+hipError_t launch_permute(int64_t T, int64_t d, int E, int k, int64_t cap,
+                          bool bf16, const int32_t* topk_idx, const void* x,
+                          int32_t* counts, int32_t* offsets,
+                          int32_t* token_of_row, int32_t* row_of_pair,
+                          uint8_t* drop_mask, void* x_perm, void* ws,
+                          hipStream_t s);
+
+hipError_t launch_expert_ffn(int64_t T, int64_t d, int E, int E_shared, int k,
+                             int64_t F, bool bf16, const void* x_perm,
+                             const int32_t* offsets, const void* x,
+                             const void* w1, const void* w3, const void* w2,
+                             const void* ws1, const void* ws3, const void* ws2,
+                             void* y_perm, void* y_shared, void* ws,
+                             hipStream_t s);
+
+hipError_t launch_combine(int64_t T, int64_t d, int E_shared, int k, bool bf16,
+                          const void* y_perm, const void* y_shared,
+                          const int32_t* row_of_pair, const float* topk_w,
+                          void* y, hipStream_t s);
+
+hipError_t launch_aux_stats(int64_t T, int E, int k, int64_t cap,
+                            const float* logits, const int32_t* counts,
+                            float* f, float* P, double* scalars, void* ws,
+                            hipStream_t s);
+
+}  // namespace moe
