@@ -34,6 +34,14 @@ constexpr int kBK = 64;
 constexpr int kLdsStride = kBK + 8;   // bf16 elements per LDS row
 constexpr int kThreads = 256;
 
+// K-slice depth and LDS ring length of the 256 x 256 bf16 kernel.
+#ifndef MOE_GEMM_BK
+#define MOE_GEMM_BK 64
+#endif
+#ifndef MOE_GEMM_NST
+#define MOE_GEMM_NST 2
+#endif
+
 struct FfnArgs {
   const void* x_perm;
   const void* x;
@@ -251,6 +259,255 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(FfnArgs a) {
   }
 }
 
+// ------------------------------------------------- bf16 MFMA, 256 x 256 --
+//
+// Block tile 256 rows x 256 B-rows, 4 wavefronts as 2 x 2, each owning
+// 128 x 128 outputs (4 x 4 blocks of v_mfma_f32_32x32x16_bf16, 256 fp32
+// accumulators per lane).  Operand tiles move global -> LDS with
+// global_load_lds_dwordx4 (no staging registers) through an NST-stage ring
+// of K-slices of BKT elements: while slice s is multiplied, the loads of
+// slices s+1 .. s+NST-1 are in flight, which hides the L2/HBM latency.
+// LDS rows hold BKT bf16 (ROW bytes = CH chunks of 16 B).  The LDS has 64
+// banks (a 256-byte line holding RPL = 256/ROW rows) and serves a 16-byte
+// read 16 lanes at a time; chunk c of row r sits at physical chunk
+// c ^ ((r / RPL) % CH), so the fragment reads of 16 consecutive rows touch
+// every bank once.  Rows past the segment (A) or past N (B) load a clamped
+// valid row: they only feed outputs that the epilogue does not store.
+//
+// Block order: a 1-D grid; each XCD (blocks are dealt to the 8 XCDs round
+// robin) takes a contiguous chunk of the live tiles, and inside a chunk
+// tiles run in groups of kGM row tiles x all column tiles, so concurrently
+// resident blocks of one XCD share A and B tiles in that XCD's L2.
+constexpr int kBM2 = 256;
+constexpr int kBN2 = 256;
+constexpr int kGM = 8;
+constexpr int kXcds = 8;
+
+template <int BKT>
+struct SliceGeom {
+  static constexpr int ROW = BKT * 2;                   // bytes per LDS row
+  static constexpr int CH = ROW / 16;                   // 16-byte chunks per row
+  static constexpr int RPL = 256 / ROW;                 // rows per 256-byte bank line
+  static constexpr int RPI = 1024 / ROW;                // rows per wave DMA instruction
+  static constexpr int STAGE = (kBM2 + kBN2) * ROW;     // bytes per slice
+};
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  // gfx9 s_waitcnt: vmcnt [3:0] and [15:14]; expcnt [6:4] and lgkmcnt
+  // [11:8] at their maxima (no wait)
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+__device__ __forceinline__ void lds_dma16(const void* gptr, uint32_t* lds_row_base) {
+  __builtin_amdgcn_global_load_lds(gptr, lds_row_base, 16, 0, 0);
+}
+
+template <int PHASE, int BKT, int NST, int WAVES>
+__global__ __launch_bounds__(WAVES * kWave) __attribute__((amdgpu_waves_per_eu(WAVES / 4, WAVES / 4)))
+void gemm256_kernel(FfnArgs a, int NT) {
+  using G = SliceGeom<BKT>;
+  constexpr int WN = WAVES / 2;             // waves along N (2 along M)
+  constexpr int WROWS = kBM2 / WAVES;       // tile rows each wave loads per operand
+  constexpr int NI = WROWS / G::RPI;        // DMA instructions per wave per operand
+  constexpr int NB = kBN2 / WN / 32;        // 32-wide B blocks per wave
+  static_assert(NI >= 1 && NB >= 2 && NB % 2 == 0, "tile geometry");
+  extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
+
+  // ---- which tile
+  const int MT = *a.ntiles;
+  const int L = MT * NT;
+  const int chunk = (L + kXcds - 1) / kXcds;
+  const int xcd = blockIdx.x % kXcds;
+  const int j = blockIdx.x / kXcds;
+  if (j >= chunk) return;
+  const int pid = xcd * chunk + j;
+  if (pid >= L) return;
+  const int group = pid / (kGM * NT);
+  const int first_m = group * kGM;
+  const int gm = min(kGM, MT - first_m);
+  const int in_group = pid - group * kGM * NT;
+  const int mt = first_m + in_group % gm;
+  const int nt = in_group / gm;
+
+  const int4 tl = a.tiles[mt];
+  const int seg = tl.x, arow0 = tl.y, mrows = tl.z, hrow0 = tl.w;
+  const bool routed = seg < a.E;
+  const int e = routed ? seg : seg - a.E;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const int wm = wave / WN, wn = wave % WN;
+
+  const int K = PHASE == 1 ? a.d : a.F;
+  const int N = PHASE == 1 ? a.F : a.d;
+  const int n0 = nt * (PHASE == 1 ? kBN2 / 2 : kBN2);
+  const uint16_t* A = PHASE == 1
+      ? static_cast<const uint16_t*>(routed ? a.x_perm : a.x) + static_cast<int64_t>(arow0) * K
+      : static_cast<const uint16_t*>(a.H) + static_cast<int64_t>(hrow0) * K;
+  const int64_t wstride = static_cast<int64_t>(a.F) * a.d;
+
+  // ---- per-lane sources of the NI A and NI B DMA instructions of a slice.
+  // Wave w, instruction i covers tile rows w*WROWS + i*RPI .. +RPI; lane l
+  // takes row r = w*WROWS + i*RPI + l/CH and the logical chunk that the
+  // swizzle stores at physical chunk l%CH of that row.
+  const uint16_t* asrc[NI];
+  const uint16_t* bsrc[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int r = wave * WROWS + i * G::RPI + lane / G::CH;
+    const int lchunk = (lane % G::CH) ^ ((r / G::RPL) % G::CH);
+    const int ra = r < mrows ? r : mrows - 1;
+    asrc[i] = A + static_cast<int64_t>(ra) * K + lchunk * 8;
+    int col;
+    const uint16_t* W;
+    if (PHASE == 1) {
+      col = n0 + (r & 127);
+      W = static_cast<const uint16_t*>(r < 128 ? (routed ? a.w1 : a.ws1) : (routed ? a.w3 : a.ws3));
+    } else {
+      col = n0 + r;
+      W = static_cast<const uint16_t*>(routed ? a.w2 : a.ws2);
+    }
+    col = col < N ? col : N - 1;
+    bsrc[i] = W + e * wstride + static_cast<int64_t>(col) * K + lchunk * 8;
+  }
+  char* lds_bytes = reinterpret_cast<char*>(lds);
+  const int a_dst = wave * WROWS * G::ROW;
+  const int b_dst = kBM2 * G::ROW + wave * WROWS * G::ROW;
+
+#define MOE_ISSUE_SLICE(slot, k0)                                                          \
+  _Pragma("unroll") for (int i = 0; i < NI; ++i) {                                         \
+    lds_dma16(asrc[i] + (k0), reinterpret_cast<uint32_t*>(                                \
+                  lds_bytes + (slot) * G::STAGE + a_dst + i * G::RPI * G::ROW));          \
+    lds_dma16(bsrc[i] + (k0), reinterpret_cast<uint32_t*>(                                \
+                  lds_bytes + (slot) * G::STAGE + b_dst + i * G::RPI * G::ROW));          \
+  }
+
+  f32x16_t acc[4][NB];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int jn = 0; jn < NB; ++jn)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][jn][v] = 0.f;
+
+  // Phase 1: the wave's first NB/2 B blocks are gate (W1) columns, the last
+  // NB/2 the same columns of W3.
+  int a_off[4], b_off[NB];
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi) a_off[mi] = (wm * 128 + mi * 32 + (lane & 31)) * G::ROW;
+#pragma unroll
+  for (int ni = 0; ni < NB; ++ni) {
+    const int r = PHASE == 1
+        ? ((ni / (NB / 2)) * 128 + wn * (128 / WN) + (ni % (NB / 2)) * 32 + (lane & 31))
+        : (wn * (kBN2 / WN) + ni * 32 + (lane & 31));
+    b_off[ni] = kBM2 * G::ROW + r * G::ROW;
+  }
+  // fragment rows are 32-aligned bases + lane%32, so the swizzle key of
+  // all of this lane's fragment rows is ((lane % 32) / RPL) % CH
+  const int key = ((lane & 31) / G::RPL) % G::CH;
+  const int khalf = lane >> 5;
+
+  const int nk = K / BKT;
+  // prologue: slices 0 .. NST-2 in flight
+#pragma unroll
+  for (int s0 = 0; s0 < NST - 1; ++s0)
+    if (s0 < nk) { MOE_ISSUE_SLICE(s0, s0 * BKT); }
+  for (int kt = 0; kt < nk; ++kt) {
+    const int slot = kt % NST;
+    // slice kt has landed once at most (NST-2) younger slices are pending
+    if (kt + NST - 2 < nk) {
+      wait_vmcnt<(NST - 2) * 2 * NI>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    __syncthreads();            // every wave's part of slice kt is in LDS, and
+                                // slot (kt-1) % NST is no longer read
+    if (kt + NST - 1 < nk) {
+      const int s_next = kt + NST - 1;
+      MOE_ISSUE_SLICE(s_next % NST, s_next * BKT);
+    }
+    const char* sb = lds_bytes + slot * G::STAGE;
+#pragma unroll
+    for (int ks = 0; ks < BKT / 16; ++ks) {
+      const int pc = ((2 * ks + khalf) ^ key) * 16;
+      bf16x8_t fa[4], fb[NB];
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi) fa[mi] = *reinterpret_cast<const bf16x8_t*>(sb + a_off[mi] + pc);
+#pragma unroll
+      for (int ni = 0; ni < NB; ++ni) fb[ni] = *reinterpret_cast<const bf16x8_t*>(sb + b_off[ni] + pc);
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < NB; ++ni)
+          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[mi], fb[ni], acc[mi][ni], 0, 0, 0);
+      __builtin_amdgcn_iglp_opt(0);
+    }
+  }
+#undef MOE_ISSUE_SLICE
+
+  // ---- epilogue (accumulator element v of lane l: row 8*(v/4) + 4*(l/32)
+  // + v%4, column l%32 of its 32 x 32 block)
+  if (PHASE == 1) {
+    uint16_t* Hout = static_cast<uint16_t*>(a.H) + static_cast<int64_t>(hrow0) * a.F;
+#pragma unroll
+    for (int ni = 0; ni < NB / 2; ++ni) {
+      const int col = n0 + wn * (128 / WN) + ni * 32 + (lane & 31);
+      if (col >= N) continue;
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int row = wm * 128 + mi * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+          if (row < mrows) {
+            const float h = silu_f(acc[mi][ni][v]) * acc[mi][ni + NB / 2][v];
+            Hout[static_cast<int64_t>(row) * a.F + col] = f32_to_bf16(h);
+          }
+        }
+    }
+  } else {
+    uint16_t* Yout = routed ? static_cast<uint16_t*>(a.y_perm) + static_cast<int64_t>(arow0) * a.d
+                            : static_cast<uint16_t*>(a.y_shared) +
+                                  static_cast<int64_t>(hrow0 - a.T * a.k) * a.d;
+#pragma unroll
+    for (int ni = 0; ni < NB; ++ni) {
+      const int col = n0 + wn * (kBN2 / WN) + ni * 32 + (lane & 31);
+      if (col >= N) continue;
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int row = wm * 128 + mi * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+          if (row < mrows) Yout[static_cast<int64_t>(row) * a.d + col] = f32_to_bf16(acc[mi][ni][v]);
+        }
+    }
+  }
+}
+
+// The configuration the library launches.
+constexpr int kBKsel = MOE_GEMM_BK;
+constexpr int kNSTsel = MOE_GEMM_NST;
+
+#ifndef MOE_GEMM_WAVES
+#define MOE_GEMM_WAVES 8
+#endif
+constexpr int kWavesSel = MOE_GEMM_WAVES;
+
+template <int PHASE>
+hipError_t launch_gemm256(const FfnArgs& a, int nt, int64_t mt, hipStream_t s) {
+  const unsigned g = static_cast<unsigned>(kXcds * ((mt * nt + kXcds - 1) / kXcds));
+  constexpr size_t lds = static_cast<size_t>(kNSTsel) * SliceGeom<kBKsel>::STAGE;
+  auto kern = &gemm256_kernel<PHASE, kBKsel, kNSTsel, kWavesSel>;
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+      static_cast<int>(lds));
+  if (attr != hipSuccess) return attr;
+  hipLaunchKernelGGL(kern, dim3(g), dim3(kWavesSel * kWave), lds, s, a, nt);
+  return hipGetLastError();
+}
+
 // ------------------------------------------------------------- fp32 VALU --
 
 // Tile: 64 rows x 64 B-rows, K step 16; thread (ty, tx) = (tid / 16,
@@ -379,13 +636,23 @@ hipError_t launch_expert_ffn(int64_t T, int64_t d, int E, int E_shared, int k, i
   const int64_t tiles_cap = max_tiles(T, E, E_shared, k, kBMf);
   void* H = base + 256 + align256(static_cast<size_t>(tiles_cap) * sizeof(int4));
 
-  const int BM = bf16 ? kBM : kBMf;
+  // Large segments take the 256 x 256 tiles; decode-sized ones (few rows
+  // per expert) the 128-row tiles.
+  const int BM = !bf16 ? kBMf : (T * k >= 64LL * E ? kBM2 : kBM);
   hipLaunchKernelGGL(tile_table_kernel, dim3(1), dim3(kWave), 0, s, offsets, tiles, ntiles, E,
                      E_shared, static_cast<int>(T), k, BM);
   FfnArgs a{x_perm, x, offsets, w1, w3, w2, ws1, ws3, ws2, H, y_perm, y_shared, tiles, ntiles,
             static_cast<int>(T), static_cast<int>(d), E, E_shared, k, static_cast<int>(F)};
   const unsigned gx = static_cast<unsigned>(max_tiles(T, E, E_shared, k, BM));
-  if (bf16) {
+  if (bf16 && BM == kBM2) {
+    const int nt1 = static_cast<int>((F + kBN2 / 2 - 1) / (kBN2 / 2));
+    const int nt2 = static_cast<int>((d + kBN2 - 1) / kBN2);
+    const int64_t mt = max_tiles(T, E, E_shared, k, kBM2);
+    hipError_t err = launch_gemm256<1>(a, nt1, mt, s);
+    if (err != hipSuccess) return err;
+    err = launch_gemm256<2>(a, nt2, mt, s);
+    if (err != hipSuccess) return err;
+  } else if (bf16) {
     hipLaunchKernelGGL(gemm_bf16_kernel<1>, dim3(gx, static_cast<unsigned>((F + 63) / 64)),
                        dim3(kThreads), 0, s, a);
     hipLaunchKernelGGL(gemm_bf16_kernel<2>, dim3(gx, static_cast<unsigned>((d + 127) / 128)),
