@@ -137,7 +137,7 @@ def main():
     def step(timed):
         if timed:
             ev[0].record(stream)
-        M.moe_route(dev["x"], dev["wg"], k, b.logits, b.topk_idx, b.topk_w, stream)
+        M.moe_route(dev["x"], dev["wg"], k, b.logits, b.topk_idx, b.topk_w, b.ws, stream)
         if timed:
             ev[1].record(stream)
         M.moe_permute(b.topk_idx, dev["x"], E, cfg.CF, b.counts, b.offsets, b.token_of_row,

@@ -33,8 +33,11 @@
  *     error nothing is launched and a negative MOE_E* code is returned;
  *     moe_last_error() then describes it (per calling thread).  A device
  *     fault surfaces at the caller's next synchronisation as a HIP error.
- *   - Limits: 1 <= k <= E <= 256; 0 <= E_shared <= 16; 1 <= T; T*k < 2^31;
- *     d_model and d_ff multiples of 64 (bf16) or of 4 (fp32).
+ *   - Limits: 1 <= k <= min(E, 64); E <= 256; 0 <= E_shared <= 16; 1 <= T;
+ *     T*k + E_shared*T < 2^31; d_model and d_ff positive multiples of 64
+ *     below 2^24.
+ *   - topk_idx rows must name distinct experts (moe_route writes them so);
+ *     ids outside [0, E) are treated as dropped pairs.
  *
  * Weight layouts (each stored row is one output feature's weights along
  * the contracted dimension, the [out, in] layout of a linear layer):
@@ -80,9 +83,9 @@ const char* moe_last_error(void);
 int moe_capacity(int64_t T, int32_t E, int32_t k, double CF, int64_t* cap);
 
 /*
- * Bytes of device workspace that moe_permute, moe_expert_ffn and
- * moe_aux_stats need for this shape (one buffer serves all three; calls on
- * one stream may share it).  Host only.
+ * Bytes of device workspace that moe_route, moe_permute, moe_expert_ffn
+ * and moe_aux_stats need for this shape (one buffer serves all four; calls
+ * on one stream may share it).  Host only.
  */
 int moe_workspace_size(int64_t T, int64_t d_model, int32_t E, int32_t E_shared,
                        int32_t k, int64_t d_ff, int32_t dtype, size_t* bytes);
@@ -99,10 +102,13 @@ int moe_workspace_size(int64_t T, int64_t d_model, int32_t E, int32_t E_shared,
  *   topk_idx[T, k]  int32            out  expert ids, larger logit first,
  *                                         ties to the lower expert id
  *   topk_w  [T, k]  fp32             out  renormalised weights p~ (sum 1)
+ *   ws      workspace of moe_workspace_size() bytes (used when T is small
+ *           and d is split across blocks; may be NULL otherwise)
  */
 int moe_route(int64_t T, int64_t d_model, int32_t E, int32_t k, int32_t dtype,
               const void* x, const void* w_gate, float* logits,
-              int32_t* topk_idx, float* topk_w, void* stream);
+              int32_t* topk_idx, float* topk_w, void* ws, size_t ws_bytes,
+              void* stream);
 
 /*
  * Counting, capacity, drop and permutation, "CMU 11-868 Lecture 17"

@@ -65,21 +65,21 @@ def test_bad_arguments_are_rejected_before_launch(M):
     fake = ctypes.c_void_p(4096)          # never dereferenced: checks fail first
     odd = ctypes.c_void_p(4097)
     # k > E
-    assert L.moe_route(16, 128, 4, 5, M.MOE_BF16, fake, fake, fake, fake, fake, nil) == -1
+    assert L.moe_route(16, 128, 4, 5, M.MOE_BF16, fake, fake, fake, fake, fake, nil, 0, nil) == -1
     assert "k must be" in L.moe_last_error().decode()
     # null pointer
-    assert L.moe_route(16, 128, 8, 2, M.MOE_BF16, nil, fake, fake, fake, fake, nil) == -1
+    assert L.moe_route(16, 128, 8, 2, M.MOE_BF16, nil, fake, fake, fake, fake, nil, 0, nil) == -1
     assert "x is NULL" in L.moe_last_error().decode()
     # misaligned pointer
-    assert L.moe_route(16, 128, 8, 2, M.MOE_BF16, odd, fake, fake, fake, fake, nil) == -1
+    assert L.moe_route(16, 128, 8, 2, M.MOE_BF16, odd, fake, fake, fake, fake, nil, 0, nil) == -1
     assert "aligned" in L.moe_last_error().decode()
     # unsupported dtype
-    assert L.moe_route(16, 128, 8, 2, 7, fake, fake, fake, fake, fake, nil) == -2
+    assert L.moe_route(16, 128, 8, 2, 7, fake, fake, fake, fake, fake, nil, 0, nil) == -2
     # d not a multiple of 64
-    assert L.moe_route(16, 100, 8, 2, M.MOE_BF16, fake, fake, fake, fake, fake, nil) == -1
+    assert L.moe_route(16, 100, 8, 2, M.MOE_BF16, fake, fake, fake, fake, fake, nil, 0, nil) == -1
     # E too large, T = 0
-    assert L.moe_route(16, 128, 300, 2, M.MOE_BF16, fake, fake, fake, fake, fake, nil) == -1
-    assert L.moe_route(0, 128, 8, 2, M.MOE_BF16, fake, fake, fake, fake, fake, nil) == -1
+    assert L.moe_route(16, 128, 300, 2, M.MOE_BF16, fake, fake, fake, fake, fake, nil, 0, nil) == -1
+    assert L.moe_route(0, 128, 8, 2, M.MOE_BF16, fake, fake, fake, fake, fake, nil, 0, nil) == -1
     # workspace too small
     rc = L.moe_permute(16, 128, 8, 2, 1.25, M.MOE_BF16, fake, fake, fake, fake, fake, fake,
                        fake, fake, fake, 16, nil)
@@ -103,3 +103,15 @@ def test_workspace_size_grows_with_the_shape(M):
     assert 0 < a < b
     # holds the fused intermediate: T*k rows of d_ff bf16 values at least
     assert b >= 16384 * 4 * 10752 * 2
+
+
+def test_decode_router_needs_its_workspace(M):
+    """Few tokens: d is split across blocks, so moe_route needs a workspace."""
+    L = M.lib()
+    nil = ctypes.c_void_p(0)
+    fake = ctypes.c_void_p(4096)
+    rc = L.moe_route(64, 7168, 256, 8, M.MOE_BF16, fake, fake, fake, fake, fake, nil, 0, nil)
+    assert rc == -1 and "ws is NULL" in L.moe_last_error().decode()
+    rc = L.moe_route(64, 7168, 256, 8, M.MOE_BF16, fake, fake, fake, fake, fake, fake, 64, nil)
+    assert rc == -4
+    assert M.moe_workspace_size(64, 7168, 256, 1, 8, 2048, M.MOE_BF16) >= 64 * 64 * 256 * 4

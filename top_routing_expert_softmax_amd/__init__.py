@@ -53,7 +53,7 @@ def lib():
     L.moe_workspace_size.restype = ctypes.c_int
     L.moe_workspace_size.argtypes = [i64, i64, i32, i32, i32, i64, i32, ctypes.POINTER(sz)]
     L.moe_route.restype = ctypes.c_int
-    L.moe_route.argtypes = [i64, i64, i32, i32, i32, vp, vp, vp, vp, vp, vp]
+    L.moe_route.argtypes = [i64, i64, i32, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp]
     L.moe_permute.restype = ctypes.c_int
     L.moe_permute.argtypes = [i64, i64, i32, i32, f64, i32, vp, vp, vp, vp, vp, vp, vp, vp,
                               vp, sz, vp]
@@ -110,11 +110,12 @@ def moe_workspace_size(T, d_model, E, E_shared, k, d_ff, dtype):
     return n.value
 
 
-def moe_route(x, w_gate, k, logits, topk_idx, topk_w, stream=None):
+def moe_route(x, w_gate, k, logits, topk_idx, topk_w, ws, stream=None):
     T, d = x.shape
     E = w_gate.shape[1]
     _check("moe_route", lib().moe_route(T, d, E, k, _dtype_code(x), _ptr(x), _ptr(w_gate),
-                                        _ptr(logits), _ptr(topk_idx), _ptr(topk_w),
+                                        _ptr(logits), _ptr(topk_idx), _ptr(topk_w), _ptr(ws),
+                                        0 if ws is None else ws.numel() * ws.element_size(),
                                         _stream(stream)))
 
 
@@ -193,7 +194,7 @@ def layer_forward(x, w_gate, w1, w3, w2, k, CF, ws1=None, ws3=None, ws2=None, bu
     if bufs is None:
         bufs = MoELayerBuffers(T, d, E, Es, k, F, x.dtype, device=x.device)
     b = bufs
-    moe_route(x, w_gate, k, b.logits, b.topk_idx, b.topk_w, stream)
+    moe_route(x, w_gate, k, b.logits, b.topk_idx, b.topk_w, b.ws, stream)
     moe_permute(b.topk_idx, x, E, CF, b.counts, b.offsets, b.token_of_row, b.row_of_pair,
                 b.drop_mask, b.x_perm, b.ws, stream)
     moe_expert_ffn(T, k, b.x_perm, b.offsets, x, w1, w3, w2, ws1, ws3, ws2, b.y_perm,

@@ -90,10 +90,11 @@ int64_t exact_capacity(int64_t T, int32_t E, int32_t k, double CF) {
 
 size_t align256(size_t b) { return (b + 255) & ~static_cast<size_t>(255); }
 
-size_t workspace_bytes(int64_t T, int64_t /*d*/, int32_t E, int32_t Es, int32_t k, int64_t F,
+size_t workspace_bytes(int64_t T, int64_t d, int32_t E, int32_t Es, int32_t k, int64_t F,
                        int32_t dtype) {
   const int elem = dtype == MOE_BF16 ? 2 : 4;
-  size_t b = moe::permute_workspace_bytes(T, E);
+  size_t b = moe::route_workspace_bytes(T, d, E);
+  b = std::max(b, moe::permute_workspace_bytes(T, E));
   b = std::max(b, moe::stats_workspace_bytes(T, E));
   b = std::max(b, moe::ffn_workspace_bytes(T, E, Es, k, F, elem));
   return align256(b);
@@ -139,8 +140,8 @@ int moe_workspace_size(int64_t T, int64_t d_model, int32_t E, int32_t E_shared, 
 }
 
 int moe_route(int64_t T, int64_t d_model, int32_t E, int32_t k, int32_t dtype, const void* x,
-              const void* w_gate, float* logits, int32_t* topk_idx, float* topk_w,
-              void* stream) {
+              const void* w_gate, float* logits, int32_t* topk_idx, float* topk_w, void* ws,
+              size_t ws_bytes, void* stream) {
   if (int r = check_common(T, E, k)) return r;
   if (int r = check_dtype(dtype)) return r;
   if (int r = check_dim("d_model", d_model)) return r;
@@ -149,9 +150,15 @@ int moe_route(int64_t T, int64_t d_model, int32_t E, int32_t k, int32_t dtype, c
   REQUIRE_PTR(logits);
   REQUIRE_PTR(topk_idx);
   REQUIRE_PTR(topk_w);
+  const size_t need = moe::route_workspace_bytes(T, d_model, E);
+  if (need > 0) {
+    REQUIRE_PTR(ws);
+    if (ws_bytes < need)
+      return fail(MOE_EWORKSPACE, "moe_route needs %zu workspace bytes, got %zu", need, ws_bytes);
+  }
   (void)hipGetLastError();
   return launched(moe::launch_route(T, d_model, E, k, dtype == MOE_BF16, x, w_gate, logits,
-                                    topk_idx, topk_w, static_cast<hipStream_t>(stream)),
+                                    topk_idx, topk_w, ws, static_cast<hipStream_t>(stream)),
                   "moe_route");
 }
 

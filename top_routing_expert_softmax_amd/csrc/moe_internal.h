@@ -17,6 +17,7 @@ constexpr int kMaxDispatchBlocks = 64;
 // Statistics: at most this many partial blocks.
 constexpr int kStatsBlocks = 256;
 
+size_t route_workspace_bytes(int64_t T, int64_t d, int E);
 size_t permute_workspace_bytes(int64_t T, int E);
 size_t stats_workspace_bytes(int64_t T, int E);
 size_t ffn_workspace_bytes(int64_t T, int E, int E_shared, int k, int64_t d_ff,
@@ -24,7 +25,7 @@ size_t ffn_workspace_bytes(int64_t T, int E, int E_shared, int k, int64_t d_ff,
 
 hipError_t launch_route(int64_t T, int64_t d, int E, int k, bool bf16,
                         const void* x, const void* w_gate, float* logits,
-                        int32_t* topk_idx, float* topk_w, hipStream_t s);
+                        int32_t* topk_idx, float* topk_w, void* ws, hipStream_t s);
 
 hipError_t launch_permute(int64_t T, int64_t d, int E, int k, int64_t cap,
                           bool bf16, const int32_t* topk_idx, const void* x,

@@ -1,18 +1,26 @@
 // Fused router: logits g = x W_gate, then top-k and renormalised weights.
 // "MoE routing math", section 2.1.
 //
-// One block owns kTW tokens and all E experts.  Its waves split d into
-// contiguous ranges; inside a wave, lane = es + ES * ds, where es picks EPL
+// A block owns kTW tokens and all E experts over a range of d.  Its waves
+// split that range; inside a wave, lane = es + ES * ds, where es picks EPL
 // consecutive experts and ds interleaves 8-element chunks of d.  Each lane
 // keeps kTW x EPL fp32 accumulators and uses plain fp32 FMAs (no MFMA), so
 // on the dyadic input grid every partial sum is exact and the logits do not
 // depend on the summation order.  Partials are reduced across ds lanes with
-// shuffles, across waves through LDS, and the block then writes the logits.
-// The epilogue gives each token one wavefront: every lane holds up to four
-// logits, k rounds of a wave-wide max over (logit, -index) keys select the
-// experts (larger logit first, ties to the lower index), and the weights are
+// shuffles and across waves through LDS.
+//
+// Many tokens (prefill): one block per kTW tokens covers all of d and runs
+// the top-k epilogue itself.  Few tokens (decode): d is also split across S
+// blocks that write partial logits to the workspace; a select kernel adds
+// the S partials in a fixed order and runs the same top-k.
+//
+// Top-k: one wavefront per token, each lane holding up to four logits; k
+// rounds of a wave-wide max over (order key of the logit, -index) pick the
+// experts, larger logit first and ties to the lower index; the weights are
 // exp(g_j - g_max) / sum over the selected j.
 #include <math.h>
+
+#include <algorithm>
 
 #include "moe_device.h"
 #include "moe_internal.h"
@@ -22,20 +30,21 @@ namespace {
 
 constexpr int kTW = 8;          // tokens per block
 constexpr int kMaxWavesR = 8;   // waves per block at most
+constexpr int kMaxSplits = 64;  // d-splits at most (decode)
 
 __device__ __forceinline__ void load8(const uint16_t* p, float (&v)[8]) {
-  const uint4 q = *reinterpret_cast<const uint4*>(p);
-  v[0] = bf16lo(q.x); v[1] = bf16hi(q.x);
-  v[2] = bf16lo(q.y); v[3] = bf16hi(q.y);
-  v[4] = bf16lo(q.z); v[5] = bf16hi(q.z);
-  v[6] = bf16lo(q.w); v[7] = bf16hi(q.w);
+  const u32x4_t q = *reinterpret_cast<const u32x4_t*>(p);
+  v[0] = bf16lo(q[0]); v[1] = bf16hi(q[0]);
+  v[2] = bf16lo(q[1]); v[3] = bf16hi(q[1]);
+  v[4] = bf16lo(q[2]); v[5] = bf16hi(q[2]);
+  v[6] = bf16lo(q[3]); v[7] = bf16hi(q[3]);
 }
 
 __device__ __forceinline__ void load8(const float* p, float (&v)[8]) {
-  const float4 a = reinterpret_cast<const float4*>(p)[0];
-  const float4 b = reinterpret_cast<const float4*>(p)[1];
-  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-  v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  const f32x4_t a = reinterpret_cast<const f32x4_t*>(p)[0];
+  const f32x4_t b = reinterpret_cast<const f32x4_t*>(p)[1];
+  v[0] = a[0]; v[1] = a[1]; v[2] = a[2]; v[3] = a[3];
+  v[4] = b[0]; v[5] = b[1]; v[6] = b[2]; v[7] = b[3];
 }
 
 __device__ __forceinline__ float load1(const uint16_t* p) { return bf16_to_f32(*p); }
@@ -68,11 +77,10 @@ struct XChunk<float> {
   __device__ __forceinline__ float get(int u) const { return u < 4 ? a[u] : b[u - 4]; }
 };
 
-// EPL consecutive experts of one W_gate row; vec: row is 16-byte aligned
-// and all EPL experts exist.
-template <int EPL>
-__device__ __forceinline__ void load_w(const uint16_t* row, int e0, int E, bool vec,
-                                       float (&w)[EPL]) {
+// EPL consecutive experts of one W_gate row; vec: the row is 16-byte
+// aligned and all EPL experts exist.
+template <int EPL, typename T>
+__device__ __forceinline__ void load_w(const T* row, int e0, int E, bool vec, float (&w)[EPL]) {
   if constexpr (EPL == 8) {
     if (vec) { load8(row + e0, w); return; }
   }
@@ -80,21 +88,53 @@ __device__ __forceinline__ void load_w(const uint16_t* row, int e0, int E, bool 
   for (int e = 0; e < EPL; ++e) w[e] = (e0 + e < E) ? load1(row + e0 + e) : 0.f;
 }
 
-template <int EPL>
-__device__ __forceinline__ void load_w(const float* row, int e0, int E, bool vec,
-                                       float (&w)[EPL]) {
-  if constexpr (EPL == 8) {
-    if (vec) { load8(row + e0, w); return; }
-  }
-#pragma unroll
-  for (int e = 0; e < EPL; ++e) w[e] = (e0 + e < E) ? load1(row + e0 + e) : 0.f;
+__device__ __forceinline__ float from_order_key(uint32_t key) {
+  const uint32_t u = (key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key;
+  return __uint_as_float(u);
 }
 
-template <typename T, int EPL>
+// Top-k of one token held by one wavefront: lane holds logits of experts
+// lane + 64 r (r < 4) in v[r].  Writes k ids and renormalised weights.
+__device__ __forceinline__ void topk_select(const float (&v)[4], int E, int k, int lane,
+                                            int32_t* __restrict__ idx_row,
+                                            float* __restrict__ w_row) {
+  uint32_t taken = 0;
+  float gmax = 0.f, wsum = 0.f, my_w = 0.f;
+  int my_e = 0;
+  for (int j = 0; j < k; ++j) {
+    uint64_t best = 0;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int e = lane + kWave * r;
+      if (e < E && !((taken >> r) & 1u)) {
+        const uint64_t key = (static_cast<uint64_t>(f32_order_key(v[r])) << 32) |
+                             static_cast<uint64_t>(0xFFFFFFFFu - static_cast<uint32_t>(e));
+        best = key > best ? key : best;
+      }
+    }
+    best = wave_max_u64(best);
+    const int e_sel = static_cast<int>(0xFFFFFFFFu - static_cast<uint32_t>(best));
+    const float g_sel = from_order_key(static_cast<uint32_t>(best >> 32));
+    if ((e_sel & (kWave - 1)) == lane) taken |= 1u << (e_sel / kWave);
+    if (j == 0) gmax = g_sel;
+    const float ex = expf(g_sel - gmax);
+    wsum += ex;
+    if (lane == j) { my_w = ex; my_e = e_sel; }
+  }
+  if (lane < k) {
+    idx_row[lane] = my_e;
+    w_row[lane] = my_w / wsum;
+  }
+}
+
+// SPLIT = false: all of d, then the top-k epilogue.  SPLIT = true: the
+// chunk range [blockIdx.y * cps, +cps) of d, partial logits to
+// partial[blockIdx.y][t][e].
+template <typename T, int EPL, bool SPLIT>
 __global__ __launch_bounds__(kMaxWavesR * kWave) void router_kernel(
     const T* __restrict__ x, const T* __restrict__ wg, float* __restrict__ logits,
-    int32_t* __restrict__ topk_idx, float* __restrict__ topk_w, int nT, int d,
-    int E, int k, int ES, int chunks_per_wave) {
+    int32_t* __restrict__ topk_idx, float* __restrict__ topk_w, float* __restrict__ partial,
+    int nT, int d, int E, int k, int ES, int chunks_per_wave, int chunks_per_split) {
   extern __shared__ float smem[];
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
@@ -114,8 +154,10 @@ __global__ __launch_bounds__(kMaxWavesR * kWave) void router_kernel(
     for (int e = 0; e < EPL; ++e) acc[t][e] = 0.f;
 
   const int nchunk = d / 8;
-  const int c_begin = wave * chunks_per_wave;
-  const int c_end = min(nchunk, c_begin + chunks_per_wave);
+  const int split_begin = SPLIT ? blockIdx.y * chunks_per_split : 0;
+  const int split_end = SPLIT ? min(nchunk, split_begin + chunks_per_split) : nchunk;
+  const int c_begin = split_begin + wave * chunks_per_wave;
+  const int c_end = min(split_end, c_begin + chunks_per_wave);
   if (e0 < E) {
     for (int c = c_begin + ds; c < c_end; c += DS) {
       const int i0 = c * 8;
@@ -154,16 +196,16 @@ __global__ __launch_bounds__(kMaxWavesR * kWave) void router_kernel(
       for (int e = 0; e < EPL; ++e) red[(wave * kTW + t) * E_pad + e0 + e] = acc[t][e];
   }
   __syncthreads();
+  float* dst = SPLIT ? partial + static_cast<int64_t>(blockIdx.y) * nT * E : logits;
   for (int q = threadIdx.x; q < kTW * E_pad; q += blockDim.x) {
     float s = 0.f;
     for (int w = 0; w < nwaves; ++w) s += red[w * kTW * E_pad + q];
     lg[q] = s;
     const int t = q / E_pad, e = q % E_pad;
-    if (t0 + t < nT && e < E) logits[static_cast<int64_t>(t0 + t) * E + e] = s;
+    if (t0 + t < nT && e < E) dst[static_cast<int64_t>(t0 + t) * E + e] = s;
   }
+  if (SPLIT) return;
   __syncthreads();
-
-  // Top-k and renormalisation, one wavefront per token.
   for (int tt = wave; tt < kTW; tt += nwaves) {
     const int t = t0 + tt;
     if (t >= nT) break;
@@ -174,79 +216,121 @@ __global__ __launch_bounds__(kMaxWavesR * kWave) void router_kernel(
       const int e = lane + kWave * r;
       v[r] = (e < E) ? row[e] : 0.f;
     }
-    uint32_t taken = 0;
-    float gmax = 0.f, wsum = 0.f, my_w = 0.f;
-    int my_e = 0;
-    for (int j = 0; j < k; ++j) {
-      uint64_t best = 0;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int e = lane + kWave * r;
-        if (e < E && !((taken >> r) & 1u)) {
-          const uint64_t key = (static_cast<uint64_t>(f32_order_key(v[r])) << 32) |
-                               static_cast<uint64_t>(0xFFFFFFFFu - static_cast<uint32_t>(e));
-          best = key > best ? key : best;
-        }
-      }
-      best = wave_max_u64(best);
-      const int e_sel = static_cast<int>(0xFFFFFFFFu - static_cast<uint32_t>(best));
-      const float g_sel = row[e_sel];
-      if ((e_sel & (kWave - 1)) == lane) taken |= 1u << (e_sel / kWave);
-      if (j == 0) gmax = g_sel;
-      const float ex = expf(g_sel - gmax);
-      wsum += ex;
-      if (lane == j) { my_w = ex; my_e = e_sel; }
-    }
-    if (lane < k) {
-      topk_idx[static_cast<int64_t>(t) * k + lane] = my_e;
-      topk_w[static_cast<int64_t>(t) * k + lane] = my_w / wsum;
-    }
+    topk_select(v, E, k, lane, topk_idx + static_cast<int64_t>(t) * k,
+                topk_w + static_cast<int64_t>(t) * k);
   }
 }
 
+// Decode: logits = sum over the S d-splits, s = 0..S-1 in order, then top-k.
+// One wavefront per token, four tokens per block.
+__global__ __launch_bounds__(4 * kWave) void router_select_kernel(
+    const float* __restrict__ partial, float* __restrict__ logits,
+    int32_t* __restrict__ topk_idx, float* __restrict__ topk_w, int nT, int E, int k, int S) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int t = blockIdx.x * 4 + threadIdx.x / kWave;
+  if (t >= nT) return;
+  float v[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int e = lane + kWave * r;
+    float s = 0.f;
+    if (e < E) {
+      for (int sp = 0; sp < S; ++sp) s += partial[(static_cast<int64_t>(sp) * nT + t) * E + e];
+      logits[static_cast<int64_t>(t) * E + e] = s;
+    }
+    v[r] = s;
+  }
+  topk_select(v, E, k, lane, topk_idx + static_cast<int64_t>(t) * k,
+              topk_w + static_cast<int64_t>(t) * k);
+}
+
+struct RouterPlan {
+  int E_pad, ES, EPL, DS;
+  int nblocks, nchunk;
+  int S, cps;               // d-splits and chunks per split
+  int nwaves, cpw;
+};
+
+RouterPlan plan_router(int64_t T, int64_t d, int E) {
+  RouterPlan p;
+  p.E_pad = 1;
+  while (p.E_pad < E) p.E_pad <<= 1;
+  p.EPL = p.E_pad >= 8 ? 8 : p.E_pad;
+  p.ES = p.E_pad / p.EPL;
+  p.DS = kWave / p.ES;
+  p.nblocks = static_cast<int>((T + kTW - 1) / kTW);
+  p.nchunk = static_cast<int>(d / 8);
+  // split d across blocks when there are too few token blocks to fill
+  // the chip (each split keeps at least one chunk per ds lane)
+  p.S = 1;
+  if (p.nblocks < 128) {
+    p.S = (512 + p.nblocks - 1) / p.nblocks;
+    p.S = std::min(p.S, kMaxSplits);
+    p.S = std::min(p.S, std::max(1, p.nchunk / p.DS));
+  }
+  p.cps = (p.nchunk + p.S - 1) / p.S;
+  p.S = (p.nchunk + p.cps - 1) / p.cps;
+  // enough waves to fill the chip, no more than the chunks can feed, and
+  // the reduction buffers within 64 KB of LDS
+  int nw = (2048 + p.nblocks * p.S - 1) / (p.nblocks * p.S);
+  nw = std::min(nw, kMaxWavesR);
+  nw = std::min(nw, std::max(1, p.cps / p.DS));
+  const int lds_per_wave = kTW * p.E_pad * 4;
+  nw = std::min(nw, 65536 / lds_per_wave - 1);
+  p.nwaves = std::max(nw, 1);
+  p.cpw = (p.cps + p.nwaves - 1) / p.nwaves;
+  p.cpw = ((p.cpw + p.DS - 1) / p.DS) * p.DS;
+  return p;
+}
+
 template <typename T, int EPL>
-hipError_t launch_t(int64_t T_, int64_t d, int E, int k, const void* x, const void* wg,
-                    float* logits, int32_t* idx, float* w, int ES, hipStream_t s) {
-  const int E_pad = ES * EPL;
-  const int DS = kWave / ES;
-  const int nblocks = static_cast<int>((T_ + kTW - 1) / kTW);
-  const int nchunk = static_cast<int>(d / 8);
-  // Enough waves to fill the chip, no more than the chunks can feed, and
-  // the reduction buffers within 64 KB of LDS.
-  int nwaves = (2048 + nblocks - 1) / nblocks;
-  nwaves = min(nwaves, kMaxWavesR);
-  nwaves = min(nwaves, max(1, nchunk / DS));
-  const int lds_per_wave = kTW * E_pad * 4;
-  nwaves = min(nwaves, 65536 / lds_per_wave - 1);
-  nwaves = max(nwaves, 1);
-  int cpw = (nchunk + nwaves - 1) / nwaves;
-  cpw = ((cpw + DS - 1) / DS) * DS;
-  const size_t lds = static_cast<size_t>(nwaves + 1) * lds_per_wave;
-  hipLaunchKernelGGL((router_kernel<T, EPL>), dim3(nblocks), dim3(nwaves * kWave), lds, s,
-                     static_cast<const T*>(x), static_cast<const T*>(wg), logits, idx, w,
-                     static_cast<int>(T_), static_cast<int>(d), E, k, ES, cpw);
+hipError_t launch_t(const RouterPlan& p, int64_t T_, int64_t d, int E, int k, const void* x,
+                    const void* wg, float* logits, int32_t* idx, float* w, float* partial,
+                    hipStream_t s) {
+  const size_t lds = static_cast<size_t>(p.nwaves + 1) * kTW * p.E_pad * 4;
+  if (p.S == 1) {
+    hipLaunchKernelGGL((router_kernel<T, EPL, false>), dim3(p.nblocks), dim3(p.nwaves * kWave),
+                       lds, s, static_cast<const T*>(x), static_cast<const T*>(wg), logits, idx,
+                       w, nullptr, static_cast<int>(T_), static_cast<int>(d), E, k, p.ES, p.cpw,
+                       p.cps);
+  } else {
+    hipLaunchKernelGGL((router_kernel<T, EPL, true>), dim3(p.nblocks, p.S),
+                       dim3(p.nwaves * kWave), lds, s, static_cast<const T*>(x),
+                       static_cast<const T*>(wg), logits, idx, w, partial, static_cast<int>(T_),
+                       static_cast<int>(d), E, k, p.ES, p.cpw, p.cps);
+    hipLaunchKernelGGL(router_select_kernel, dim3(static_cast<unsigned>((T_ + 3) / 4)),
+                       dim3(4 * kWave), 0, s, partial, logits, idx, w, static_cast<int>(T_), E, k,
+                       p.S);
+  }
   return hipGetLastError();
 }
 
 template <typename T>
 hipError_t dispatch_epl(int64_t T_, int64_t d, int E, int k, const void* x, const void* wg,
-                        float* logits, int32_t* idx, float* w, hipStream_t s) {
-  int E_pad = 1;
-  while (E_pad < E) E_pad <<= 1;
-  if (E_pad >= 8) return launch_t<T, 8>(T_, d, E, k, x, wg, logits, idx, w, E_pad / 8, s);
-  if (E_pad == 4) return launch_t<T, 4>(T_, d, E, k, x, wg, logits, idx, w, 1, s);
-  if (E_pad == 2) return launch_t<T, 2>(T_, d, E, k, x, wg, logits, idx, w, 1, s);
-  return launch_t<T, 1>(T_, d, E, k, x, wg, logits, idx, w, 1, s);
+                        float* logits, int32_t* idx, float* w, float* partial, hipStream_t s) {
+  const RouterPlan p = plan_router(T_, d, E);
+  switch (p.EPL) {
+    case 8: return launch_t<T, 8>(p, T_, d, E, k, x, wg, logits, idx, w, partial, s);
+    case 4: return launch_t<T, 4>(p, T_, d, E, k, x, wg, logits, idx, w, partial, s);
+    case 2: return launch_t<T, 2>(p, T_, d, E, k, x, wg, logits, idx, w, partial, s);
+    default: return launch_t<T, 1>(p, T_, d, E, k, x, wg, logits, idx, w, partial, s);
+  }
 }
 
 }  // namespace
 
+size_t route_workspace_bytes(int64_t T, int64_t d, int E) {
+  const RouterPlan p = plan_router(T, d, E);
+  return p.S == 1 ? 0 : static_cast<size_t>(p.S) * T * E * sizeof(float);
+}
+
 hipError_t launch_route(int64_t T, int64_t d, int E, int k, bool bf16, const void* x,
-                        const void* w_gate, float* logits, int32_t* topk_idx,
-                        float* topk_w, hipStream_t s) {
+                        const void* w_gate, float* logits, int32_t* topk_idx, float* topk_w,
+                        void* ws, hipStream_t s) {
+  float* partial = static_cast<float*>(ws);
   if (bf16)
-    return dispatch_epl<uint16_t>(T, d, E, k, x, w_gate, logits, topk_idx, topk_w, s);
-  return dispatch_epl<float>(T, d, E, k, x, w_gate, logits, topk_idx, topk_w, s);
+    return dispatch_epl<uint16_t>(T, d, E, k, x, w_gate, logits, topk_idx, topk_w, partial, s);
+  return dispatch_epl<float>(T, d, E, k, x, w_gate, logits, topk_idx, topk_w, partial, s);
 }
 
 }  // namespace moe
