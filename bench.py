@@ -30,6 +30,15 @@ PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3        # MI355X fp32 vector
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 
+# HBM bytes per moe_expert_ffn call measured with rocprofv3 FETCH_SIZE and
+# WRITE_SIZE (scaled by a plain copy of known size), keyed by the workload
+# and the sha256 prefix of the GEMM source they were taken with.  A changed
+# kernel reports null until it is measured again.
+MEASURED_TRAFFIC = {
+    ("mixtral_prefill", "19897c51a0a23860"): 8.605e9,
+    ("dsv3_decode", "19897c51a0a23860"): 1.9786e10,
+}
+
 
 def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
@@ -105,16 +114,33 @@ def cpu_baseline(cfg, x, wg, host, sample_tokens):
     return len(tokens) / dt, threads, len(tokens), dt
 
 
+def copy_calibration(nbytes):
+    """A plain copy of known size: its FETCH_SIZE / WRITE_SIZE readings turn
+    the counters of the layer's kernels into bytes."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": nbytes}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="mixtral_prefill", choices=sorted(CONFIGS))
-    ap.add_argument("--cpu-sample", type=int, default=48,
+    ap.add_argument("--cpu-sample", type=int, default=4096,
                     help="tokens whose expert outputs the oracle computes")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device copy of BYTES bytes (reference for "
+                         "the FETCH_SIZE / WRITE_SIZE counters) and exit")
     args = ap.parse_args()
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(see DESIGN.md for how the layer would shard).", file=sys.stderr)
@@ -189,6 +215,10 @@ def main():
         achieved = flop / (ffn_ms / 1e3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak,
                 "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None}
+    import hashlib
+    with open(os.path.join(ROOT, "top_routing_expert_softmax_amd", "csrc", "ffn.hip"), "rb") as fh:
+        src_hash = hashlib.sha256(fh.read()).hexdigest()[:16]
+    roof["traffic"] = MEASURED_TRAFFIC.get((cfg.name, src_hash))
     roof["kernel"] = "moe_expert_ffn (grouped GEMM phase 1 + phase 2 + tile table)"
     roof["kernel_ms"] = round(ffn_ms, 4)
 

@@ -221,27 +221,36 @@ __global__ __launch_bounds__(kMaxWavesR * kWave) void router_kernel(
   }
 }
 
-// Decode: logits = sum over the S d-splits, s = 0..S-1 in order, then top-k.
-// One wavefront per token, four tokens per block.
-__global__ __launch_bounds__(4 * kWave) void router_select_kernel(
+// Decode: logits = sum over the S d-splits, then top-k.  One block of 256
+// threads per token, thread e < E adds partial[s][t][e] into eight
+// accumulators (s mod 8) that are combined in a fixed order; wavefront 0
+// then selects from the LDS copy of the row.
+__global__ __launch_bounds__(256) void router_select_kernel(
     const float* __restrict__ partial, float* __restrict__ logits,
     int32_t* __restrict__ topk_idx, float* __restrict__ topk_w, int nT, int E, int k, int S) {
-  const int lane = threadIdx.x & (kWave - 1);
-  const int t = blockIdx.x * 4 + threadIdx.x / kWave;
-  if (t >= nT) return;
-  float v[4];
+  __shared__ float row[256];
+  const int t = blockIdx.x;
+  const int e = threadIdx.x;
+  float s8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  if (e < E) {
+    for (int s0 = 0; s0 < S; s0 += 8) {
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int e = lane + kWave * r;
-    float s = 0.f;
-    if (e < E) {
-      for (int sp = 0; sp < S; ++sp) s += partial[(static_cast<int64_t>(sp) * nT + t) * E + e];
-      logits[static_cast<int64_t>(t) * E + e] = s;
+      for (int q = 0; q < 8; ++q)
+        if (s0 + q < S) s8[q] += partial[(static_cast<int64_t>(s0 + q) * nT + t) * E + e];
     }
-    v[r] = s;
   }
-  topk_select(v, E, k, lane, topk_idx + static_cast<int64_t>(t) * k,
-              topk_w + static_cast<int64_t>(t) * k);
+  const float g = ((s8[0] + s8[1]) + (s8[2] + s8[3])) + ((s8[4] + s8[5]) + (s8[6] + s8[7]));
+  if (e < E) logits[static_cast<int64_t>(t) * E + e] = g;
+  row[e] = g;
+  __syncthreads();
+  if (threadIdx.x < kWave) {
+    const int lane = threadIdx.x;
+    float v[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) v[r] = row[lane + kWave * r];
+    topk_select(v, E, k, lane, topk_idx + static_cast<int64_t>(t) * k,
+                topk_w + static_cast<int64_t>(t) * k);
+  }
 }
 
 struct RouterPlan {
@@ -298,9 +307,8 @@ hipError_t launch_t(const RouterPlan& p, int64_t T_, int64_t d, int E, int k, co
                        dim3(p.nwaves * kWave), lds, s, static_cast<const T*>(x),
                        static_cast<const T*>(wg), logits, idx, w, partial, static_cast<int>(T_),
                        static_cast<int>(d), E, k, p.ES, p.cpw, p.cps);
-    hipLaunchKernelGGL(router_select_kernel, dim3(static_cast<unsigned>((T_ + 3) / 4)),
-                       dim3(4 * kWave), 0, s, partial, logits, idx, w, static_cast<int>(T_), E, k,
-                       p.S);
+    hipLaunchKernelGGL(router_select_kernel, dim3(static_cast<unsigned>(T_)), dim3(256), 0, s,
+                       partial, logits, idx, w, static_cast<int>(T_), E, k, p.S);
   }
   return hipGetLastError();
 }
