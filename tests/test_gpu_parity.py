@@ -53,6 +53,17 @@ SMALL_CASES = {
     "bf16_skew_drop": ("skewed_train", dict(T=1024, d_model=256, E=8, k=2, d_ff=256, CF=1.0,
                                             zipf_tau=1.0)),
     "bf16_E256_decode_small": ("dsv3_decode", dict(T=64, d_model=512, d_ff=256)),
+    # fewer 256 x 256 tiles than compute units and K >= 2048: both phases
+    # split K in two and sum the partial tiles
+    "bf16_split_k2": ("mixtral_prefill", dict(T=640, d_model=2048, E=4, k=2, d_ff=2048,
+                                              CF=1.25)),
+    # more tiles than compute units in phase 1: one whole wave of tiles and
+    # a split remainder in the same launch
+    "bf16_split_mixed": ("mixtral_prefill", dict(T=2048, d_model=2048, E=4, k=2, d_ff=2048,
+                                                 CF=1.25)),
+    # phase 1 split in four parts (K = 4096), with a shared expert
+    "bf16_split_k4_shared": ("dsmoe16b_prefill", dict(T=300, d_model=4096, E=4, E_shared=1,
+                                                      k=2, d_ff=1024, CF=1.25)),
 }
 
 

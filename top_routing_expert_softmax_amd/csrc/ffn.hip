@@ -16,10 +16,13 @@
 // Both operands are K-contiguous in memory ([rows][K] activations and
 // [out][in] weights), which is the layout bf16 MFMA operands want.
 //
-// bf16: v_mfma_f32_32x32x16_bf16, fp32 accumulators.  Block = 256 threads
-// (4 wavefronts as 2 x 2), tile BM x 128 B-rows x BK=64, LDS rows padded by
-// 16 bytes so the 16-byte fragment reads of 8 consecutive rows fall in
-// distinct banks.  fp32 (small configs): VALU tiles, correctness path.
+// bf16, large segments: 256 x 256 output tiles, 8 wavefronts, K slices of
+// 64 streamed into a two-slot LDS ring by direct-to-LDS loads,
+// v_mfma_f32_32x32x16_bf16 with fp32 accumulators.  Tiles of the last,
+// partial wave of the chip are split along K and summed in a fixed order
+// (gemm256_kernel).  bf16, decode-sized segments: 128-row tiles with
+// register prefetch (gemm_bf16_kernel).  fp32 (small configs): VALU tiles,
+// the correctness path.
 #include <math.h>
 
 #include "moe_device.h"
@@ -33,6 +36,13 @@ constexpr int kBMf = 64;        // rows per tile (fp32 path)
 constexpr int kBK = 64;
 constexpr int kLdsStride = kBK + 8;   // bf16 elements per LDS row
 constexpr int kThreads = 256;
+
+// Split-K of the last, partial wave of 256 x 256 tiles (see gemm256_kernel):
+// at most kMaxSplit parts per tile, each at least kMinSplitSlices K slices,
+// and at most kMaxCUs partial tiles in flight.
+constexpr int kMaxSplit = 4;
+constexpr int kMinSplitSlices = 16;
+constexpr int kMaxCUs = 256;
 
 // K-slice depth and LDS ring length of the 256 x 256 bf16 kernel.
 #ifndef MOE_GEMM_BK
@@ -57,6 +67,8 @@ struct FfnArgs {
   void* y_shared;
   const int4* tiles;     // (segment, A row, rows, H row)
   const int* ntiles;
+  float* sk_partial;     // split-K partial tiles of the last wave (256 x 256 fp32 each)
+  unsigned* sk_count;    // arrivals per split tile: [2][kMaxCUs], phase 1 then 2
   int T, d, E, Es, k, F;
 };
 
@@ -65,9 +77,13 @@ struct FfnArgs {
 __global__ __launch_bounds__(kWave) void tile_table_kernel(const int32_t* __restrict__ offsets,
                                                           int4* __restrict__ tiles,
                                                           int* __restrict__ ntiles, int E,
-                                                          int Es, int T, int k, int BM) {
+                                                          int Es, int T, int k, int BM,
+                                                          unsigned* __restrict__ sk_count) {
   // One wavefront; each lane owns up to 5 segments (E + Es <= 272 < 320).
   const int lane = threadIdx.x;
+  // arrival counters of the split tiles start at zero in every call
+  if (sk_count != nullptr)
+    for (int i = lane; i < 2 * kMaxCUs; i += kWave) sk_count[i] = 0u;
   const int nseg = E + Es;
   int cnt[5];
   int tot = 0;
@@ -304,9 +320,69 @@ __device__ __forceinline__ void lds_dma16(const void* gptr, uint32_t* lds_row_ba
   __builtin_amdgcn_global_load_lds(gptr, lds_row_base, 16, 0, 0);
 }
 
+// K loop of one wave: stream slices of A and B into the LDS ring with DMA
+// loads and run the wave's MFMAs on them.  MIA (0..4) is the number of the
+// wave's four 32-row blocks that hold segment rows; the others take no
+// MFMA work.  Every wave of the block runs the same loads and barriers.
+template <int BKT, int NST, int NI, int NB, int MIA>
+__device__ __forceinline__ void gemm256_mainloop(
+    f32x16_t (&acc)[4][NB], const uint16_t* const (&asrc)[NI],
+    const uint16_t* const (&bsrc)[NI], char* lds_bytes,
+    int a_dst, int b_dst, const int (&a_off)[4], const int (&b_off)[NB], int lane, int nk) {
+  using G = SliceGeom<BKT>;
+#define MOE_ISSUE_SLICE(slot, k0)                                                          \
+  _Pragma("unroll") for (int i = 0; i < NI; ++i) {                                         \
+    lds_dma16(asrc[i] + (k0), reinterpret_cast<uint32_t*>(                                \
+                  lds_bytes + (slot) * G::STAGE + a_dst + i * G::RPI * G::ROW));          \
+    lds_dma16(bsrc[i] + (k0), reinterpret_cast<uint32_t*>(                                \
+                  lds_bytes + (slot) * G::STAGE + b_dst + i * G::RPI * G::ROW));          \
+  }
+  // fragment rows are 32-aligned bases + lane%32, so the swizzle key of
+  // all of this lane's fragment rows is ((lane % 32) / RPL) % CH
+  const int key = ((lane & 31) / G::RPL) % G::CH;
+  const int khalf = lane >> 5;
+  // prologue: slices 0 .. NST-2 in flight
+#pragma unroll
+  for (int s0 = 0; s0 < NST - 1; ++s0)
+    if (s0 < nk) { MOE_ISSUE_SLICE(s0, s0 * BKT); }
+  for (int kt = 0; kt < nk; ++kt) {
+    const int slot = kt % NST;
+    // slice kt has landed once at most (NST-2) younger slices are pending
+    if (kt + NST - 2 < nk) {
+      wait_vmcnt<(NST - 2) * 2 * NI>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    __syncthreads();            // every wave's part of slice kt is in LDS, and
+                                // slot (kt-1) % NST is no longer read
+    if (kt + NST - 1 < nk) {
+      const int s_next = kt + NST - 1;
+      MOE_ISSUE_SLICE(s_next % NST, s_next * BKT);
+    }
+    if (MIA == 0) continue;
+    const char* sb = lds_bytes + slot * G::STAGE;
+#pragma unroll
+    for (int ks = 0; ks < BKT / 16; ++ks) {
+      const int pc = ((2 * ks + khalf) ^ key) * 16;
+      bf16x8_t fa[MIA > 0 ? MIA : 1], fb[NB];
+#pragma unroll
+      for (int mi = 0; mi < MIA; ++mi) fa[mi] = *reinterpret_cast<const bf16x8_t*>(sb + a_off[mi] + pc);
+#pragma unroll
+      for (int ni = 0; ni < NB; ++ni) fb[ni] = *reinterpret_cast<const bf16x8_t*>(sb + b_off[ni] + pc);
+#pragma unroll
+      for (int mi = 0; mi < MIA; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < NB; ++ni)
+          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[mi], fb[ni], acc[mi][ni], 0, 0, 0);
+      __builtin_amdgcn_iglp_opt(0);
+    }
+  }
+#undef MOE_ISSUE_SLICE
+}
+
 template <int PHASE, int BKT, int NST, int WAVES>
 __global__ __launch_bounds__(WAVES * kWave) __attribute__((amdgpu_waves_per_eu(WAVES / 4, WAVES / 4)))
-void gemm256_kernel(FfnArgs a, int NT) {
+void gemm256_kernel(FfnArgs a, int NT, int ncu) {
   using G = SliceGeom<BKT>;
   constexpr int WN = WAVES / 2;             // waves along N (2 along M)
   constexpr int WROWS = kBM2 / WAVES;       // tile rows each wave loads per operand
@@ -315,15 +391,46 @@ void gemm256_kernel(FfnArgs a, int NT) {
   static_assert(NI >= 1 && NB >= 2 && NB % 2 == 0, "tile geometry");
   extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
 
-  // ---- which tile
+  // ---- which tile, and which part of its K range
+  // The L = MT * NT tiles fill L / ncu whole waves of the chip (one block
+  // per CU).  A partial last wave of r tiles would leave CUs idle, so
+  // those r tiles are split along K into S parts that run as separate
+  // blocks; each part writes an fp32 partial tile, and the block that
+  // arrives last sums the S partials in part order (so the result does not
+  // depend on arrival order) and runs the epilogue.
   const int MT = *a.ntiles;
   const int L = MT * NT;
-  const int chunk = (L + kXcds - 1) / kXcds;
-  const int xcd = blockIdx.x % kXcds;
-  const int j = blockIdx.x / kXcds;
-  if (j >= chunk) return;
-  const int pid = xcd * chunk + j;
-  if (pid >= L) return;
+  const int K = PHASE == 1 ? a.d : a.F;
+  const int nk_all = K / BKT;
+  const int r = L % ncu;
+  int S = 1;
+  if (r > 0) {
+    const int rr = (r + kXcds - 1) / kXcds * kXcds;
+    S = min(min(kMaxSplit, ncu / rr), nk_all / kMinSplitSlices);
+    if (S < 2) S = 1;
+  }
+  const int D = S > 1 ? L - r : L;              // tiles that run whole
+  const int chunk = (D + kXcds - 1) / kXcds;
+  const int b = blockIdx.x;
+  int pid, part = 0, tile_sk = 0;
+  const bool split_unit = b >= kXcds * chunk;
+  if (!split_unit) {
+    const int xcd = b % kXcds;
+    const int j = b / kXcds;
+    pid = xcd * chunk + j;
+    if (pid >= D) return;
+  } else {
+    if (S == 1) return;
+    // the S parts of a split tile go to blocks of one XCD
+    const int u = b - kXcds * chunk;
+    tile_sk = u % kXcds + kXcds * (u / (kXcds * S));
+    part = (u / kXcds) % S;
+    if (tile_sk >= r) return;
+    pid = D + tile_sk;
+  }
+  const int parts = split_unit ? S : 1;         // whole tiles take all of K
+  const int kb = part * nk_all / parts;
+  const int nk = (part + 1) * nk_all / parts - kb;
   const int group = pid / (kGM * NT);
   const int first_m = group * kGM;
   const int gm = min(kGM, MT - first_m);
@@ -341,7 +448,6 @@ void gemm256_kernel(FfnArgs a, int NT) {
   const int wave = tid / kWave;
   const int wm = wave / WN, wn = wave % WN;
 
-  const int K = PHASE == 1 ? a.d : a.F;
   const int N = PHASE == 1 ? a.F : a.d;
   const int n0 = nt * (PHASE == 1 ? kBN2 / 2 : kBN2);
   const uint16_t* A = PHASE == 1
@@ -360,7 +466,7 @@ void gemm256_kernel(FfnArgs a, int NT) {
     const int r = wave * WROWS + i * G::RPI + lane / G::CH;
     const int lchunk = (lane % G::CH) ^ ((r / G::RPL) % G::CH);
     const int ra = r < mrows ? r : mrows - 1;
-    asrc[i] = A + static_cast<int64_t>(ra) * K + lchunk * 8;
+    asrc[i] = A + static_cast<int64_t>(ra) * K + kb * BKT + lchunk * 8;
     int col;
     const uint16_t* W;
     if (PHASE == 1) {
@@ -371,19 +477,11 @@ void gemm256_kernel(FfnArgs a, int NT) {
       W = static_cast<const uint16_t*>(routed ? a.w2 : a.ws2);
     }
     col = col < N ? col : N - 1;
-    bsrc[i] = W + e * wstride + static_cast<int64_t>(col) * K + lchunk * 8;
+    bsrc[i] = W + e * wstride + static_cast<int64_t>(col) * K + kb * BKT + lchunk * 8;
   }
   char* lds_bytes = reinterpret_cast<char*>(lds);
   const int a_dst = wave * WROWS * G::ROW;
   const int b_dst = kBM2 * G::ROW + wave * WROWS * G::ROW;
-
-#define MOE_ISSUE_SLICE(slot, k0)                                                          \
-  _Pragma("unroll") for (int i = 0; i < NI; ++i) {                                         \
-    lds_dma16(asrc[i] + (k0), reinterpret_cast<uint32_t*>(                                \
-                  lds_bytes + (slot) * G::STAGE + a_dst + i * G::RPI * G::ROW));          \
-    lds_dma16(bsrc[i] + (k0), reinterpret_cast<uint32_t*>(                                \
-                  lds_bytes + (slot) * G::STAGE + b_dst + i * G::RPI * G::ROW));          \
-  }
 
   f32x16_t acc[4][NB];
 #pragma unroll
@@ -405,48 +503,62 @@ void gemm256_kernel(FfnArgs a, int NT) {
         : (wn * (kBN2 / WN) + ni * 32 + (lane & 31));
     b_off[ni] = kBM2 * G::ROW + r * G::ROW;
   }
-  // fragment rows are 32-aligned bases + lane%32, so the swizzle key of
-  // all of this lane's fragment rows is ((lane % 32) / RPL) % CH
-  const int key = ((lane & 31) / G::RPL) % G::CH;
-  const int khalf = lane >> 5;
-
-  const int nk = K / BKT;
-  // prologue: slices 0 .. NST-2 in flight
-#pragma unroll
-  for (int s0 = 0; s0 < NST - 1; ++s0)
-    if (s0 < nk) { MOE_ISSUE_SLICE(s0, s0 * BKT); }
-  for (int kt = 0; kt < nk; ++kt) {
-    const int slot = kt % NST;
-    // slice kt has landed once at most (NST-2) younger slices are pending
-    if (kt + NST - 2 < nk) {
-      wait_vmcnt<(NST - 2) * 2 * NI>();
-    } else {
-      wait_vmcnt<0>();
-    }
-    __syncthreads();            // every wave's part of slice kt is in LDS, and
-                                // slot (kt-1) % NST is no longer read
-    if (kt + NST - 1 < nk) {
-      const int s_next = kt + NST - 1;
-      MOE_ISSUE_SLICE(s_next % NST, s_next * BKT);
-    }
-    const char* sb = lds_bytes + slot * G::STAGE;
-#pragma unroll
-    for (int ks = 0; ks < BKT / 16; ++ks) {
-      const int pc = ((2 * ks + khalf) ^ key) * 16;
-      bf16x8_t fa[4], fb[NB];
-#pragma unroll
-      for (int mi = 0; mi < 4; ++mi) fa[mi] = *reinterpret_cast<const bf16x8_t*>(sb + a_off[mi] + pc);
-#pragma unroll
-      for (int ni = 0; ni < NB; ++ni) fb[ni] = *reinterpret_cast<const bf16x8_t*>(sb + b_off[ni] + pc);
-#pragma unroll
-      for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < NB; ++ni)
-          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[mi], fb[ni], acc[mi][ni], 0, 0, 0);
-      __builtin_amdgcn_iglp_opt(0);
-    }
+  // 32-row blocks of this wave's 128 rows that hold segment rows: a tail
+  // tile runs MFMAs only for those.
+  const int rows_w = mrows - wm * 128;
+  const int mia = __builtin_amdgcn_readfirstlane(
+      rows_w <= 0 ? 0 : (rows_w >= 128 ? 4 : (rows_w + 31) / 32));
+  switch (mia) {
+    case 4: gemm256_mainloop<BKT, NST, NI, NB, 4>(acc, asrc, bsrc, lds_bytes, a_dst, b_dst, a_off, b_off, lane, nk); break;
+    case 3: gemm256_mainloop<BKT, NST, NI, NB, 3>(acc, asrc, bsrc, lds_bytes, a_dst, b_dst, a_off, b_off, lane, nk); break;
+    case 2: gemm256_mainloop<BKT, NST, NI, NB, 2>(acc, asrc, bsrc, lds_bytes, a_dst, b_dst, a_off, b_off, lane, nk); break;
+    case 1: gemm256_mainloop<BKT, NST, NI, NB, 1>(acc, asrc, bsrc, lds_bytes, a_dst, b_dst, a_off, b_off, lane, nk); break;
+    default: gemm256_mainloop<BKT, NST, NI, NB, 0>(acc, asrc, bsrc, lds_bytes, a_dst, b_dst, a_off, b_off, lane, nk); break;
   }
-#undef MOE_ISSUE_SLICE
+
+  if (split_unit) {
+    // Partial tile in accumulator order: float4 q of accumulator (mi, ni)
+    // of thread tid sits at ((mi * NB + ni) * 4 + q) * NTHR + tid.
+    constexpr int NTHR = WAVES * kWave;
+    f32x4_t* mine = reinterpret_cast<f32x4_t*>(a.sk_partial) +
+                    static_cast<int64_t>(tile_sk * S + part) * (kBM2 * kBN2 / 4);
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < NB; ++ni)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          f32x4_t v = {acc[mi][ni][4 * q], acc[mi][ni][4 * q + 1], acc[mi][ni][4 * q + 2],
+                       acc[mi][ni][4 * q + 3]};
+          mine[((mi * NB + ni) * 4 + q) * NTHR + tid] = v;
+        }
+    // Release the partial device-wide, then count the arrival; the last of
+    // the S parts takes the tile.
+    __threadfence();
+    __syncthreads();
+    int* flag = reinterpret_cast<int*>(lds_bytes + NST * G::STAGE);
+    if (tid == 0) {
+      *flag = atomicAdd(&a.sk_count[(PHASE - 1) * kMaxCUs + tile_sk], 1u) ==
+              static_cast<unsigned>(S - 1);
+    }
+    __syncthreads();
+    if (*flag == 0) return;
+    __threadfence();            // acquire: the other parts' partials
+    const f32x4_t* first = reinterpret_cast<const f32x4_t*>(a.sk_partial) +
+                           static_cast<int64_t>(tile_sk * S) * (kBM2 * kBN2 / 4);
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < NB; ++ni)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int64_t at = ((mi * NB + ni) * 4 + q) * NTHR + tid;
+          f32x4_t v = first[at];
+          for (int p = 1; p < S; ++p) v += first[static_cast<int64_t>(p) * (kBM2 * kBN2 / 4) + at];
+#pragma unroll
+          for (int c = 0; c < 4; ++c) acc[mi][ni][4 * q + c] = v[c];
+        }
+  }
 
   // ---- epilogue (accumulator element v of lane l: row 8*(v/4) + 4*(l/32)
   // + v%4, column l%32 of its 32 x 32 block)
@@ -496,15 +608,19 @@ constexpr int kNSTsel = MOE_GEMM_NST;
 constexpr int kWavesSel = MOE_GEMM_WAVES;
 
 template <int PHASE>
-hipError_t launch_gemm256(const FfnArgs& a, int nt, int64_t mt, hipStream_t s) {
-  const unsigned g = static_cast<unsigned>(kXcds * ((mt * nt + kXcds - 1) / kXcds));
-  constexpr size_t lds = static_cast<size_t>(kNSTsel) * SliceGeom<kBKsel>::STAGE;
+hipError_t launch_gemm256(const FfnArgs& a, int nt, int64_t mt, int ncu, hipStream_t s) {
+  // whole-tile blocks (at most every tile, in XCD-sized steps) plus one
+  // wave of split-K blocks
+  const int64_t lmax = mt * nt;
+  const unsigned g = static_cast<unsigned>(kXcds * ((lmax + kXcds - 1) / kXcds) + ncu);
+  // the LDS ring, then one word for the split-K arrival flag
+  constexpr size_t lds = static_cast<size_t>(kNSTsel) * SliceGeom<kBKsel>::STAGE + 16;
   auto kern = &gemm256_kernel<PHASE, kBKsel, kNSTsel, kWavesSel>;
   static const hipError_t attr = hipFuncSetAttribute(
       reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
       static_cast<int>(lds));
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL(kern, dim3(g), dim3(kWavesSel * kWave), lds, s, a, nt);
+  hipLaunchKernelGGL(kern, dim3(g), dim3(kWavesSel * kWave), lds, s, a, nt, ncu);
   return hipGetLastError();
 }
 
@@ -617,11 +733,19 @@ size_t align256(size_t b) { return (b + 255) & ~static_cast<size_t>(255); }
 
 }  // namespace
 
+// Workspace: tile count and table, the bf16 split-K partial tiles and
+// arrival counters, then the intermediate H.
+size_t ffn_sk_bytes(int elem_bytes) {
+  return elem_bytes == 2 ? static_cast<size_t>(kMaxCUs) * kBM2 * kBN2 * sizeof(float) +
+                               align256(2 * kMaxCUs * sizeof(unsigned))
+                         : 0;
+}
+
 size_t ffn_workspace_bytes(int64_t T, int E, int E_shared, int k, int64_t d_ff,
                            int elem_bytes) {
   const int64_t tiles = max_tiles(T, E, E_shared, k, kBMf);   // the smaller BM bounds both
   const int64_t hrows = T * k + static_cast<int64_t>(E_shared) * T;
-  return 256 + align256(static_cast<size_t>(tiles) * sizeof(int4)) +
+  return 256 + align256(static_cast<size_t>(tiles) * sizeof(int4)) + ffn_sk_bytes(elem_bytes) +
          static_cast<size_t>(hrows) * d_ff * elem_bytes;
 }
 
@@ -634,23 +758,36 @@ hipError_t launch_expert_ffn(int64_t T, int64_t d, int E, int E_shared, int k, i
   int* ntiles = reinterpret_cast<int*>(base);
   int4* tiles = reinterpret_cast<int4*>(base + 256);
   const int64_t tiles_cap = max_tiles(T, E, E_shared, k, kBMf);
-  void* H = base + 256 + align256(static_cast<size_t>(tiles_cap) * sizeof(int4));
+  char* sk = base + 256 + align256(static_cast<size_t>(tiles_cap) * sizeof(int4));
+  float* sk_partial = bf16 ? reinterpret_cast<float*>(sk) : nullptr;
+  unsigned* sk_count =
+      bf16 ? reinterpret_cast<unsigned*>(sk + static_cast<size_t>(kMaxCUs) * kBM2 * kBN2 * 4)
+           : nullptr;
+  void* H = sk + ffn_sk_bytes(bf16 ? 2 : 4);
 
   // Large segments take the 256 x 256 tiles; decode-sized ones (few rows
   // per expert) the 128-row tiles.
   const int BM = !bf16 ? kBMf : (T * k >= 64LL * E ? kBM2 : kBM);
   hipLaunchKernelGGL(tile_table_kernel, dim3(1), dim3(kWave), 0, s, offsets, tiles, ntiles, E,
-                     E_shared, static_cast<int>(T), k, BM);
+                     E_shared, static_cast<int>(T), k, BM, sk_count);
   FfnArgs a{x_perm, x, offsets, w1, w3, w2, ws1, ws3, ws2, H, y_perm, y_shared, tiles, ntiles,
+            sk_partial, sk_count,
             static_cast<int>(T), static_cast<int>(d), E, E_shared, k, static_cast<int>(F)};
   const unsigned gx = static_cast<unsigned>(max_tiles(T, E, E_shared, k, BM));
   if (bf16 && BM == kBM2) {
     const int nt1 = static_cast<int>((F + kBN2 / 2 - 1) / (kBN2 / 2));
     const int nt2 = static_cast<int>((d + kBN2 - 1) / kBN2);
     const int64_t mt = max_tiles(T, E, E_shared, k, kBM2);
-    hipError_t err = launch_gemm256<1>(a, nt1, mt, s);
+    // compute units of the current device: one 256 x 256 block fits a CU
+    int dev = 0, ncu = 0;
+    hipError_t err = hipGetDevice(&dev);
+    if (err == hipSuccess)
+      err = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
     if (err != hipSuccess) return err;
-    err = launch_gemm256<2>(a, nt2, mt, s);
+    ncu = max(kXcds, min(ncu, kMaxCUs));
+    err = launch_gemm256<1>(a, nt1, mt, ncu, s);
+    if (err != hipSuccess) return err;
+    err = launch_gemm256<2>(a, nt2, mt, ncu, s);
     if (err != hipSuccess) return err;
   } else if (bf16) {
     hipLaunchKernelGGL(gemm_bf16_kernel<1>, dim3(gx, static_cast<unsigned>((F + 63) / 64)),
