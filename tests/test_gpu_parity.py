@@ -53,6 +53,10 @@ SMALL_CASES = {
     "bf16_skew_drop": ("skewed_train", dict(T=1024, d_model=256, E=8, k=2, d_ff=256, CF=1.0,
                                             zipf_tau=1.0)),
     "bf16_E256_decode_small": ("dsv3_decode", dict(T=64, d_model=512, d_ff=256)),
+    # decode-sized segments streamed, K long enough for the two-batch
+    # pipeline and its remainder; a shared expert with 48 rows (3 groups)
+    "bf16_decode_stream": ("dsv3_decode", dict(T=48, d_model=2048, E=64, E_shared=1, k=4,
+                                               d_ff=1024)),
     # fewer 256 x 256 tiles than compute units and K >= 2048: both phases
     # split K in two and sum the partial tiles
     "bf16_split_k2": ("mixtral_prefill", dict(T=640, d_model=2048, E=4, k=2, d_ff=2048,
@@ -101,11 +105,15 @@ def test_x_perm_is_exact_copy_and_runs_are_deterministic():
     R = int(b.offsets[-1].item())
     tor = b.token_of_row[:R].long()
     assert torch.equal(b.x_perm[:R], inp.x_dev[tor])
-    first = {n: getattr(b, n).clone() for n in ("logits", "topk_idx", "topk_w", "row_of_pair",
-                                                "y", "y_perm", "f", "P", "scalars")}
+    # rows of y_perm past R are never written (their contents are undefined)
+    outs = {"y_perm": lambda bb: bb.y_perm[:R]}
+    for n in ("logits", "topk_idx", "topk_w", "row_of_pair", "y", "y_shared", "f", "P",
+              "scalars"):
+        outs[n] = lambda bb, n=n: getattr(bb, n)
+    first = {n: get(b).clone() for n, get in outs.items()}
     b2 = H.run_gpu(inp, bufs=b)
-    for n, v in first.items():
-        assert torch.equal(getattr(b2, n), v), f"{n} differs between runs"
+    for n, get in outs.items():
+        assert torch.equal(get(b2), first[n]), f"{n} differs between runs"
 
 
 FULL = ["mixtral_prefill", "dsv3_decode", "dsmoe16b_prefill", "skewed_train"]

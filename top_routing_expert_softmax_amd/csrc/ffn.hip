@@ -141,6 +141,8 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(FfnArgs a) {
   const int seg = tl.x, arow0 = tl.y, mrows = tl.z, hrow0 = tl.w;
   const bool routed = seg < a.E;
   const int e = routed ? seg : seg - a.E;
+  // segments of at most kStreamMaxRows rows belong to the streaming kernels
+  if ((routed ? a.offsets[seg + 1] - a.offsets[seg] : a.T) <= kStreamMaxRows) return;
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -768,8 +770,11 @@ hipError_t launch_expert_ffn(int64_t T, int64_t d, int E, int E_shared, int k, i
   // Large segments take the 256 x 256 tiles; decode-sized ones (few rows
   // per expert) the 128-row tiles.
   const int BM = !bf16 ? kBMf : (T * k >= 64LL * E ? kBM2 : kBM);
-  hipLaunchKernelGGL(tile_table_kernel, dim3(1), dim3(kWave), 0, s, offsets, tiles, ntiles, E,
-                     E_shared, static_cast<int>(T), k, BM, sk_count);
+  // decode-sized calls with T <= kStreamMaxRows only stream (no tiles)
+  const bool stream_only = bf16 && BM == kBM && T <= kStreamMaxRows;
+  if (!stream_only)
+    hipLaunchKernelGGL(tile_table_kernel, dim3(1), dim3(kWave), 0, s, offsets, tiles, ntiles, E,
+                       E_shared, static_cast<int>(T), k, BM, sk_count);
   FfnArgs a{x_perm, x, offsets, w1, w3, w2, ws1, ws3, ws2, H, y_perm, y_shared, tiles, ntiles,
             sk_partial, sk_count,
             static_cast<int>(T), static_cast<int>(d), E, E_shared, k, static_cast<int>(F)};
@@ -790,10 +795,22 @@ hipError_t launch_expert_ffn(int64_t T, int64_t d, int E, int E_shared, int k, i
     err = launch_gemm256<2>(a, nt2, mt, ncu, s);
     if (err != hipSuccess) return err;
   } else if (bf16) {
-    hipLaunchKernelGGL(gemm_bf16_kernel<1>, dim3(gx, static_cast<unsigned>((F + 63) / 64)),
-                       dim3(kThreads), 0, s, a);
-    hipLaunchKernelGGL(gemm_bf16_kernel<2>, dim3(gx, static_cast<unsigned>((d + 127) / 128)),
-                       dim3(kThreads), 0, s, a);
+    // Decode-sized: segments of at most kStreamMaxRows rows stream their
+    // weights; larger ones (possible only when T exceeds that) take the
+    // 128-row tiles.
+    const bool tiled = !stream_only;
+    hipError_t err = launch_ffn_stream(1, T, d, E, E_shared, k, F, x_perm, offsets, x, w1, w3, w2,
+                                       ws1, ws3, ws2, H, y_perm, y_shared, s);
+    if (err != hipSuccess) return err;
+    if (tiled)
+      hipLaunchKernelGGL(gemm_bf16_kernel<1>, dim3(gx, static_cast<unsigned>((F + 63) / 64)),
+                         dim3(kThreads), 0, s, a);
+    err = launch_ffn_stream(2, T, d, E, E_shared, k, F, x_perm, offsets, x, w1, w3, w2, ws1, ws3,
+                            ws2, H, y_perm, y_shared, s);
+    if (err != hipSuccess) return err;
+    if (tiled)
+      hipLaunchKernelGGL(gemm_bf16_kernel<2>, dim3(gx, static_cast<unsigned>((d + 127) / 128)),
+                         dim3(kThreads), 0, s, a);
   } else {
     hipLaunchKernelGGL(gemm_f32_kernel<1>, dim3(gx, static_cast<unsigned>((F + 31) / 32)),
                        dim3(kThreads), 0, s, a);

@@ -1,0 +1,253 @@
+// Expert FFN of decode-sized segments: weight streaming.
+//
+// In a decode step each touched expert sees only a few tokens while all of
+// its weights are read ("CMU 11-868 Lecture 17", section 1.4: with a batch
+// of 64 tokens DeepSeek-V3 touches about 222 of 256 experts, two tokens
+// each), so the expert FFN is bound by HBM bandwidth.  Here every weight
+// byte is read once, straight from HBM into registers, and goes through
+// v_mfma_f32_16x16x32_bf16 against the segment's (at most 64) token rows;
+// the matrix unit has time to spare, so no LDS staging is needed.
+//
+// Work split.  A block of 4 wavefronts owns one group of weight rows of one
+// segment: phase 1 takes 16 rows of W1 and the same 16 rows of W3 (16
+// columns of H), phase 2 takes 32 rows of W2 (32 output columns).  Its
+// waves stream the four quarters of the contracted dimension; the four
+// partial sums meet in LDS and are added in wave order (deterministic),
+// then phase 1 applies SiLU(gate) * up and rounds H to bf16.
+//
+// Fragments (16 x 16 x 32 MFMA, lane l): the A operand holds token
+// l % 16 of a 16-token group and the B operand weight row l % 16 of a
+// 16-row group, both for contracted indices 8 * (l / 16) .. +7 of a 32-wide
+// step; accumulator element v of lane l is token 4 * (l / 16) + v, weight
+// row l % 16.  Token rows past the segment read its last row; their sums
+// are never stored.
+#include "moe_device.h"
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+constexpr int kSWaves = 4;               // waves per block (K quarters)
+constexpr int kSNB = 2;                  // 16-row weight fragments per K step
+
+#ifndef MOE_STREAM_NT
+#define MOE_STREAM_NT 0
+#endif
+#ifndef MOE_STREAM_U
+#define MOE_STREAM_U 4
+#endif
+#ifndef MOE_STREAM_PIPE
+#define MOE_STREAM_PIPE 1
+#endif
+
+template <typename V>
+__device__ __forceinline__ V wload(const V* p) {
+#if MOE_STREAM_NT
+  return __builtin_nontemporal_load(p);
+#else
+  return *p;
+#endif
+}
+
+struct StreamArgs {
+  const void* x_perm;
+  const void* x;
+  const int32_t* offsets;
+  const void* w1;
+  const void* w3;
+  const void* w2;
+  const void* ws1;
+  const void* ws3;
+  const void* ws2;
+  void* H;
+  void* y_perm;
+  void* y_shared;
+  int T, d, E, Es, k, F;
+};
+
+__device__ __forceinline__ float silu_s(float g) { return g / (1.0f + __expf(-g)); }
+
+// One block, TG groups of 16 tokens.  U = K steps loaded per batch.
+template <int PHASE, int TG>
+__device__ __forceinline__ void stream_block(const StreamArgs& a, int seg, int rows, int arow0,
+                                             int hrow0, float* red) {
+  constexpr int U = TG == 1 ? MOE_STREAM_U : (TG == 2 ? (MOE_STREAM_U + 1) / 2 : 1);
+  const bool routed = seg < a.E;
+  const int e = routed ? seg : seg - a.E;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int K = PHASE == 1 ? a.d : a.F;
+  const int64_t wstride = static_cast<int64_t>(a.F) * a.d;
+
+  // weight rows of the two B fragments
+  const uint16_t* wrow[kSNB];
+  int n0;
+  if (PHASE == 1) {
+    n0 = blockIdx.x * 16;                      // H columns n0 .. n0+15
+    const uint16_t* W1 = static_cast<const uint16_t*>(routed ? a.w1 : a.ws1) + e * wstride;
+    const uint16_t* W3 = static_cast<const uint16_t*>(routed ? a.w3 : a.ws3) + e * wstride;
+    wrow[0] = W1 + static_cast<int64_t>(n0 + (lane & 15)) * K;
+    wrow[1] = W3 + static_cast<int64_t>(n0 + (lane & 15)) * K;
+  } else {
+    n0 = blockIdx.x * 32;                      // output columns n0 .. n0+31
+    const uint16_t* W2 = static_cast<const uint16_t*>(routed ? a.w2 : a.ws2) + e * wstride;
+    wrow[0] = W2 + static_cast<int64_t>(n0 + (lane & 15)) * K;
+    wrow[1] = W2 + static_cast<int64_t>(n0 + 16 + (lane & 15)) * K;
+  }
+  // token rows of the TG A fragments
+  const uint16_t* arow[TG];
+  const uint16_t* Abase = PHASE == 1
+      ? static_cast<const uint16_t*>(routed ? a.x_perm : a.x) + static_cast<int64_t>(arow0) * K
+      : static_cast<const uint16_t*>(a.H) + static_cast<int64_t>(hrow0) * K;
+#pragma unroll
+  for (int tg = 0; tg < TG; ++tg) {
+    const int m = min(tg * 16 + (lane & 15), rows - 1);
+    arow[tg] = Abase + static_cast<int64_t>(m) * K;
+  }
+  const int kq = 8 * (lane >> 4);
+
+  f32x4_t acc[TG][kSNB];
+#pragma unroll
+  for (int tg = 0; tg < TG; ++tg)
+#pragma unroll
+    for (int b = 0; b < kSNB; ++b) acc[tg][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  // this wave's quarter of the 32-wide K steps
+  const int nsteps = K / 32;
+  const int s0 = wave * nsteps / kSWaves;
+  const int s1 = (wave + 1) * nsteps / kSWaves;
+  int s = s0;
+#define MOE_SLOAD(FA, FB, S0)                                                              \
+  _Pragma("unroll") for (int u = 0; u < U; ++u) {                                         \
+    const int kk = ((S0) + u) * 32 + kq;                                                  \
+    _Pragma("unroll") for (int b = 0; b < kSNB; ++b)                                      \
+      FB[u][b] = wload(reinterpret_cast<const bf16x8_t*>(wrow[b] + kk));                  \
+    _Pragma("unroll") for (int tg = 0; tg < TG; ++tg)                                     \
+      FA[u][tg] = *reinterpret_cast<const bf16x8_t*>(arow[tg] + kk);                      \
+  }
+#define MOE_SMFMA(FA, FB)                                                                  \
+  _Pragma("unroll") for (int u = 0; u < U; ++u)                                           \
+    _Pragma("unroll") for (int tg = 0; tg < TG; ++tg)                                     \
+      _Pragma("unroll") for (int b = 0; b < kSNB; ++b)                                    \
+        acc[tg][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(FA[u][tg], FB[u][b], acc[tg][b], 0, 0, 0);
+#if MOE_STREAM_PIPE
+  if (s + 2 * U <= s1) {
+    // two batches in flight: load batch i+1, then use batch i
+    bf16x8_t fa0[U][TG], fb0[U][kSNB], fa1[U][TG], fb1[U][kSNB];
+    MOE_SLOAD(fa0, fb0, s);
+    s += U;
+    for (; s + 2 * U <= s1; s += 2 * U) {
+      MOE_SLOAD(fa1, fb1, s);
+      MOE_SMFMA(fa0, fb0);
+      MOE_SLOAD(fa0, fb0, s + U);
+      MOE_SMFMA(fa1, fb1);
+    }
+    MOE_SMFMA(fa0, fb0);
+  }
+#endif
+  for (; s + U <= s1; s += U) {
+    bf16x8_t fa[U][TG], fb[U][kSNB];
+    MOE_SLOAD(fa, fb, s);
+    MOE_SMFMA(fa, fb);
+  }
+#undef MOE_SLOAD
+#undef MOE_SMFMA
+  for (; s < s1; ++s) {
+    const int kk = s * 32 + kq;
+    bf16x8_t fb[kSNB], fa[TG];
+#pragma unroll
+    for (int b = 0; b < kSNB; ++b)
+      fb[b] = wload(reinterpret_cast<const bf16x8_t*>(wrow[b] + kk));
+#pragma unroll
+    for (int tg = 0; tg < TG; ++tg) fa[tg] = *reinterpret_cast<const bf16x8_t*>(arow[tg] + kk);
+#pragma unroll
+    for (int tg = 0; tg < TG; ++tg)
+#pragma unroll
+      for (int b = 0; b < kSNB; ++b)
+        acc[tg][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[tg], fb[b], acc[tg][b], 0, 0, 0);
+  }
+
+  // Sum the four quarters in wave order, one token group at a time; wave
+  // (tg % 4) finishes group tg.
+  f32x4_t* R = reinterpret_cast<f32x4_t*>(red);
+#pragma unroll
+  for (int tg = 0; tg < TG; ++tg) {
+#pragma unroll
+    for (int b = 0; b < kSNB; ++b) R[(wave * kSNB + b) * kWave + lane] = acc[tg][b];
+    __syncthreads();
+    if (wave == (tg & (kSWaves - 1))) {
+      f32x4_t v[kSNB];
+#pragma unroll
+      for (int b = 0; b < kSNB; ++b) {
+        v[b] = R[b * kWave + lane];
+#pragma unroll
+        for (int w = 1; w < kSWaves; ++w) v[b] += R[(w * kSNB + b) * kWave + lane];
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int m = tg * 16 + 4 * (lane >> 4) + q;
+        if (m >= rows) continue;
+        if (PHASE == 1) {
+          uint16_t* Hout = static_cast<uint16_t*>(a.H) + static_cast<int64_t>(hrow0 + m) * a.F;
+          Hout[n0 + (lane & 15)] = f32_to_bf16(silu_s(v[0][q]) * v[1][q]);
+        } else {
+          uint16_t* Y = routed
+              ? static_cast<uint16_t*>(a.y_perm) + static_cast<int64_t>(arow0 + m) * a.d
+              : static_cast<uint16_t*>(a.y_shared) +
+                    static_cast<int64_t>(hrow0 - a.T * a.k + m) * a.d;
+#pragma unroll
+          for (int b = 0; b < kSNB; ++b) Y[n0 + b * 16 + (lane & 15)] = f32_to_bf16(v[b][q]);
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// Grid: x = weight-row group, y = segment (routed experts, then shared).
+// Segments with no rows, or more than kStreamMaxRows rows, exit at once.
+template <int PHASE>
+__global__ __launch_bounds__(kSWaves * kWave) void ffn_stream_kernel(StreamArgs a) {
+  __shared__ f32x4_t red[kSWaves * kSNB * kWave];
+  const int seg = blockIdx.y;
+  int rows, arow0, hrow0;
+  if (seg < a.E) {
+    arow0 = a.offsets[seg];
+    rows = a.offsets[seg + 1] - arow0;
+    hrow0 = arow0;
+  } else {
+    arow0 = 0;
+    rows = a.T;
+    hrow0 = a.T * a.k + (seg - a.E) * a.T;
+  }
+  if (rows <= 0 || rows > kStreamMaxRows) return;
+  float* r = reinterpret_cast<float*>(red);
+  switch ((rows + 15) / 16) {
+    case 1: stream_block<PHASE, 1>(a, seg, rows, arow0, hrow0, r); break;
+    case 2: stream_block<PHASE, 2>(a, seg, rows, arow0, hrow0, r); break;
+    case 3: stream_block<PHASE, 3>(a, seg, rows, arow0, hrow0, r); break;
+    default: stream_block<PHASE, 4>(a, seg, rows, arow0, hrow0, r); break;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_ffn_stream(int phase, int64_t T, int64_t d, int E, int E_shared, int k,
+                             int64_t F, const void* x_perm, const int32_t* offsets,
+                             const void* x, const void* w1, const void* w3, const void* w2,
+                             const void* ws1, const void* ws3, const void* ws2, void* H,
+                             void* y_perm, void* y_shared, hipStream_t s) {
+  StreamArgs a{x_perm, x, offsets, w1, w3, w2, ws1, ws3, ws2, H, y_perm, y_shared,
+               static_cast<int>(T), static_cast<int>(d), E, E_shared, k, static_cast<int>(F)};
+  const unsigned nseg = static_cast<unsigned>(E + E_shared);
+  if (phase == 1) {
+    hipLaunchKernelGGL(ffn_stream_kernel<1>, dim3(static_cast<unsigned>(F / 16), nseg),
+                       dim3(kSWaves * kWave), 0, s, a);
+  } else {
+    hipLaunchKernelGGL(ffn_stream_kernel<2>, dim3(static_cast<unsigned>(d / 32), nseg),
+                       dim3(kSWaves * kWave), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace moe

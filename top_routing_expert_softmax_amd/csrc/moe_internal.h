@@ -17,6 +17,10 @@ constexpr int kMaxDispatchBlocks = 64;
 // Statistics: at most this many partial blocks.
 constexpr int kStatsBlocks = 256;
 
+// Decode-sized expert segments (at most this many rows) take the
+// weight-streaming FFN kernels.
+constexpr int kStreamMaxRows = 64;
+
 size_t route_workspace_bytes(int64_t T, int64_t d, int E);
 size_t permute_workspace_bytes(int64_t T, int E);
 size_t stats_workspace_bytes(int64_t T, int E);
@@ -41,6 +45,14 @@ hipError_t launch_expert_ffn(int64_t T, int64_t d, int E, int E_shared, int k,
                              const void* ws1, const void* ws3, const void* ws2,
                              void* y_perm, void* y_shared, void* ws,
                              hipStream_t s);
+
+// One phase (1: H = SiLU(X W1^T) * (X W3^T), 2: Y = H W2^T) of the
+// weight-streaming FFN over the segments with 1 .. kStreamMaxRows rows.
+hipError_t launch_ffn_stream(int phase, int64_t T, int64_t d, int E, int E_shared, int k,
+                             int64_t F, const void* x_perm, const int32_t* offsets,
+                             const void* x, const void* w1, const void* w3, const void* w2,
+                             const void* ws1, const void* ws3, const void* ws2, void* H,
+                             void* y_perm, void* y_shared, hipStream_t s);
 
 hipError_t launch_combine(int64_t T, int64_t d, int E_shared, int k, bool bf16,
                           const void* y_perm, const void* y_shared,
