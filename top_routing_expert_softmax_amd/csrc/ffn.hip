@@ -20,7 +20,7 @@
 // 64 streamed into a two-slot LDS ring by direct-to-LDS loads,
 // v_mfma_f32_32x32x16_bf16 with fp32 accumulators.  Tiles of the last,
 // partial wave of the chip are split along K and summed in a fixed order
-// (gemm256_kernel).  bf16, decode-sized segments: 128-row tiles with
+// (gemm_big_kernel).  bf16, decode-sized segments: 128-row tiles with
 // register prefetch (gemm_bf16_kernel).  fp32 (small configs): VALU tiles,
 // the correctness path.
 #include <math.h>
@@ -37,19 +37,25 @@ constexpr int kBK = 64;
 constexpr int kLdsStride = kBK + 8;   // bf16 elements per LDS row
 constexpr int kThreads = 256;
 
-// Split-K of the last, partial wave of 256 x 256 tiles (see gemm256_kernel):
+// Split-K of the last, partial wave of BM x 256 tiles (see gemm_big_kernel):
 // at most kMaxSplit parts per tile, each at least kMinSplitSlices K slices,
 // and at most kMaxCUs partial tiles in flight.
 constexpr int kMaxSplit = 4;
 constexpr int kMinSplitSlices = 16;
 constexpr int kMaxCUs = 256;
 
-// K-slice depth and LDS ring length of the 256 x 256 bf16 kernel.
+// K-slice depth and LDS ring length of the large-tile bf16 kernel.
 #ifndef MOE_GEMM_BK
 #define MOE_GEMM_BK 64
 #endif
 #ifndef MOE_GEMM_NST
 #define MOE_GEMM_NST 2
+#endif
+#ifndef MOE_GEMM_UNCOND
+#define MOE_GEMM_UNCOND 1
+#endif
+#ifndef MOE_GEMM_PRIO
+#define MOE_GEMM_PRIO 1
 #endif
 
 struct FfnArgs {
@@ -67,7 +73,7 @@ struct FfnArgs {
   void* y_shared;
   const int4* tiles;     // (segment, A row, rows, H row)
   const int* ntiles;
-  float* sk_partial;     // split-K partial tiles of the last wave (256 x 256 fp32 each)
+  float* sk_partial;     // split-K partial tiles of the last wave (fp32)
   unsigned* sk_count;    // arrivals per split tile: [2][kMaxCUs], phase 1 then 2
   int T, d, E, Es, k, F;
 };
@@ -277,14 +283,16 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(FfnArgs a) {
   }
 }
 
-// ------------------------------------------------- bf16 MFMA, 256 x 256 --
+// ---------------------------------------------- bf16 MFMA, BM x 256 tiles --
 //
-// Block tile 256 rows x 256 B-rows, 4 wavefronts as 2 x 2, each owning
-// 128 x 128 outputs (4 x 4 blocks of v_mfma_f32_32x32x16_bf16, 256 fp32
-// accumulators per lane).  Operand tiles move global -> LDS with
-// global_load_lds_dwordx4 (no staging registers) through an NST-stage ring
-// of K-slices of BKT elements: while slice s is multiplied, the loads of
-// slices s+1 .. s+NST-1 are in flight, which hides the L2/HBM latency.
+// Block tile BM rows x 256 B-rows (BM = kBM2), 8 wavefronts as WM x (8/WM),
+// each owning (BM/WM) x (256*WM/8) outputs in 32 x 32 blocks of
+// v_mfma_f32_32x32x16_bf16 with fp32 accumulators.  Operand tiles move
+// global -> LDS with global_load_lds_dwordx4 (no staging registers)
+// through an NST-stage ring of K-slices of BKT elements: while slice s is
+// multiplied, the loads of slices s+1 .. s+NST-1 are in flight.  Taller
+// tiles carry more rows per weight byte streamed: an expert segment of c
+// rows streams its weights ceil(c / BM) times.
 // LDS rows hold BKT bf16 (ROW bytes = CH chunks of 16 B).  The LDS has 64
 // banks (a 256-byte line holding RPL = 256/ROW rows) and serves a 16-byte
 // read 16 lanes at a time; chunk c of row r sits at physical chunk
@@ -296,18 +304,25 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(FfnArgs a) {
 // robin) takes a contiguous chunk of the live tiles, and inside a chunk
 // tiles run in groups of kGM row tiles x all column tiles, so concurrently
 // resident blocks of one XCD share A and B tiles in that XCD's L2.
-constexpr int kBM2 = 256;
+#ifndef MOE_GEMM_BM
+#define MOE_GEMM_BM 256
+#endif
+#ifndef MOE_GEMM_WM
+#define MOE_GEMM_WM 2
+#endif
+constexpr int kBM2 = MOE_GEMM_BM;   // rows per tile, large segments
+constexpr int kWM = MOE_GEMM_WM;    // wavefronts along M
 constexpr int kBN2 = 256;
 constexpr int kGM = 8;
 constexpr int kXcds = 8;
 
-template <int BKT>
+template <int BKT, int BMT>
 struct SliceGeom {
   static constexpr int ROW = BKT * 2;                   // bytes per LDS row
   static constexpr int CH = ROW / 16;                   // 16-byte chunks per row
   static constexpr int RPL = 256 / ROW;                 // rows per 256-byte bank line
   static constexpr int RPI = 1024 / ROW;                // rows per wave DMA instruction
-  static constexpr int STAGE = (kBM2 + kBN2) * ROW;     // bytes per slice
+  static constexpr int STAGE = (BMT + kBN2) * ROW;      // bytes per slice
 };
 
 template <int N>
@@ -323,22 +338,22 @@ __device__ __forceinline__ void lds_dma16(const void* gptr, uint32_t* lds_row_ba
 }
 
 // K loop of one wave: stream slices of A and B into the LDS ring with DMA
-// loads and run the wave's MFMAs on them.  MIA (0..4) is the number of the
-// wave's four 32-row blocks that hold segment rows; the others take no
+// loads and run the wave's MFMAs on them.  MIA (0..MI) is the number of
+// the wave's MI 32-row blocks that hold segment rows; the others take no
 // MFMA work.  Every wave of the block runs the same loads and barriers.
-template <int BKT, int NST, int NI, int NB, int MIA>
-__device__ __forceinline__ void gemm256_mainloop(
-    f32x16_t (&acc)[4][NB], const uint16_t* const (&asrc)[NI],
-    const uint16_t* const (&bsrc)[NI], char* lds_bytes,
-    int a_dst, int b_dst, const int (&a_off)[4], const int (&b_off)[NB], int lane, int nk) {
-  using G = SliceGeom<BKT>;
+template <int BKT, int BMT, int NST, int NIA, int NIB, int MI, int NB, int MIA>
+__device__ __forceinline__ void gemm_mainloop(
+    f32x16_t (&acc)[MI][NB], const uint16_t* const (&asrc)[NIA],
+    const uint16_t* const (&bsrc)[NIB], char* lds_bytes, int a_dst, int b_dst,
+    const int (&a_off)[MI], const int (&b_off)[NB], int lane, int nk) {
+  using G = SliceGeom<BKT, BMT>;
 #define MOE_ISSUE_SLICE(slot, k0)                                                          \
-  _Pragma("unroll") for (int i = 0; i < NI; ++i) {                                         \
+  _Pragma("unroll") for (int i = 0; i < NIA; ++i)                                          \
     lds_dma16(asrc[i] + (k0), reinterpret_cast<uint32_t*>(                                \
                   lds_bytes + (slot) * G::STAGE + a_dst + i * G::RPI * G::ROW));          \
+  _Pragma("unroll") for (int i = 0; i < NIB; ++i)                                          \
     lds_dma16(bsrc[i] + (k0), reinterpret_cast<uint32_t*>(                                \
-                  lds_bytes + (slot) * G::STAGE + b_dst + i * G::RPI * G::ROW));          \
-  }
+                  lds_bytes + (slot) * G::STAGE + b_dst + i * G::RPI * G::ROW));
   // fragment rows are 32-aligned bases + lane%32, so the swizzle key of
   // all of this lane's fragment rows is ((lane % 32) / RPL) % CH
   const int key = ((lane & 31) / G::RPL) % G::CH;
@@ -351,18 +366,30 @@ __device__ __forceinline__ void gemm256_mainloop(
     const int slot = kt % NST;
     // slice kt has landed once at most (NST-2) younger slices are pending
     if (kt + NST - 2 < nk) {
-      wait_vmcnt<(NST - 2) * 2 * NI>();
+      wait_vmcnt<(NST - 2) * (NIA + NIB)>();
     } else {
       wait_vmcnt<0>();
     }
     __syncthreads();            // every wave's part of slice kt is in LDS, and
                                 // slot (kt-1) % NST is no longer read
+#if MOE_GEMM_UNCOND
+    {
+      // always issue (one block of code for the scheduler): past the last
+      // slice, reload the last slice into the free slot
+      const int s_next = kt + NST - 1;
+      MOE_ISSUE_SLICE(s_next % NST, min(s_next, nk - 1) * BKT);
+    }
+#else
     if (kt + NST - 1 < nk) {
       const int s_next = kt + NST - 1;
       MOE_ISSUE_SLICE(s_next % NST, s_next * BKT);
     }
+#endif
     if (MIA == 0) continue;
     const char* sb = lds_bytes + slot * G::STAGE;
+#if MOE_GEMM_PRIO
+    __builtin_amdgcn_s_setprio(1);
+#endif
 #pragma unroll
     for (int ks = 0; ks < BKT / 16; ++ks) {
       const int pc = ((2 * ks + khalf) ^ key) * 16;
@@ -378,19 +405,31 @@ __device__ __forceinline__ void gemm256_mainloop(
           acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[mi], fb[ni], acc[mi][ni], 0, 0, 0);
       __builtin_amdgcn_iglp_opt(0);
     }
+#if MOE_GEMM_PRIO
+    __builtin_amdgcn_s_setprio(0);
+#endif
   }
+#if MOE_GEMM_UNCOND
+  wait_vmcnt<0>();              // the extra loads of the last iterations
+#endif
 #undef MOE_ISSUE_SLICE
 }
 
-template <int PHASE, int BKT, int NST, int WAVES>
+template <int PHASE, int BKT, int NST, int WAVES, int BMT, int WMW>
 __global__ __launch_bounds__(WAVES * kWave) __attribute__((amdgpu_waves_per_eu(WAVES / 4, WAVES / 4)))
-void gemm256_kernel(FfnArgs a, int NT, int ncu) {
-  using G = SliceGeom<BKT>;
-  constexpr int WN = WAVES / 2;             // waves along N (2 along M)
-  constexpr int WROWS = kBM2 / WAVES;       // tile rows each wave loads per operand
-  constexpr int NI = WROWS / G::RPI;        // DMA instructions per wave per operand
+void gemm_big_kernel(FfnArgs a, int NT, int ncu) {
+  using G = SliceGeom<BKT, BMT>;
+  constexpr int WN = WAVES / WMW;           // waves along N
+  constexpr int WR = BMT / WMW;             // output rows per wave
+  constexpr int MI = WR / 32;               // 32-row blocks per wave
   constexpr int NB = kBN2 / WN / 32;        // 32-wide B blocks per wave
-  static_assert(NI >= 1 && NB >= 2 && NB % 2 == 0, "tile geometry");
+  constexpr int AROWS = BMT / WAVES;        // A tile rows each wave loads
+  constexpr int BROWS = kBN2 / WAVES;       // B tile rows each wave loads
+  constexpr int NIA = AROWS / G::RPI;       // DMA instructions per wave, A
+  constexpr int NIB = BROWS / G::RPI;       // DMA instructions per wave, B
+  static_assert(MI * 32 == WR && MI >= 1 && MI <= 4, "tile rows per wave");
+  static_assert(NIA * G::RPI == AROWS && NIB * G::RPI == BROWS, "DMA rows");
+  static_assert(NB >= 2 && NB % 2 == 0, "tile columns per wave");
   extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
 
   // ---- which tile, and which part of its K range
@@ -457,18 +496,23 @@ void gemm256_kernel(FfnArgs a, int NT, int ncu) {
       : static_cast<const uint16_t*>(a.H) + static_cast<int64_t>(hrow0) * K;
   const int64_t wstride = static_cast<int64_t>(a.F) * a.d;
 
-  // ---- per-lane sources of the NI A and NI B DMA instructions of a slice.
-  // Wave w, instruction i covers tile rows w*WROWS + i*RPI .. +RPI; lane l
-  // takes row r = w*WROWS + i*RPI + l/CH and the logical chunk that the
-  // swizzle stores at physical chunk l%CH of that row.
-  const uint16_t* asrc[NI];
-  const uint16_t* bsrc[NI];
+  // ---- per-lane sources of the DMA instructions of a slice.  Wave w,
+  // instruction i covers tile rows w*ROWS + i*RPI .. +RPI of its operand;
+  // lane l takes row r = w*ROWS + i*RPI + l/CH and the logical chunk that
+  // the swizzle stores at physical chunk l%CH of that row.
+  const uint16_t* asrc[NIA];
+  const uint16_t* bsrc[NIB];
 #pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    const int r = wave * WROWS + i * G::RPI + lane / G::CH;
+  for (int i = 0; i < NIA; ++i) {
+    const int r = wave * AROWS + i * G::RPI + lane / G::CH;
     const int lchunk = (lane % G::CH) ^ ((r / G::RPL) % G::CH);
     const int ra = r < mrows ? r : mrows - 1;
     asrc[i] = A + static_cast<int64_t>(ra) * K + kb * BKT + lchunk * 8;
+  }
+#pragma unroll
+  for (int i = 0; i < NIB; ++i) {
+    const int r = wave * BROWS + i * G::RPI + lane / G::CH;
+    const int lchunk = (lane % G::CH) ^ ((r / G::RPL) % G::CH);
     int col;
     const uint16_t* W;
     if (PHASE == 1) {
@@ -482,12 +526,12 @@ void gemm256_kernel(FfnArgs a, int NT, int ncu) {
     bsrc[i] = W + e * wstride + static_cast<int64_t>(col) * K + kb * BKT + lchunk * 8;
   }
   char* lds_bytes = reinterpret_cast<char*>(lds);
-  const int a_dst = wave * WROWS * G::ROW;
-  const int b_dst = kBM2 * G::ROW + wave * WROWS * G::ROW;
+  const int a_dst = wave * AROWS * G::ROW;
+  const int b_dst = BMT * G::ROW + wave * BROWS * G::ROW;
 
-  f32x16_t acc[4][NB];
+  f32x16_t acc[MI][NB];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int jn = 0; jn < NB; ++jn)
 #pragma unroll
@@ -495,37 +539,43 @@ void gemm256_kernel(FfnArgs a, int NT, int ncu) {
 
   // Phase 1: the wave's first NB/2 B blocks are gate (W1) columns, the last
   // NB/2 the same columns of W3.
-  int a_off[4], b_off[NB];
+  int a_off[MI], b_off[NB];
 #pragma unroll
-  for (int mi = 0; mi < 4; ++mi) a_off[mi] = (wm * 128 + mi * 32 + (lane & 31)) * G::ROW;
+  for (int mi = 0; mi < MI; ++mi) a_off[mi] = (wm * WR + mi * 32 + (lane & 31)) * G::ROW;
 #pragma unroll
   for (int ni = 0; ni < NB; ++ni) {
     const int r = PHASE == 1
         ? ((ni / (NB / 2)) * 128 + wn * (128 / WN) + (ni % (NB / 2)) * 32 + (lane & 31))
         : (wn * (kBN2 / WN) + ni * 32 + (lane & 31));
-    b_off[ni] = kBM2 * G::ROW + r * G::ROW;
+    b_off[ni] = BMT * G::ROW + r * G::ROW;
   }
-  // 32-row blocks of this wave's 128 rows that hold segment rows: a tail
+
+  // 32-row blocks of this wave's WR rows that hold segment rows: a tail
   // tile runs MFMAs only for those.
-  const int rows_w = mrows - wm * 128;
+  const int rows_w = mrows - wm * WR;
   const int mia = __builtin_amdgcn_readfirstlane(
-      rows_w <= 0 ? 0 : (rows_w >= 128 ? 4 : (rows_w + 31) / 32));
+      rows_w <= 0 ? 0 : (rows_w >= WR ? MI : (rows_w + 31) / 32));
+#define MOE_MAINLOOP(X)                                                                    \
+  gemm_mainloop<BKT, BMT, NST, NIA, NIB, MI, NB, (X)>(acc, asrc, bsrc, lds_bytes, a_dst,   \
+                                                      b_dst, a_off, b_off, lane, nk)
   switch (mia) {
-    case 4: gemm256_mainloop<BKT, NST, NI, NB, 4>(acc, asrc, bsrc, lds_bytes, a_dst, b_dst, a_off, b_off, lane, nk); break;
-    case 3: gemm256_mainloop<BKT, NST, NI, NB, 3>(acc, asrc, bsrc, lds_bytes, a_dst, b_dst, a_off, b_off, lane, nk); break;
-    case 2: gemm256_mainloop<BKT, NST, NI, NB, 2>(acc, asrc, bsrc, lds_bytes, a_dst, b_dst, a_off, b_off, lane, nk); break;
-    case 1: gemm256_mainloop<BKT, NST, NI, NB, 1>(acc, asrc, bsrc, lds_bytes, a_dst, b_dst, a_off, b_off, lane, nk); break;
-    default: gemm256_mainloop<BKT, NST, NI, NB, 0>(acc, asrc, bsrc, lds_bytes, a_dst, b_dst, a_off, b_off, lane, nk); break;
+    case 4: if constexpr (MI >= 4) MOE_MAINLOOP(MI >= 4 ? 4 : 0); break;
+    case 3: if constexpr (MI >= 3) MOE_MAINLOOP(MI >= 3 ? 3 : 0); break;
+    case 2: if constexpr (MI >= 2) MOE_MAINLOOP(MI >= 2 ? 2 : 0); break;
+    case 1: MOE_MAINLOOP(1); break;
+    default: MOE_MAINLOOP(0); break;
   }
+#undef MOE_MAINLOOP
 
   if (split_unit) {
     // Partial tile in accumulator order: float4 q of accumulator (mi, ni)
     // of thread tid sits at ((mi * NB + ni) * 4 + q) * NTHR + tid.
     constexpr int NTHR = WAVES * kWave;
+    constexpr int64_t kSlot = static_cast<int64_t>(BMT) * kBN2 / 4;   // float4 per tile
     f32x4_t* mine = reinterpret_cast<f32x4_t*>(a.sk_partial) +
-                    static_cast<int64_t>(tile_sk * S + part) * (kBM2 * kBN2 / 4);
+                    static_cast<int64_t>(tile_sk * S + part) * kSlot;
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
+    for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
       for (int ni = 0; ni < NB; ++ni)
 #pragma unroll
@@ -535,28 +585,28 @@ void gemm256_kernel(FfnArgs a, int NT, int ncu) {
           mine[((mi * NB + ni) * 4 + q) * NTHR + tid] = v;
         }
     // Release the partial device-wide, then count the arrival; the last of
-    // the S parts takes the tile.
+    // the S parts takes the tile.  The LDS ring is idle by now (every wave
+    // is past its K loop), so its first word carries the verdict.
     __threadfence();
     __syncthreads();
-    int* flag = reinterpret_cast<int*>(lds_bytes + NST * G::STAGE);
-    if (tid == 0) {
+    int* flag = reinterpret_cast<int*>(lds_bytes);
+    if (tid == 0)
       *flag = atomicAdd(&a.sk_count[(PHASE - 1) * kMaxCUs + tile_sk], 1u) ==
               static_cast<unsigned>(S - 1);
-    }
     __syncthreads();
     if (*flag == 0) return;
     __threadfence();            // acquire: the other parts' partials
     const f32x4_t* first = reinterpret_cast<const f32x4_t*>(a.sk_partial) +
-                           static_cast<int64_t>(tile_sk * S) * (kBM2 * kBN2 / 4);
+                           static_cast<int64_t>(tile_sk * S) * kSlot;
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
+    for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
       for (int ni = 0; ni < NB; ++ni)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int64_t at = ((mi * NB + ni) * 4 + q) * NTHR + tid;
           f32x4_t v = first[at];
-          for (int p = 1; p < S; ++p) v += first[static_cast<int64_t>(p) * (kBM2 * kBN2 / 4) + at];
+          for (int p = 1; p < S; ++p) v += first[static_cast<int64_t>(p) * kSlot + at];
 #pragma unroll
           for (int c = 0; c < 4; ++c) acc[mi][ni][4 * q + c] = v[c];
         }
@@ -571,10 +621,10 @@ void gemm256_kernel(FfnArgs a, int NT, int ncu) {
       const int col = n0 + wn * (128 / WN) + ni * 32 + (lane & 31);
       if (col >= N) continue;
 #pragma unroll
-      for (int mi = 0; mi < 4; ++mi)
+      for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          const int row = wm * 128 + mi * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+          const int row = wm * WR + mi * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
           if (row < mrows) {
             const float h = silu_f(acc[mi][ni][v]) * acc[mi][ni + NB / 2][v];
             Hout[static_cast<int64_t>(row) * a.F + col] = f32_to_bf16(h);
@@ -590,10 +640,10 @@ void gemm256_kernel(FfnArgs a, int NT, int ncu) {
       const int col = n0 + wn * (kBN2 / WN) + ni * 32 + (lane & 31);
       if (col >= N) continue;
 #pragma unroll
-      for (int mi = 0; mi < 4; ++mi)
+      for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          const int row = wm * 128 + mi * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+          const int row = wm * WR + mi * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
           if (row < mrows) Yout[static_cast<int64_t>(row) * a.d + col] = f32_to_bf16(acc[mi][ni][v]);
         }
     }
@@ -610,14 +660,14 @@ constexpr int kNSTsel = MOE_GEMM_NST;
 constexpr int kWavesSel = MOE_GEMM_WAVES;
 
 template <int PHASE>
-hipError_t launch_gemm256(const FfnArgs& a, int nt, int64_t mt, int ncu, hipStream_t s) {
+hipError_t launch_gemm_big(const FfnArgs& a, int nt, int64_t mt, int ncu, hipStream_t s) {
   // whole-tile blocks (at most every tile, in XCD-sized steps) plus one
   // wave of split-K blocks
   const int64_t lmax = mt * nt;
   const unsigned g = static_cast<unsigned>(kXcds * ((lmax + kXcds - 1) / kXcds) + ncu);
-  // the LDS ring, then one word for the split-K arrival flag
-  constexpr size_t lds = static_cast<size_t>(kNSTsel) * SliceGeom<kBKsel>::STAGE + 16;
-  auto kern = &gemm256_kernel<PHASE, kBKsel, kNSTsel, kWavesSel>;
+  constexpr size_t lds = static_cast<size_t>(kNSTsel) * SliceGeom<kBKsel, kBM2>::STAGE;
+  static_assert(lds <= 160 * 1024, "LDS ring exceeds the 160 KB of a CU");
+  auto kern = &gemm_big_kernel<PHASE, kBKsel, kNSTsel, kWavesSel, kBM2, kWM>;
   static const hipError_t attr = hipFuncSetAttribute(
       reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
       static_cast<int>(lds));
@@ -767,7 +817,7 @@ hipError_t launch_expert_ffn(int64_t T, int64_t d, int E, int E_shared, int k, i
            : nullptr;
   void* H = sk + ffn_sk_bytes(bf16 ? 2 : 4);
 
-  // Large segments take the 256 x 256 tiles; decode-sized ones (few rows
+  // Large segments take the large tiles; decode-sized ones (few rows
   // per expert) the 128-row tiles.
   const int BM = !bf16 ? kBMf : (T * k >= 64LL * E ? kBM2 : kBM);
   // decode-sized calls with T <= kStreamMaxRows only stream (no tiles)
@@ -783,16 +833,16 @@ hipError_t launch_expert_ffn(int64_t T, int64_t d, int E, int E_shared, int k, i
     const int nt1 = static_cast<int>((F + kBN2 / 2 - 1) / (kBN2 / 2));
     const int nt2 = static_cast<int>((d + kBN2 - 1) / kBN2);
     const int64_t mt = max_tiles(T, E, E_shared, k, kBM2);
-    // compute units of the current device: one 256 x 256 block fits a CU
+    // compute units of the current device: one large-tile block fits a CU
     int dev = 0, ncu = 0;
     hipError_t err = hipGetDevice(&dev);
     if (err == hipSuccess)
       err = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
     if (err != hipSuccess) return err;
     ncu = max(kXcds, min(ncu, kMaxCUs));
-    err = launch_gemm256<1>(a, nt1, mt, ncu, s);
+    err = launch_gemm_big<1>(a, nt1, mt, ncu, s);
     if (err != hipSuccess) return err;
-    err = launch_gemm256<2>(a, nt2, mt, ncu, s);
+    err = launch_gemm_big<2>(a, nt2, mt, ncu, s);
     if (err != hipSuccess) return err;
   } else if (bf16) {
     // Decode-sized: segments of at most kStreamMaxRows rows stream their
