@@ -25,6 +25,12 @@ Readings where the pages are silent or disagree (each is listed in the design doc):
     not renormalised.
   * f_i is counted before the drop (sum_i f_i = k); N = T.
   * SiLU(z) = z * sigmoid(z); W1 is the gated branch, W3 the linear one.
+  * DeepSeek-V3 gate: the affinity sigmoid(g) is evaluated in fp64 and
+    rounded once to fp32; the bias add, the two-largest group sums and every
+    comparison that picks groups and experts are fp32 (the precision of the
+    kernel, so both sides take the same integer decisions); ties go to the
+    lower group / expert index; the bias rule compares counts_i with the
+    mean T k / E exactly.
 """
 from fractions import Fraction
 import math
@@ -36,6 +42,7 @@ __all__ = [
     "renormalise", "topk_softmax_weights", "route", "expert_counts",
     "capacity", "dispatch", "silu", "swiglu_expert", "combine_grouped",
     "combine_per_token", "load_balance_loss", "aux_stats", "layer_forward",
+    "affinity_f32", "v3_gate", "update_bias",
 ]
 
 
@@ -98,6 +105,69 @@ def route(x, w_gate, k):
     w = renormalise(p, idx)
     return {"logits": g, "probs": p, "idx": idx, "weights": w,
             "lse": logsumexp(g)}
+
+
+# ------------------------------------------------- DeepSeek-V3 gate (N1) --
+
+def affinity_f32(g):
+    """s = sigmoid(g), one affinity in (0, 1) per expert ([L17] section 5.3,
+    first step of the V3 gate).  Evaluated in fp64 and rounded once to fp32,
+    the precision in which the gate takes its decisions."""
+    g = _f64(g)
+    return (1.0 / (1.0 + np.exp(-g))).astype(np.float32)
+
+
+def v3_gate(g, bias, k, n_groups, topk_groups, route_scale):
+    """DeepSeek-V3 gate, sigmoid branch ([L17] section 5.3, with the
+    selection-only bias of section 3.4), in its steps:
+
+      1. s = sigmoid(g) per expert;
+      2. biased = s + b: the balance bias enters only the choice;
+      3. the E experts form n_groups contiguous groups; a group's score is
+         the sum of its two largest biased scores;
+      4. the topk_groups best groups are kept, the others masked out;
+      5. the k largest biased scores among the kept experts are chosen;
+      6. the weights are the UNBIASED affinities of the chosen experts,
+         divided by their sum and multiplied by route_scale.
+
+    Steps 2-5 are fp32 (see the module notes); step 6 is fp64.  Returns the
+    chosen ids (larger biased score first, ties to the lower index), the
+    weights and the intermediate arrays."""
+    s = affinity_f32(g)
+    T, E = s.shape
+    if E % n_groups or E // n_groups < 2:
+        raise ValueError("groups must split E evenly, two experts or more each")
+    b = np.asarray(bias, dtype=np.float32)
+    biased = s + b[None, :]                                   # fp32 + fp32
+    G = E // n_groups
+    ranked = -np.sort(-biased.reshape(T, n_groups, G), axis=-1)
+    gscore = ranked[..., 0] + ranked[..., 1]                  # fp32 sum of the two largest
+    kept = np.argsort(-gscore, axis=-1, kind="stable")[:, :topk_groups]
+    in_kept = np.zeros((T, n_groups), dtype=bool)
+    np.put_along_axis(in_kept, kept, True, axis=-1)
+    allowed = np.repeat(in_kept, G, axis=-1)
+    masked = np.where(allowed, biased.astype(np.float64), -np.inf)
+    idx = np.argsort(-masked, axis=-1, kind="stable")[:, :k].astype(np.int64)
+    sel = np.take_along_axis(_f64(s), idx, axis=-1)
+    w = sel / sel.sum(axis=-1, keepdims=True) * float(route_scale)
+    return {"idx": idx, "weights": w, "affinity": s, "biased": biased,
+            "group_score": gscore, "kept_groups": kept, "logits": _f64(g)}
+
+
+def update_bias(counts, bias, T, k, gamma):
+    """Balance-bias step of DeepSeek-V3 ([L17] section 3.4; [SA]
+    update_bias): an expert loaded above the mean T k / E loses gamma, one
+    below it gains gamma, one exactly at it keeps its bias.  fp32, like the
+    stored bias."""
+    counts = np.asarray(counts, dtype=np.int64)
+    E = counts.shape[0]
+    b = np.asarray(bias, dtype=np.float32).copy()
+    gam = np.float32(gamma)
+    over = counts * E > T * k
+    under = counts * E < T * k
+    b[over] = b[over] - gam
+    b[under] = b[under] + gam
+    return b
 
 
 # --------------------------------------------------------------- dispatch --
