@@ -134,6 +134,10 @@ def main():
     ap.add_argument("--cpu-sample", type=int, default=4096,
                     help="tokens whose expert outputs the oracle computes")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--router", default="softmax", choices=["softmax", "v3"],
+                    help="softmax top-k router (moe_route) or the DeepSeek-V3 gate "
+                         "(moe_route_v3: 8 groups, 4 kept, scale 2.5, seeded bias in "
+                         "+-1e-3)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes (reference for "
                          "the FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -160,10 +164,30 @@ def main():
     names = ["route", "permute", "expert_ffn", "combine", "aux_stats"]
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
 
+    v3 = None
+    if args.router == "v3":
+        ng = 8 if E % 8 == 0 and E // 8 >= 2 else 1
+        # a bias of the size a few gamma = 1e-3 balance steps give (well
+        # below the spread of the affinities, so routing still follows x)
+        v3 = {"n_groups": ng, "topk_groups": max(1, ng // 2), "route_scale": 2.5,
+              "bias": torch.tensor(np.random.default_rng(cfg.seed).uniform(-1e-3, 1e-3, E),
+                                   dtype=torch.float32, device="cuda")}
+        if k > v3["topk_groups"] * (E // ng):
+            print("--router v3: k exceeds the experts of the kept groups", file=sys.stderr)
+            sys.exit(2)
+
+    def route():
+        if v3 is None:
+            M.moe_route(dev["x"], dev["wg"], k, b.logits, b.topk_idx, b.topk_w, b.ws, stream)
+        else:
+            M.moe_route_v3(dev["x"], dev["wg"], v3["bias"], k, v3["n_groups"],
+                           v3["topk_groups"], v3["route_scale"], b.logits, b.topk_idx,
+                           b.topk_w, b.ws, stream)
+
     def step(timed):
         if timed:
             ev[0].record(stream)
-        M.moe_route(dev["x"], dev["wg"], k, b.logits, b.topk_idx, b.topk_w, b.ws, stream)
+        route()
         if timed:
             ev[1].record(stream)
         M.moe_permute(b.topk_idx, dev["x"], E, cfg.CF, b.counts, b.offsets, b.token_of_row,
@@ -222,8 +246,24 @@ def main():
     roof["kernel"] = "moe_expert_ffn (grouped GEMM phase 1 + phase 2 + tile table)"
     roof["kernel_ms"] = round(ffn_ms, 4)
 
+    extra = {}
+    if v3 is not None:
+        # the balance-bias step, timed on its own (a training-time update,
+        # not part of the forward step); restored afterwards
+        saved = v3["bias"].clone()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            M.moe_update_bias(T, k, 1e-3, b.counts, v3["bias"], stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        extra = {"router": "deepseek_v3_gate", "n_groups": v3["n_groups"],
+                 "topk_groups": v3["topk_groups"], "route_scale": v3["route_scale"],
+                 "bias_update_ms": round(e0.elapsed_time(e1) / args.steps, 4)}
+        v3["bias"].copy_(saved)
+
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and v3 is None:
         log("timing the CPU oracle on a token sample")
         v, threads, n, dt = cpu_baseline(cfg, x, wg, host, args.cpu_sample)
         cpu = {"value": round(v, 3), "unit": "tokens/s", "cores": int(threads),
@@ -239,7 +279,7 @@ def main():
         "data": "synthetic (seeded; inputs resident in HBM)",
         "config": {"workload": cfg.name, "T": T, "d_model": d, "E": E, "E_shared": Es,
                    "k": k, "d_ff": F, "CF": cfg.CF, "kept_rows": rows,
-                   "experts_touched": touched},
+                   "experts_touched": touched, **extra},
         "breakdown_ms": {n: round(float(v), 4) for n, v in zip(names, per_call)},
         "roofline": roof,
         "cpu_baseline": cpu,

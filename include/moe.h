@@ -111,6 +111,43 @@ int moe_route(int64_t T, int64_t d_model, int32_t E, int32_t k, int32_t dtype,
               void* stream);
 
 /*
+ * DeepSeek-V3 gate ("CMU 11-868 Lecture 17" section 5.3, the sigmoid
+ * branch of the V3 inference gate; the bias of section 3.4), on the same
+ * logits g = x W_gate as moe_route:
+ *   s = sigmoid(g)                 per expert (fp64, rounded once to fp32)
+ *   biased = s + bias              fp32; the bias only steers the choice
+ *   group score = sum of the two largest biased scores of each of n_groups
+ *                 contiguous groups of E / n_groups experts (fp32)
+ *   keep the topk_groups best groups, then choose the k largest biased
+ *   scores among their experts (ties to the lower group / expert index)
+ *   topk_w = route_scale * s_j / sum of s over the chosen j
+ * (V3: E = 256, n_groups = 8, topk_groups = 4, k = 8, route_scale = 2.5.)
+ *   x, w_gate, logits, topk_idx, topk_w, ws: as for moe_route; topk_idx is
+ *                 ordered by biased score, larger first
+ *   bias   [E]  fp32  in
+ * Requires E % n_groups == 0, E / n_groups >= 2, n_groups <= 64,
+ * 1 <= topk_groups <= n_groups and k <= topk_groups * E / n_groups.
+ * The outputs feed moe_permute and moe_combine unchanged (the weights of a
+ * token sum to route_scale).
+ */
+int moe_route_v3(int64_t T, int64_t d_model, int32_t E, int32_t k,
+                 int32_t n_groups, int32_t topk_groups, float route_scale,
+                 int32_t dtype, const void* x, const void* w_gate,
+                 const float* bias, float* logits, int32_t* topk_idx,
+                 float* topk_w, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Balance-bias step of DeepSeek-V3 ("CMU 11-868 Lecture 17" section 3.4):
+ * for each expert e, with the mean load T k / E compared exactly,
+ *   counts[e] > mean:  bias[e] -= gamma
+ *   counts[e] < mean:  bias[e] += gamma
+ *   counts[e] = mean:  unchanged
+ *   counts [E] int32 in (pre-drop, from moe_permute); bias [E] fp32 in/out.
+ */
+int moe_update_bias(int64_t T, int32_t E, int32_t k, float gamma,
+                    const int32_t* counts, float* bias, void* stream);
+
+/*
  * Counting, capacity, drop and permutation, "CMU 11-868 Lecture 17"
  * sections 2.2 (group by expert) and 2.4 (capacity, overflow dropped).
  * Pairs (t, j) are ranked inside their expert in token order; a pair is

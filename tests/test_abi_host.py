@@ -27,7 +27,7 @@ def M():
 def _declared():
     src = open(os.path.join(ROOT, "include", "moe.h")).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", src)))
 
 
 def test_exports_every_declared_symbol(M):
@@ -115,3 +115,23 @@ def test_decode_router_needs_its_workspace(M):
     rc = L.moe_route(64, 7168, 256, 8, M.MOE_BF16, fake, fake, fake, fake, fake, fake, 64, nil)
     assert rc == -4
     assert M.moe_workspace_size(64, 7168, 256, 1, 8, 2048, M.MOE_BF16) >= 64 * 64 * 256 * 4
+
+
+def test_v3_gate_arguments_are_checked(M):
+    L = M.lib()
+    nil = ctypes.c_void_p(0)
+    fake = ctypes.c_void_p(4096)
+
+    def v3(E=256, k=8, ng=8, tg=4, scale=2.5, bias=fake):
+        return L.moe_route_v3(64, 512, E, k, ng, tg, scale, M.MOE_BF16, fake, fake, bias, fake,
+                              fake, fake, fake, 1 << 30, nil)
+    assert v3(ng=7) == -1 and "n_groups" in L.moe_last_error().decode()      # 256 % 7
+    assert v3(E=8, k=2, ng=8, tg=1) == -1                                     # groups of 1
+    assert v3(ng=128, tg=4) == -1                                             # > 64 groups
+    assert v3(tg=9) == -1 and "topk_groups" in L.moe_last_error().decode()
+    assert v3(ng=8, tg=1, k=33) == -1 and "exceeds" in L.moe_last_error().decode()
+    assert v3(scale=float("nan")) == -1
+    assert v3(scale=0.0) == -1
+    assert v3(bias=nil) == -1 and "bias is NULL" in L.moe_last_error().decode()
+    assert L.moe_update_bias(64, 256, 8, float("inf"), fake, fake, nil) == -1
+    assert L.moe_update_bias(64, 256, 8, 1e-3, nil, fake, nil) == -1

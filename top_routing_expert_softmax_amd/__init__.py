@@ -20,8 +20,8 @@ MOE_BF16 = 1
 
 # Symbols declared in include/moe.h.
 EXPORTS = ("moe_strerror", "moe_last_error", "moe_capacity", "moe_workspace_size",
-           "moe_route", "moe_permute", "moe_expert_ffn", "moe_combine",
-           "moe_aux_stats")
+           "moe_route", "moe_route_v3", "moe_update_bias", "moe_permute", "moe_expert_ffn",
+           "moe_combine", "moe_aux_stats")
 
 _lib = None
 
@@ -54,6 +54,12 @@ def lib():
     L.moe_workspace_size.argtypes = [i64, i64, i32, i32, i32, i64, i32, ctypes.POINTER(sz)]
     L.moe_route.restype = ctypes.c_int
     L.moe_route.argtypes = [i64, i64, i32, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp]
+    f32 = ctypes.c_float
+    L.moe_route_v3.restype = ctypes.c_int
+    L.moe_route_v3.argtypes = [i64, i64, i32, i32, i32, i32, f32, i32, vp, vp, vp, vp, vp, vp,
+                               vp, sz, vp]
+    L.moe_update_bias.restype = ctypes.c_int
+    L.moe_update_bias.argtypes = [i64, i32, i32, f32, vp, vp, vp]
     L.moe_permute.restype = ctypes.c_int
     L.moe_permute.argtypes = [i64, i64, i32, i32, f64, i32, vp, vp, vp, vp, vp, vp, vp, vp,
                               vp, sz, vp]
@@ -117,6 +123,22 @@ def moe_route(x, w_gate, k, logits, topk_idx, topk_w, ws, stream=None):
                                         _ptr(logits), _ptr(topk_idx), _ptr(topk_w), _ptr(ws),
                                         0 if ws is None else ws.numel() * ws.element_size(),
                                         _stream(stream)))
+
+
+def moe_route_v3(x, w_gate, bias, k, n_groups, topk_groups, route_scale, logits, topk_idx,
+                 topk_w, ws, stream=None):
+    T, d = x.shape
+    E = w_gate.shape[1]
+    _check("moe_route_v3", lib().moe_route_v3(
+        T, d, E, k, n_groups, topk_groups, float(route_scale), _dtype_code(x), _ptr(x),
+        _ptr(w_gate), _ptr(bias), _ptr(logits), _ptr(topk_idx), _ptr(topk_w), _ptr(ws),
+        0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def moe_update_bias(T, k, gamma, counts, bias, stream=None):
+    E = bias.shape[0]
+    _check("moe_update_bias", lib().moe_update_bias(T, E, k, float(gamma), _ptr(counts),
+                                                    _ptr(bias), _stream(stream)))
 
 
 def moe_permute(topk_idx, x, E, CF, counts, offsets, token_of_row, row_of_pair, drop_mask,

@@ -157,9 +157,57 @@ int moe_route(int64_t T, int64_t d_model, int32_t E, int32_t k, int32_t dtype, c
       return fail(MOE_EWORKSPACE, "moe_route needs %zu workspace bytes, got %zu", need, ws_bytes);
   }
   (void)hipGetLastError();
-  return launched(moe::launch_route(T, d_model, E, k, dtype == MOE_BF16, x, w_gate, logits,
-                                    topk_idx, topk_w, ws, static_cast<hipStream_t>(stream)),
+  return launched(moe::launch_route_softmax(T, d_model, E, k, dtype == MOE_BF16, x, w_gate,
+                                            logits, topk_idx, topk_w, ws,
+                                            static_cast<hipStream_t>(stream)),
                   "moe_route");
+}
+
+int moe_route_v3(int64_t T, int64_t d_model, int32_t E, int32_t k, int32_t n_groups,
+                 int32_t topk_groups, float route_scale, int32_t dtype, const void* x,
+                 const void* w_gate, const float* bias, float* logits, int32_t* topk_idx,
+                 float* topk_w, void* ws, size_t ws_bytes, void* stream) {
+  if (int r = check_common(T, E, k)) return r;
+  if (int r = check_dtype(dtype)) return r;
+  if (int r = check_dim("d_model", d_model)) return r;
+  REQUIRE(n_groups >= 1 && n_groups <= 64 && E % n_groups == 0 && E / n_groups >= 2,
+          "n_groups must divide E into groups of 2 or more experts, at most 64 groups "
+          "(got n_groups=%d, E=%d)", n_groups, E);
+  REQUIRE(topk_groups >= 1 && topk_groups <= n_groups,
+          "topk_groups must be in [1, n_groups] (got %d)", topk_groups);
+  REQUIRE(static_cast<int64_t>(k) <= static_cast<int64_t>(topk_groups) * (E / n_groups),
+          "k=%d exceeds the experts of the kept groups (%d)", k, topk_groups * (E / n_groups));
+  REQUIRE(isfinite(route_scale) && route_scale > 0.f, "route_scale must be finite and > 0");
+  REQUIRE_PTR(x);
+  REQUIRE_PTR(w_gate);
+  REQUIRE_PTR(bias);
+  REQUIRE_PTR(logits);
+  REQUIRE_PTR(topk_idx);
+  REQUIRE_PTR(topk_w);
+  const size_t need = moe::route_workspace_bytes(T, d_model, E);
+  if (need > 0) {
+    REQUIRE_PTR(ws);
+    if (ws_bytes < need)
+      return fail(MOE_EWORKSPACE, "moe_route_v3 needs %zu workspace bytes, got %zu", need,
+                  ws_bytes);
+  }
+  (void)hipGetLastError();
+  return launched(moe::launch_route_v3(T, d_model, E, k, n_groups, topk_groups, route_scale,
+                                       dtype == MOE_BF16, x, w_gate, bias, logits, topk_idx,
+                                       topk_w, ws, static_cast<hipStream_t>(stream)),
+                  "moe_route_v3");
+}
+
+int moe_update_bias(int64_t T, int32_t E, int32_t k, float gamma, const int32_t* counts,
+                    float* bias, void* stream) {
+  if (int r = check_common(T, E, k)) return r;
+  REQUIRE(isfinite(gamma), "gamma must be finite");
+  REQUIRE_PTR(counts);
+  REQUIRE_PTR(bias);
+  (void)hipGetLastError();
+  return launched(moe::launch_update_bias(T, E, k, gamma, counts, bias,
+                                          static_cast<hipStream_t>(stream)),
+                  "moe_update_bias");
 }
 
 int moe_permute(int64_t T, int64_t d_model, int32_t E, int32_t k, double CF, int32_t dtype,

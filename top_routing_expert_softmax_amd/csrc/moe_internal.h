@@ -27,9 +27,25 @@ size_t stats_workspace_bytes(int64_t T, int E);
 size_t ffn_workspace_bytes(int64_t T, int E, int E_shared, int k, int64_t d_ff,
                            int elem_bytes);
 
+struct GateParams;   // router.hip: which top-k follows the logits
+
 hipError_t launch_route(int64_t T, int64_t d, int E, int k, bool bf16,
                         const void* x, const void* w_gate, float* logits,
-                        int32_t* topk_idx, float* topk_w, void* ws, hipStream_t s);
+                        int32_t* topk_idx, float* topk_w, void* ws,
+                        const GateParams& gp, hipStream_t s);
+
+// The softmax top-k router and the DeepSeek-V3 gate.
+hipError_t launch_route_softmax(int64_t T, int64_t d, int E, int k, bool bf16,
+                                const void* x, const void* w_gate, float* logits,
+                                int32_t* topk_idx, float* topk_w, void* ws,
+                                hipStream_t s);
+hipError_t launch_route_v3(int64_t T, int64_t d, int E, int k, int n_groups,
+                           int topk_groups, float route_scale, bool bf16,
+                           const void* x, const void* w_gate, const float* bias,
+                           float* logits, int32_t* topk_idx, float* topk_w,
+                           void* ws, hipStream_t s);
+hipError_t launch_update_bias(int64_t T, int E, int k, float gamma,
+                              const int32_t* counts, float* bias, hipStream_t s);
 
 hipError_t launch_permute(int64_t T, int64_t d, int E, int k, int64_t cap,
                           bool bf16, const int32_t* topk_idx, const void* x,

@@ -18,6 +18,14 @@
 // rounds of a wave-wide max over (order key of the logit, -index) pick the
 // experts, larger logit first and ties to the lower index; the weights are
 // exp(g_j - g_max) / sum over the selected j.
+//
+// DeepSeek-V3 gate ("CMU 11-868 Lecture 17", section 5.3; the bias of
+// section 3.4), same logits: affinity s = sigmoid(g) (evaluated in fp64,
+// rounded once to fp32), biased = s + b in fp32; a group's score is the
+// fp32 sum of its two largest biased scores; topk_groups groups are kept
+// (ties to the lower group); the k largest biased scores inside them are
+// chosen (ties to the lower expert); the weights are the chosen unbiased
+// affinities over their sum, times route_scale.
 #include <math.h>
 
 #include <algorithm>
@@ -31,6 +39,21 @@ namespace {
 constexpr int kTW = 8;          // tokens per block
 constexpr int kMaxWavesR = 8;   // waves per block at most
 constexpr int kMaxSplits = 64;  // d-splits at most (decode)
+#ifndef MOE_ROUTER_SPLIT_BLOCKS
+#define MOE_ROUTER_SPLIT_BLOCKS 256  // blocks the d-split aims for
+#endif
+
+}  // namespace
+
+// Which top-k follows the logits (see the file comment).
+struct GateParams {
+  int v3;                 // 0: softmax top-k; 1: DeepSeek-V3 gate
+  const float* bias;      // [E] selection bias (V3)
+  int n_groups, topk_groups;
+  float route_scale;
+};
+
+namespace {
 
 __device__ __forceinline__ void load8(const uint16_t* p, float (&v)[8]) {
   const u32x4_t q = *reinterpret_cast<const u32x4_t*>(p);
@@ -127,6 +150,79 @@ __device__ __forceinline__ void topk_select(const float (&v)[4], int E, int k, i
   }
 }
 
+// DeepSeek-V3 gate of one token held by one wavefront: g_row (LDS) holds
+// the E logits, scratch (LDS, E floats) is this wave's own.
+__device__ __forceinline__ void v3_select(const float* g_row, float* scratch, const GateParams& gp,
+                                          int E, int k, int lane, int32_t* __restrict__ idx_row,
+                                          float* __restrict__ w_row) {
+  float s[4], bsc[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int e = lane + kWave * r;
+    s[r] = 0.f;
+    bsc[r] = 0.f;
+    if (e < E) {
+      s[r] = static_cast<float>(1.0 / (1.0 + exp(-static_cast<double>(g_row[e]))));
+      bsc[r] = s[r] + gp.bias[e];
+      scratch[e] = bsc[r];
+    }
+  }
+  // the scratch row is read by other lanes of this wave
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const int G = E / gp.n_groups;
+  // lane q < n_groups: the two largest biased scores of group q
+  uint32_t gkey = 0;
+  if (lane < gp.n_groups) {
+    float t1 = -INFINITY, t2 = -INFINITY;
+    for (int i = 0; i < G; ++i) {
+      const float v = scratch[lane * G + i];
+      if (v > t1) { t2 = t1; t1 = v; }
+      else if (v > t2) { t2 = v; }
+    }
+    gkey = f32_order_key(t1 + t2);
+  }
+  // keep topk_groups groups: rounds of a wave max over (score, -group)
+  uint64_t kept = 0;
+  for (int j = 0; j < gp.topk_groups; ++j) {
+    uint64_t key = 0;
+    if (lane < gp.n_groups && !((kept >> lane) & 1ull))
+      key = (static_cast<uint64_t>(gkey) << 32) | static_cast<uint64_t>(0xFFFFFFFFu - lane);
+    key = wave_max_u64(key);
+    kept |= 1ull << (0xFFFFFFFFu - static_cast<uint32_t>(key));
+  }
+  // k experts of the kept groups by biased score
+  uint32_t taken = 0;
+  float wsum = 0.f, my_s = 0.f;
+  int my_e = 0;
+  for (int j = 0; j < k; ++j) {
+    uint64_t best = 0;
+    float best_s = 0.f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int e = lane + kWave * r;
+      if (e < E && ((kept >> (e / G)) & 1ull) && !((taken >> r) & 1u)) {
+        const uint64_t key = (static_cast<uint64_t>(f32_order_key(bsc[r])) << 32) |
+                             static_cast<uint64_t>(0xFFFFFFFFu - static_cast<uint32_t>(e));
+        if (key > best) { best = key; best_s = s[r]; }
+      }
+    }
+    const uint64_t wbest = wave_max_u64(best);
+    const int e_sel = static_cast<int>(0xFFFFFFFFu - static_cast<uint32_t>(wbest));
+    // the lane that holds the winner broadcasts its affinity
+    const int owner = e_sel & (kWave - 1);
+    const float s_sel = __shfl(best_s, owner, kWave);
+    if (owner == lane) taken |= 1u << (e_sel / kWave);
+    wsum += s_sel;
+    if (lane == j) { my_s = s_sel; my_e = e_sel; }
+  }
+  if (lane < k) {
+    idx_row[lane] = my_e;
+    w_row[lane] = my_s / wsum * gp.route_scale;
+  }
+}
+
 // SPLIT = false: all of d, then the top-k epilogue.  SPLIT = true: the
 // chunk range [blockIdx.y * cps, +cps) of d, partial logits to
 // partial[blockIdx.y][t][e].
@@ -134,7 +230,8 @@ template <typename T, int EPL, bool SPLIT>
 __global__ __launch_bounds__(kMaxWavesR * kWave) void router_kernel(
     const T* __restrict__ x, const T* __restrict__ wg, float* __restrict__ logits,
     int32_t* __restrict__ topk_idx, float* __restrict__ topk_w, float* __restrict__ partial,
-    int nT, int d, int E, int k, int ES, int chunks_per_wave, int chunks_per_split) {
+    int nT, int d, int E, int k, int ES, int chunks_per_wave, int chunks_per_split,
+    GateParams gp) {
   extern __shared__ float smem[];
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
@@ -210,6 +307,12 @@ __global__ __launch_bounds__(kMaxWavesR * kWave) void router_kernel(
     const int t = t0 + tt;
     if (t >= nT) break;
     const float* row = lg + tt * E_pad;
+    if (gp.v3) {
+      // the per-wave reduction rows are free by now: scratch for the gate
+      v3_select(row, red + wave * kTW * E_pad, gp, E, k, lane,
+                topk_idx + static_cast<int64_t>(t) * k, topk_w + static_cast<int64_t>(t) * k);
+      continue;
+    }
     float v[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -227,8 +330,10 @@ __global__ __launch_bounds__(kMaxWavesR * kWave) void router_kernel(
 // then selects from the LDS copy of the row.
 __global__ __launch_bounds__(256) void router_select_kernel(
     const float* __restrict__ partial, float* __restrict__ logits,
-    int32_t* __restrict__ topk_idx, float* __restrict__ topk_w, int nT, int E, int k, int S) {
+    int32_t* __restrict__ topk_idx, float* __restrict__ topk_w, int nT, int E, int k, int S,
+    GateParams gp) {
   __shared__ float row[256];
+  __shared__ float scratch[256];
   const int t = blockIdx.x;
   const int e = threadIdx.x;
   float s8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
@@ -243,7 +348,10 @@ __global__ __launch_bounds__(256) void router_select_kernel(
   if (e < E) logits[static_cast<int64_t>(t) * E + e] = g;
   row[e] = g;
   __syncthreads();
-  if (threadIdx.x < kWave) {
+  if (threadIdx.x < kWave && gp.v3) {
+    v3_select(row, scratch, gp, E, k, threadIdx.x, topk_idx + static_cast<int64_t>(t) * k,
+              topk_w + static_cast<int64_t>(t) * k);
+  } else if (threadIdx.x < kWave) {
     const int lane = threadIdx.x;
     float v[4];
 #pragma unroll
@@ -273,7 +381,7 @@ RouterPlan plan_router(int64_t T, int64_t d, int E) {
   // the chip (each split keeps at least one chunk per ds lane)
   p.S = 1;
   if (p.nblocks < 128) {
-    p.S = (512 + p.nblocks - 1) / p.nblocks;
+    p.S = (MOE_ROUTER_SPLIT_BLOCKS + p.nblocks - 1) / p.nblocks;
     p.S = std::min(p.S, kMaxSplits);
     p.S = std::min(p.S, std::max(1, p.nchunk / p.DS));
   }
@@ -295,34 +403,47 @@ RouterPlan plan_router(int64_t T, int64_t d, int E) {
 template <typename T, int EPL>
 hipError_t launch_t(const RouterPlan& p, int64_t T_, int64_t d, int E, int k, const void* x,
                     const void* wg, float* logits, int32_t* idx, float* w, float* partial,
-                    hipStream_t s) {
+                    const GateParams& gp, hipStream_t s) {
   const size_t lds = static_cast<size_t>(p.nwaves + 1) * kTW * p.E_pad * 4;
   if (p.S == 1) {
     hipLaunchKernelGGL((router_kernel<T, EPL, false>), dim3(p.nblocks), dim3(p.nwaves * kWave),
                        lds, s, static_cast<const T*>(x), static_cast<const T*>(wg), logits, idx,
                        w, nullptr, static_cast<int>(T_), static_cast<int>(d), E, k, p.ES, p.cpw,
-                       p.cps);
+                       p.cps, gp);
   } else {
     hipLaunchKernelGGL((router_kernel<T, EPL, true>), dim3(p.nblocks, p.S),
                        dim3(p.nwaves * kWave), lds, s, static_cast<const T*>(x),
                        static_cast<const T*>(wg), logits, idx, w, partial, static_cast<int>(T_),
-                       static_cast<int>(d), E, k, p.ES, p.cpw, p.cps);
+                       static_cast<int>(d), E, k, p.ES, p.cpw, p.cps, gp);
     hipLaunchKernelGGL(router_select_kernel, dim3(static_cast<unsigned>(T_)), dim3(256), 0, s,
-                       partial, logits, idx, w, static_cast<int>(T_), E, k, p.S);
+                       partial, logits, idx, w, static_cast<int>(T_), E, k, p.S, gp);
   }
   return hipGetLastError();
 }
 
 template <typename T>
 hipError_t dispatch_epl(int64_t T_, int64_t d, int E, int k, const void* x, const void* wg,
-                        float* logits, int32_t* idx, float* w, float* partial, hipStream_t s) {
+                        float* logits, int32_t* idx, float* w, float* partial,
+                        const GateParams& gp, hipStream_t s) {
   const RouterPlan p = plan_router(T_, d, E);
   switch (p.EPL) {
-    case 8: return launch_t<T, 8>(p, T_, d, E, k, x, wg, logits, idx, w, partial, s);
-    case 4: return launch_t<T, 4>(p, T_, d, E, k, x, wg, logits, idx, w, partial, s);
-    case 2: return launch_t<T, 2>(p, T_, d, E, k, x, wg, logits, idx, w, partial, s);
-    default: return launch_t<T, 1>(p, T_, d, E, k, x, wg, logits, idx, w, partial, s);
+    case 8: return launch_t<T, 8>(p, T_, d, E, k, x, wg, logits, idx, w, partial, gp, s);
+    case 4: return launch_t<T, 4>(p, T_, d, E, k, x, wg, logits, idx, w, partial, gp, s);
+    case 2: return launch_t<T, 2>(p, T_, d, E, k, x, wg, logits, idx, w, partial, gp, s);
+    default: return launch_t<T, 1>(p, T_, d, E, k, x, wg, logits, idx, w, partial, gp, s);
   }
+}
+
+// Balance-bias step ("CMU 11-868 Lecture 17", section 3.4): thread e
+// compares counts[e] * E with T * k (the mean load, exactly).
+__global__ __launch_bounds__(256) void update_bias_kernel(const int32_t* __restrict__ counts,
+                                                          float* __restrict__ bias, int E,
+                                                          int64_t Tk, float gamma) {
+  const int e = threadIdx.x;
+  if (e >= E) return;
+  const int64_t load = static_cast<int64_t>(counts[e]) * E;
+  if (load > Tk) bias[e] = bias[e] - gamma;
+  else if (load < Tk) bias[e] = bias[e] + gamma;
 }
 
 }  // namespace
@@ -334,11 +455,33 @@ size_t route_workspace_bytes(int64_t T, int64_t d, int E) {
 
 hipError_t launch_route(int64_t T, int64_t d, int E, int k, bool bf16, const void* x,
                         const void* w_gate, float* logits, int32_t* topk_idx, float* topk_w,
-                        void* ws, hipStream_t s) {
+                        void* ws, const GateParams& gp, hipStream_t s) {
   float* partial = static_cast<float*>(ws);
   if (bf16)
-    return dispatch_epl<uint16_t>(T, d, E, k, x, w_gate, logits, topk_idx, topk_w, partial, s);
-  return dispatch_epl<float>(T, d, E, k, x, w_gate, logits, topk_idx, topk_w, partial, s);
+    return dispatch_epl<uint16_t>(T, d, E, k, x, w_gate, logits, topk_idx, topk_w, partial, gp,
+                                  s);
+  return dispatch_epl<float>(T, d, E, k, x, w_gate, logits, topk_idx, topk_w, partial, gp, s);
+}
+
+hipError_t launch_route_softmax(int64_t T, int64_t d, int E, int k, bool bf16, const void* x,
+                                const void* w_gate, float* logits, int32_t* topk_idx,
+                                float* topk_w, void* ws, hipStream_t s) {
+  const GateParams gp{0, nullptr, 1, 1, 1.0f};
+  return launch_route(T, d, E, k, bf16, x, w_gate, logits, topk_idx, topk_w, ws, gp, s);
+}
+
+hipError_t launch_route_v3(int64_t T, int64_t d, int E, int k, int n_groups, int topk_groups,
+                           float route_scale, bool bf16, const void* x, const void* w_gate,
+                           const float* bias, float* logits, int32_t* topk_idx, float* topk_w,
+                           void* ws, hipStream_t s) {
+  const GateParams gp{1, bias, n_groups, topk_groups, route_scale};
+  return launch_route(T, d, E, k, bf16, x, w_gate, logits, topk_idx, topk_w, ws, gp, s);
+}
+
+hipError_t launch_update_bias(int64_t T, int E, int k, float gamma, const int32_t* counts,
+                              float* bias, hipStream_t s) {
+  hipLaunchKernelGGL(update_bias_kernel, dim3(1), dim3(256), 0, s, counts, bias, E, T * k, gamma);
+  return hipGetLastError();
 }
 
 }  // namespace moe
