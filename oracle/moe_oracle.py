@@ -31,6 +31,11 @@ Readings where the pages are silent or disagree (each is listed in the design doc):
     kernel, so both sides take the same integer decisions); ties go to the
     lower group / expert index; the bias rule compares counts_i with the
     mean T k / E exactly.
+  * expert choice: capacity = floor((T // E) * CF) as the listing writes
+    it, clamped to T; each expert takes its capacity tokens with the largest
+    logits (ties to the lower token); the pages give no combine weight, so a
+    chosen (token, expert) pair is weighted by the router probability
+    softmax(g_t)_e, not renormalised, and a token no expert chose outputs 0.
 """
 from fractions import Fraction
 import math
@@ -43,6 +48,7 @@ __all__ = [
     "capacity", "dispatch", "silu", "swiglu_expert", "combine_grouped",
     "combine_per_token", "load_balance_loss", "aux_stats", "layer_forward",
     "affinity_f32", "v3_gate", "update_bias",
+    "ec_capacity", "expert_choice", "ec_dispatch", "ec_combine",
 ]
 
 
@@ -168,6 +174,63 @@ def update_bias(counts, bias, T, k, gamma):
     b[over] = b[over] - gam
     b[under] = b[under] + gam
     return b
+
+
+# ------------------------------------------------- expert choice (N3) --
+
+def ec_capacity(T, E, CF):
+    """Tokens per expert under expert choice: T // E tokens times the
+    capacity factor ([DD] section 2.2, ExpertChoiceRouter), floored (a top-k
+    size is an integer), at most T."""
+    c = Fraction(T // E) * Fraction(CF)
+    return int(min(T, max(0, c.numerator // c.denominator)))
+
+
+def expert_choice(g, cap):
+    """Expert choice ([DD] section 2.2): transpose the logits so experts come
+    first, and let each expert take the cap tokens with the largest logits
+    (larger first, ties to the lower token index).  Weights: the router
+    probability softmax(g_t)_e of each chosen pair ([RM] section 2.1's p;
+    the listing leaves the weight open)."""
+    g = _f64(g)
+    gt = g.T
+    tokens = np.argsort(-gt, axis=-1, kind="stable")[:, :cap].astype(np.int64)
+    p = softmax(g)
+    E = g.shape[1]
+    w = np.stack([p[tokens[e], e] for e in range(E)]) if cap else np.zeros((E, 0))
+    return {"logits": g, "probs": p, "tokens": tokens, "weights": w}
+
+
+def ec_dispatch(tokens, weights, T):
+    """Rows of the grouped layout: expert e owns rows e*cap .. e*cap+cap-1,
+    row e*cap+j holding token tokens[e][j] ([L17] section 2.2, one segment
+    per expert).  row_of_te[t][e] is that row or -1, w_te[t][e] its weight
+    or 0."""
+    E, cap = tokens.shape
+    row_of_te = -np.ones((T, E), dtype=np.int64)
+    w_te = np.zeros((T, E))
+    for e in range(E):
+        for j in range(cap):
+            row_of_te[tokens[e, j], e] = e * cap + j
+            w_te[tokens[e, j], e] = weights[e, j]
+    return {"offsets": np.arange(E + 1, dtype=np.int64) * cap,
+            "token_of_row": tokens.reshape(-1), "row_of_te": row_of_te, "w_te": w_te}
+
+
+def ec_combine(x, tokens, weights, load_expert, shared_out=None):
+    """y_t = sum_s Shared_s(x_t) + sum over experts e that chose t of
+    w_{t,e} Expert_e(x_t); per expert, one product over its chosen rows."""
+    x = _f64(x)
+    y = np.zeros_like(x)
+    if shared_out is not None:
+        y += _f64(shared_out)
+    for e in range(tokens.shape[0]):
+        if tokens.shape[1] == 0:
+            break
+        out = swiglu_expert(x[tokens[e]], *load_expert(e))
+        for j, t in enumerate(tokens[e]):
+            y[t] += weights[e, j] * out[j]
+    return y
 
 
 # --------------------------------------------------------------- dispatch --
