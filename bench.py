@@ -134,10 +134,11 @@ def main():
     ap.add_argument("--cpu-sample", type=int, default=4096,
                     help="tokens whose expert outputs the oracle computes")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--router", default="softmax", choices=["softmax", "v3"],
+    ap.add_argument("--router", default="softmax", choices=["softmax", "v3", "ec"],
                     help="softmax top-k router (moe_route) or the DeepSeek-V3 gate "
                          "(moe_route_v3: 8 groups, 4 kept, scale 2.5, seeded bias in "
-                         "+-1e-3)")
+                         "+-1e-3) or expert choice (moe_route_ec + moe_permute_ec, "
+                         "capacity factor 1)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes (reference for "
                          "the FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -184,7 +185,42 @@ def main():
                            v3["topk_groups"], v3["route_scale"], b.logits, b.topk_idx,
                            b.topk_w, b.ws, stream)
 
+    ec = None
+    if args.router == "ec":
+        cap = M.moe_ec_capacity(T, E, 1.0)
+        kf = M.ec_ffn_k(T, E, cap)
+        emp = lambda *shape, dt=torch.float32: torch.empty(shape, dtype=dt, device="cuda")  # noqa
+        ec = {"cap": cap, "k": kf, "tok": emp(E, cap, dt=torch.int32), "w": emp(E, cap),
+              "rte": emp(T, E, dt=torch.int32), "wte": emp(T, E),
+              "x_perm": emp(T * kf, d, dt=dtype), "y_perm": emp(T * kf, d, dt=dtype),
+              "ws": torch.empty(M.moe_workspace_size(T, d, E, Es, kf, F, dtype),
+                                dtype=torch.uint8, device="cuda")}
+
+    def step_ec(timed):
+        # expert choice: route, gather, the same grouped FFN, combine with k = E
+        if timed:
+            ev[0].record(stream)
+        M.moe_route_ec(dev["x"], dev["wg"], ec["cap"], b.logits, ec["tok"], ec["w"], ec["ws"],
+                       stream)
+        if timed:
+            ev[1].record(stream)
+        M.moe_permute_ec(ec["tok"], ec["w"], dev["x"], b.offsets, ec["rte"], ec["wte"],
+                         ec["x_perm"], stream)
+        if timed:
+            ev[2].record(stream)
+        M.moe_expert_ffn(T, ec["k"], ec["x_perm"], b.offsets, dev["x"], dev["w1"], dev["w3"],
+                         dev["w2"], dev.get("ws1"), dev.get("ws3"), dev.get("ws2"),
+                         ec["y_perm"], b.y_shared, ec["ws"], stream)
+        if timed:
+            ev[3].record(stream)
+        M.moe_combine(ec["y_perm"], b.y_shared, ec["rte"], ec["wte"], b.y, stream)
+        if timed:
+            ev[4].record(stream)
+            ev[5].record(stream)
+
     def step(timed):
+        if ec is not None:
+            return step_ec(timed)
         if timed:
             ev[0].record(stream)
         route()
@@ -226,8 +262,13 @@ def main():
     ms = elapsed * 1e3 / args.steps
     tokens_per_s = T / (ms / 1e3)
 
-    counts = b.counts.cpu().numpy()
-    cap = M.moe_capacity(T, E, k, cfg.CF)
+    if ec is None:
+        counts = b.counts.cpu().numpy()
+        cap = M.moe_capacity(T, E, k, cfg.CF)
+    else:
+        # every expert takes exactly cap tokens
+        cap = ec["cap"]
+        counts = np.full(E, cap)
     flop, bytes_alg, touched, rows = gemm_work(cfg, counts, cap)
     ffn_ms = float(per_call[names.index("expert_ffn")])
     if cfg.T <= 256:      # decode-shaped: weight streaming, HBM-bound
@@ -247,6 +288,9 @@ def main():
     roof["kernel_ms"] = round(ffn_ms, 4)
 
     extra = {}
+    if ec is not None:
+        extra = {"router": "expert_choice", "ec_capacity": ec["cap"], "ec_ffn_k": ec["k"],
+                 "tokens_unpicked": int(T - torch.unique(ec["tok"]).numel())}
     if v3 is not None:
         # the balance-bias step, timed on its own (a training-time update,
         # not part of the forward step); restored afterwards
@@ -263,7 +307,7 @@ def main():
         v3["bias"].copy_(saved)
 
     cpu = None
-    if not args.no_cpu_baseline and v3 is None:
+    if not args.no_cpu_baseline and v3 is None and ec is None:
         log("timing the CPU oracle on a token sample")
         v, threads, n, dt = cpu_baseline(cfg, x, wg, host, args.cpu_sample)
         cpu = {"value": round(v, 3), "unit": "tokens/s", "cores": int(threads),

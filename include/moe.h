@@ -148,6 +148,47 @@ int moe_update_bias(int64_t T, int32_t E, int32_t k, float gamma,
                     const int32_t* counts, float* bias, void* stream);
 
 /*
+ * Expert choice ("MoE deep dive: routing mechanisms and load balancing",
+ * section 2.2): experts pick tokens.  Tokens per expert
+ *   cap = min(T, floor((T // E) * CF))       (exact on the double CF)
+ * Host only; CF >= 0.
+ */
+int moe_ec_capacity(int64_t T, int32_t E, double CF, int64_t* cap);
+
+/*
+ * Expert-choice router: logits g = x W_gate as in moe_route, then each
+ * expert e takes the cap tokens with the largest g[t][e] (larger first, ties
+ * to the lower token index).  The weight of a chosen pair is the router
+ * probability softmax(g[t])[e] (fp32); it is not renormalised.
+ *   x [T, d], w_gate [d, E]  dtype in;  logits [T, E] fp32 out
+ *   ec_token [E, cap] int32 out;  ec_w [E, cap] fp32 out
+ *   ws: moe_workspace_size() bytes
+ * Limits: 0 <= cap <= min(T, 4096); T * E < 2^31.
+ */
+int moe_route_ec(int64_t T, int64_t d_model, int32_t E, int64_t cap,
+                 int32_t dtype, const void* x, const void* w_gate,
+                 float* logits, int32_t* ec_token, float* ec_w, void* ws,
+                 size_t ws_bytes, void* stream);
+
+/*
+ * Grouped layout of the expert-choice picks ("CMU 11-868 Lecture 17" section
+ * 2.2, one segment per expert): expert e owns rows e*cap .. e*cap+cap-1.
+ *   ec_token, ec_w [E, cap]   in (from moe_route_ec)
+ *   x [T, d] dtype            in
+ *   offsets [E + 1] int32     out  e * cap
+ *   row_of_te [T, E] int32    out  row of (t, e), -1 if e did not pick t
+ *   w_te [T, E] fp32          out  weight of (t, e), 0 if e did not pick t
+ *   x_perm [E * cap, d] dtype out  row r = x[ec_token[r]]
+ * Then moe_expert_ffn runs unchanged with k = ceil(E * cap / T) (its row
+ * bound T * k covers the E * cap rows), and moe_combine with k = E,
+ * row_of_pair = row_of_te and topk_w = w_te.
+ */
+int moe_permute_ec(int64_t T, int64_t d_model, int32_t E, int64_t cap,
+                   int32_t dtype, const int32_t* ec_token, const float* ec_w,
+                   const void* x, int32_t* offsets, int32_t* row_of_te,
+                   float* w_te, void* x_perm, void* stream);
+
+/*
  * Counting, capacity, drop and permutation, "CMU 11-868 Lecture 17"
  * sections 2.2 (group by expert) and 2.4 (capacity, overflow dropped).
  * Pairs (t, j) are ranked inside their expert in token order; a pair is
@@ -200,7 +241,8 @@ int moe_expert_ffn(int64_t T, int64_t d_model, int32_t E, int32_t E_shared,
  *   y[t] = sum_s y_shared[s][t] + sum_{j : row_of_pair[t][j] >= 0}
  *          topk_w[t][j] * y_perm[row_of_pair[t][j]]
  * A dropped pair adds nothing; the surviving weights are not renormalised.
- * Summation in fp32: shared experts first, then j = 0..k-1.
+ * Summation in fp32: shared experts first, then j = 0..k-1.  1 <= k <= 256
+ * (expert choice passes k = E).
  *   y_perm [T*k, d] dtype in; y_shared [E_shared, T, d] dtype in (NULL if
  *   E_shared == 0); row_of_pair [T, k] int32 in; topk_w [T, k] fp32 in;
  *   y [T, d] dtype out.

@@ -135,3 +135,31 @@ def test_v3_gate_arguments_are_checked(M):
     assert v3(bias=nil) == -1 and "bias is NULL" in L.moe_last_error().decode()
     assert L.moe_update_bias(64, 256, 8, float("inf"), fake, fake, nil) == -1
     assert L.moe_update_bias(64, 256, 8, 1e-3, nil, fake, nil) == -1
+
+
+def test_expert_choice_capacity_and_arguments(M):
+    rng = np.random.default_rng(5)
+    cases = [(4096, 8, 1.0), (4096, 8, 1.25), (10, 3, 0.5), (64, 256, 1.0), (5, 1, 3.0),
+             (7, 7, 1e-300), (100000, 3, 1e30), (9, 2, 0.0)]
+    for _ in range(300):
+        T = int(rng.integers(1, 100000))
+        E = int(rng.integers(1, 257))
+        CF = float(rng.choice([rng.uniform(0, 4), rng.integers(0, 17) / 8, 1 / 3]))
+        cases.append((T, E, CF))
+    for T, E, CF in cases:
+        assert M.moe_ec_capacity(T, E, CF) == O.ec_capacity(T, E, CF), (T, E, CF)
+    L = M.lib()
+    nil = ctypes.c_void_p(0)
+    fake = ctypes.c_void_p(4096)
+    ws = 1 << 30
+    assert L.moe_route_ec(100, 128, 8, 101, M.MOE_BF16, fake, fake, fake, fake, fake, fake, ws,
+                          nil) == -1                                         # cap > T
+    assert L.moe_route_ec(10000, 128, 8, 5000, M.MOE_BF16, fake, fake, fake, fake, fake, fake,
+                          ws, nil) == -1                                     # cap > 4096
+    assert L.moe_route_ec(100, 128, 300, 1, M.MOE_BF16, fake, fake, fake, fake, fake, fake, ws,
+                          nil) == -1                                         # E > 256
+    assert L.moe_route_ec(100, 128, 8, 10, M.MOE_BF16, fake, fake, fake, fake, fake, fake, 8,
+                          nil) == -4                                         # workspace
+    assert L.moe_permute_ec(100, 128, 8, 10, M.MOE_BF16, fake, fake, fake, fake, nil, fake, fake,
+                            nil) == -1                                       # row_of_te NULL
+    assert L.moe_ec_capacity(10, 2, -1.0, ctypes.byref(ctypes.c_int64())) == -1

@@ -20,8 +20,8 @@ MOE_BF16 = 1
 
 # Symbols declared in include/moe.h.
 EXPORTS = ("moe_strerror", "moe_last_error", "moe_capacity", "moe_workspace_size",
-           "moe_route", "moe_route_v3", "moe_update_bias", "moe_permute", "moe_expert_ffn",
-           "moe_combine", "moe_aux_stats")
+           "moe_route", "moe_route_v3", "moe_update_bias", "moe_ec_capacity", "moe_route_ec",
+           "moe_permute_ec", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_aux_stats")
 
 _lib = None
 
@@ -60,6 +60,12 @@ def lib():
                                vp, sz, vp]
     L.moe_update_bias.restype = ctypes.c_int
     L.moe_update_bias.argtypes = [i64, i32, i32, f32, vp, vp, vp]
+    L.moe_ec_capacity.restype = ctypes.c_int
+    L.moe_ec_capacity.argtypes = [i64, i32, f64, ctypes.POINTER(i64)]
+    L.moe_route_ec.restype = ctypes.c_int
+    L.moe_route_ec.argtypes = [i64, i64, i32, i64, i32, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.moe_permute_ec.restype = ctypes.c_int
+    L.moe_permute_ec.argtypes = [i64, i64, i32, i64, i32, vp, vp, vp, vp, vp, vp, vp, vp]
     L.moe_permute.restype = ctypes.c_int
     L.moe_permute.argtypes = [i64, i64, i32, i32, f64, i32, vp, vp, vp, vp, vp, vp, vp, vp,
                               vp, sz, vp]
@@ -139,6 +145,35 @@ def moe_update_bias(T, k, gamma, counts, bias, stream=None):
     E = bias.shape[0]
     _check("moe_update_bias", lib().moe_update_bias(T, E, k, float(gamma), _ptr(counts),
                                                     _ptr(bias), _stream(stream)))
+
+
+def moe_ec_capacity(T, E, CF):
+    """Expert choice: tokens per expert, min(T, floor((T // E) * CF))."""
+    cap = ctypes.c_int64()
+    _check("moe_ec_capacity", lib().moe_ec_capacity(T, E, float(CF), ctypes.byref(cap)))
+    return cap.value
+
+
+def moe_route_ec(x, w_gate, cap, logits, ec_token, ec_w, ws, stream=None):
+    T, d = x.shape
+    E = w_gate.shape[1]
+    _check("moe_route_ec", lib().moe_route_ec(
+        T, d, E, cap, _dtype_code(x), _ptr(x), _ptr(w_gate), _ptr(logits), _ptr(ec_token),
+        _ptr(ec_w), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def moe_permute_ec(ec_token, ec_w, x, offsets, row_of_te, w_te, x_perm, stream=None):
+    E, cap = ec_token.shape
+    T, d = x.shape
+    _check("moe_permute_ec", lib().moe_permute_ec(
+        T, d, E, cap, _dtype_code(x), _ptr(ec_token), _ptr(ec_w), _ptr(x), _ptr(offsets),
+        _ptr(row_of_te), _ptr(w_te), _ptr(x_perm), _stream(stream)))
+
+
+def ec_ffn_k(T, E, cap):
+    """The k to pass moe_expert_ffn / moe_workspace_size for expert choice:
+    its row bound T * k must cover the E * cap rows."""
+    return max(1, -(-(E * cap) // T))
 
 
 def moe_permute(topk_idx, x, E, CF, counts, offsets, token_of_row, row_of_pair, drop_mask,

@@ -14,7 +14,7 @@
 namespace moe {
 namespace {
 
-constexpr int kMaxK = 64;
+constexpr int kMaxK = 256;   // k; expert choice passes k = E
 constexpr int kTokPB = 4;   // tokens (wavefronts) per block
 
 __device__ __forceinline__ void acc_chunk(float (&a)[8], const u32x4_t q, float w) {
@@ -38,9 +38,9 @@ __global__ __launch_bounds__(256) void combine_bf16_kernel(
   const int wv = threadIdx.x / kWave;
   const int t = blockIdx.x * kTokPB + wv;
   if (t >= nT) return;
-  if (lane < k) {
-    s_rows[wv][lane] = row_of_pair[static_cast<int64_t>(t) * k + lane];
-    s_w[wv][lane] = topk_w[static_cast<int64_t>(t) * k + lane];
+  for (int j = lane; j < k; j += kWave) {
+    s_rows[wv][j] = row_of_pair[static_cast<int64_t>(t) * k + j];
+    s_w[wv][j] = topk_w[static_cast<int64_t>(t) * k + j];
   }
   __builtin_amdgcn_wave_barrier();
   const int* rows = s_rows[wv];
@@ -56,7 +56,8 @@ __global__ __launch_bounds__(256) void combine_bf16_kernel(
       for (int u = 0; u < 8; ++u) {
         const int j = j0 + u;
         const int r = j < k ? rows[j] : -1;
-        q[u] = y_perm[static_cast<int64_t>(r >= 0 ? r : 0) * chunks + c];
+        // r is the same for the whole wavefront (one token): no divergence
+        q[u] = r >= 0 ? y_perm[static_cast<int64_t>(r) * chunks + c] : u32x4_t{0u, 0u, 0u, 0u};
       }
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
@@ -84,9 +85,9 @@ __global__ __launch_bounds__(256) void combine_f32_kernel(
   const int wv = threadIdx.x / kWave;
   const int t = blockIdx.x * kTokPB + wv;
   if (t >= nT) return;
-  if (lane < k) {
-    s_rows[wv][lane] = row_of_pair[static_cast<int64_t>(t) * k + lane];
-    s_w[wv][lane] = topk_w[static_cast<int64_t>(t) * k + lane];
+  for (int j = lane; j < k; j += kWave) {
+    s_rows[wv][j] = row_of_pair[static_cast<int64_t>(t) * k + j];
+    s_w[wv][j] = topk_w[static_cast<int64_t>(t) * k + j];
   }
   __builtin_amdgcn_wave_barrier();
   const int* rows = s_rows[wv];

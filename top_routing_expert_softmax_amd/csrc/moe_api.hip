@@ -88,6 +88,25 @@ int64_t exact_capacity(int64_t T, int32_t E, int32_t k, double CF) {
   return std::min<int64_t>(c, T);
 }
 
+// floor((T // E) * CF) on the exact double value of CF, at most T.
+int64_t ec_capacity_exact(int64_t T, int32_t E, double CF) {
+  const int64_t base = T / E;
+  if (base == 0 || !(CF > 0.0)) return 0;
+  int ex = 0;
+  const double fr = frexp(CF, &ex);
+  const int64_t m = static_cast<int64_t>(ldexp(fr, 53));       // CF = m * 2^(ex - 53)
+  ex -= 53;
+  __int128 num = static_cast<__int128>(m) * base;              // < 2^84
+  if (ex >= 0) {
+    if (ex >= 40) return T;
+    num <<= ex;
+    return static_cast<int64_t>(std::min<__int128>(num, static_cast<__int128>(T)));
+  }
+  const int sh = -ex;
+  if (sh >= 100) return 0;
+  return static_cast<int64_t>(std::min<__int128>(num >> sh, static_cast<__int128>(T)));
+}
+
 size_t align256(size_t b) { return (b + 255) & ~static_cast<size_t>(255); }
 
 size_t workspace_bytes(int64_t T, int64_t d, int32_t E, int32_t Es, int32_t k, int64_t F,
@@ -96,6 +115,7 @@ size_t workspace_bytes(int64_t T, int64_t d, int32_t E, int32_t Es, int32_t k, i
   size_t b = moe::route_workspace_bytes(T, d, E);
   b = std::max(b, moe::permute_workspace_bytes(T, E));
   b = std::max(b, moe::stats_workspace_bytes(T, E));
+  b = std::max(b, moe::ec_workspace_bytes(T, d, E));
   b = std::max(b, moe::ffn_workspace_bytes(T, E, Es, k, F, elem));
   return align256(b);
 }
@@ -210,6 +230,70 @@ int moe_update_bias(int64_t T, int32_t E, int32_t k, float gamma, const int32_t*
                   "moe_update_bias");
 }
 
+int moe_ec_capacity(int64_t T, int32_t E, double CF, int64_t* cap) {
+  REQUIRE(T >= 1, "T must be >= 1 (got %lld)", static_cast<long long>(T));
+  REQUIRE(E >= 1 && E <= 256, "E must be in [1, 256] (got %d)", E);
+  REQUIRE(cap != nullptr, "cap is NULL");
+  REQUIRE(isfinite(CF) && CF >= 0.0, "CF must be finite and >= 0");
+  *cap = ec_capacity_exact(T, E, CF);
+  return MOE_OK;
+}
+
+static int check_ec(int64_t T, int32_t E, int64_t cap) {
+  REQUIRE(T >= 1, "T must be >= 1 (got %lld)", static_cast<long long>(T));
+  REQUIRE(E >= 1 && E <= 256, "E must be in [1, 256] (got %d)", E);
+  REQUIRE(T * E < (int64_t(1) << 31), "T*E must be < 2^31");
+  REQUIRE(cap >= 0 && cap <= T && cap <= moe::kEcMaxCap,
+          "cap must be in [0, min(T, %d)] (got %lld)", moe::kEcMaxCap,
+          static_cast<long long>(cap));
+  return MOE_OK;
+}
+
+int moe_route_ec(int64_t T, int64_t d_model, int32_t E, int64_t cap, int32_t dtype, const void* x,
+                 const void* w_gate, float* logits, int32_t* ec_token, float* ec_w, void* ws,
+                 size_t ws_bytes, void* stream) {
+  if (int r = check_ec(T, E, cap)) return r;
+  if (int r = check_dtype(dtype)) return r;
+  if (int r = check_dim("d_model", d_model)) return r;
+  REQUIRE_PTR(x);
+  REQUIRE_PTR(w_gate);
+  REQUIRE_PTR(logits);
+  if (cap > 0) {
+    REQUIRE_PTR(ec_token);
+    REQUIRE_PTR(ec_w);
+  }
+  REQUIRE_PTR(ws);
+  const size_t need = moe::ec_workspace_bytes(T, d_model, E);
+  if (ws_bytes < need)
+    return fail(MOE_EWORKSPACE, "moe_route_ec needs %zu workspace bytes, got %zu", need, ws_bytes);
+  (void)hipGetLastError();
+  return launched(moe::launch_route_ec(T, d_model, E, cap, dtype == MOE_BF16, x, w_gate, logits,
+                                       ec_token, ec_w, ws, static_cast<hipStream_t>(stream)),
+                  "moe_route_ec");
+}
+
+int moe_permute_ec(int64_t T, int64_t d_model, int32_t E, int64_t cap, int32_t dtype,
+                   const int32_t* ec_token, const float* ec_w, const void* x, int32_t* offsets,
+                   int32_t* row_of_te, float* w_te, void* x_perm, void* stream) {
+  if (int r = check_ec(T, E, cap)) return r;
+  if (int r = check_dtype(dtype)) return r;
+  if (int r = check_dim("d_model", d_model)) return r;
+  if (cap > 0) {
+    REQUIRE_PTR(ec_token);
+    REQUIRE_PTR(ec_w);
+    REQUIRE_PTR(x);
+    REQUIRE_PTR(x_perm);
+  }
+  REQUIRE_PTR(offsets);
+  REQUIRE_PTR(row_of_te);
+  REQUIRE_PTR(w_te);
+  (void)hipGetLastError();
+  return launched(moe::launch_permute_ec(T, d_model, E, cap, dtype == MOE_BF16, ec_token, ec_w,
+                                         x, offsets, row_of_te, w_te, x_perm,
+                                         static_cast<hipStream_t>(stream)),
+                  "moe_permute_ec");
+}
+
 int moe_permute(int64_t T, int64_t d_model, int32_t E, int32_t k, double CF, int32_t dtype,
                 const int32_t* topk_idx, const void* x, int32_t* counts, int32_t* offsets,
                 int32_t* token_of_row, int32_t* row_of_pair, uint8_t* drop_mask, void* x_perm,
@@ -279,7 +363,7 @@ int moe_combine(int64_t T, int64_t d_model, int32_t E_shared, int32_t k, int32_t
                 const void* y_perm, const void* y_shared, const int32_t* row_of_pair,
                 const float* topk_w, void* y, void* stream) {
   REQUIRE(T >= 1, "T must be >= 1");
-  REQUIRE(k >= 1 && k <= 64, "k must be in [1, 64]");
+  REQUIRE(k >= 1 && k <= 256, "k must be in [1, 256]");
   REQUIRE(T * k < (int64_t(1) << 31), "T*k must be < 2^31");
   if (int r = check_dtype(dtype)) return r;
   if (int r = check_dim("d_model", d_model)) return r;

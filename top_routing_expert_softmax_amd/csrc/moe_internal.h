@@ -17,6 +17,10 @@ constexpr int kMaxDispatchBlocks = 64;
 // Statistics: at most this many partial blocks.
 constexpr int kStatsBlocks = 256;
 
+// Expert choice: at most this many tokens per expert (the picks of one
+// expert are sorted in LDS).
+constexpr int kEcMaxCap = 4096;
+
 // Decode-sized expert segments (at most this many rows) take the
 // weight-streaming FFN kernels.
 constexpr int kStreamMaxRows = 64;
@@ -46,6 +50,19 @@ hipError_t launch_route_v3(int64_t T, int64_t d, int E, int k, int n_groups,
                            void* ws, hipStream_t s);
 hipError_t launch_update_bias(int64_t T, int E, int k, float gamma,
                               const int32_t* counts, float* bias, hipStream_t s);
+// Logits only (no top-k).
+hipError_t launch_logits(int64_t T, int64_t d, int E, bool bf16, const void* x,
+                         const void* w_gate, float* logits, void* ws, hipStream_t s);
+
+// Expert choice (ec.hip).
+size_t ec_workspace_bytes(int64_t T, int64_t d, int E);
+hipError_t launch_route_ec(int64_t T, int64_t d, int E, int64_t cap, bool bf16,
+                           const void* x, const void* w_gate, float* logits,
+                           int32_t* ec_token, float* ec_w, void* ws, hipStream_t s);
+hipError_t launch_permute_ec(int64_t T, int64_t d, int E, int64_t cap, bool bf16,
+                             const int32_t* ec_token, const float* ec_w,
+                             const void* x, int32_t* offsets, int32_t* row_of_te,
+                             float* w_te, void* x_perm, hipStream_t s);
 
 hipError_t launch_permute(int64_t T, int64_t d, int E, int k, int64_t cap,
                           bool bf16, const int32_t* topk_idx, const void* x,

@@ -47,7 +47,7 @@ constexpr int kMaxSplits = 64;  // d-splits at most (decode)
 
 // Which top-k follows the logits (see the file comment).
 struct GateParams {
-  int v3;                 // 0: softmax top-k; 1: DeepSeek-V3 gate
+  int v3;                 // 0: softmax top-k; 1: DeepSeek-V3 gate; 2: logits only
   const float* bias;      // [E] selection bias (V3)
   int n_groups, topk_groups;
   float route_scale;
@@ -301,13 +301,13 @@ __global__ __launch_bounds__(kMaxWavesR * kWave) void router_kernel(
     const int t = q / E_pad, e = q % E_pad;
     if (t0 + t < nT && e < E) dst[static_cast<int64_t>(t0 + t) * E + e] = s;
   }
-  if (SPLIT) return;
+  if (SPLIT || gp.v3 == 2) return;
   __syncthreads();
   for (int tt = wave; tt < kTW; tt += nwaves) {
     const int t = t0 + tt;
     if (t >= nT) break;
     const float* row = lg + tt * E_pad;
-    if (gp.v3) {
+    if (gp.v3 == 1) {
       // the per-wave reduction rows are free by now: scratch for the gate
       v3_select(row, red + wave * kTW * E_pad, gp, E, k, lane,
                 topk_idx + static_cast<int64_t>(t) * k, topk_w + static_cast<int64_t>(t) * k);
@@ -346,9 +346,10 @@ __global__ __launch_bounds__(256) void router_select_kernel(
   }
   const float g = ((s8[0] + s8[1]) + (s8[2] + s8[3])) + ((s8[4] + s8[5]) + (s8[6] + s8[7]));
   if (e < E) logits[static_cast<int64_t>(t) * E + e] = g;
+  if (gp.v3 == 2) return;
   row[e] = g;
   __syncthreads();
-  if (threadIdx.x < kWave && gp.v3) {
+  if (threadIdx.x < kWave && gp.v3 == 1) {
     v3_select(row, scratch, gp, E, k, threadIdx.x, topk_idx + static_cast<int64_t>(t) * k,
               topk_w + static_cast<int64_t>(t) * k);
   } else if (threadIdx.x < kWave) {
@@ -476,6 +477,12 @@ hipError_t launch_route_v3(int64_t T, int64_t d, int E, int k, int n_groups, int
                            void* ws, hipStream_t s) {
   const GateParams gp{1, bias, n_groups, topk_groups, route_scale};
   return launch_route(T, d, E, k, bf16, x, w_gate, logits, topk_idx, topk_w, ws, gp, s);
+}
+
+hipError_t launch_logits(int64_t T, int64_t d, int E, bool bf16, const void* x,
+                         const void* w_gate, float* logits, void* ws, hipStream_t s) {
+  const GateParams gp{2, nullptr, 1, 1, 1.0f};
+  return launch_route(T, d, E, 1, bf16, x, w_gate, logits, nullptr, nullptr, ws, gp, s);
 }
 
 hipError_t launch_update_bias(int64_t T, int E, int k, float gamma, const int32_t* counts,
