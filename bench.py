@@ -32,11 +32,12 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 
 # HBM bytes per moe_expert_ffn call measured with rocprofv3 FETCH_SIZE and
 # WRITE_SIZE (scaled by a plain copy of known size), keyed by the workload
-# and the sha256 prefix of the GEMM source they were taken with.  A changed
+# and the sha256 prefix of the expert-FFN sources (ffn.hip, ffn_stream.hip)
+# they were taken with (softmax router).  A changed
 # kernel reports null until it is measured again.
 MEASURED_TRAFFIC = {
-    ("mixtral_prefill", "19897c51a0a23860"): 8.605e9,
-    ("dsv3_decode", "19897c51a0a23860"): 1.9786e10,
+    ("mixtral_prefill", "a4187651e2873ded"): 8.8014e9,
+    ("dsv3_decode", "a4187651e2873ded"): 1.96668e10,
 }
 
 
@@ -281,9 +282,14 @@ def main():
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak,
                 "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None}
     import hashlib
-    with open(os.path.join(ROOT, "top_routing_expert_softmax_amd", "csrc", "ffn.hip"), "rb") as fh:
-        src_hash = hashlib.sha256(fh.read()).hexdigest()[:16]
-    roof["traffic"] = MEASURED_TRAFFIC.get((cfg.name, src_hash))
+    h = hashlib.sha256()
+    for src in ("ffn.hip", "ffn_stream.hip"):
+        with open(os.path.join(ROOT, "top_routing_expert_softmax_amd", "csrc", src), "rb") as fh:
+            h.update(fh.read())
+    src_hash = h.hexdigest()[:16]
+    # counters were taken with the softmax router (the routing decides the rows)
+    roof["traffic"] = (MEASURED_TRAFFIC.get((cfg.name, src_hash))
+                       if args.router == "softmax" else None)
     roof["kernel"] = "moe_expert_ffn (grouped GEMM phase 1 + phase 2 + tile table)"
     roof["kernel_ms"] = round(ffn_ms, 4)
 
