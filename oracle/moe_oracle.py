@@ -36,6 +36,11 @@ Readings where the pages are silent or disagree (each is listed in the design doc):
     logits (ties to the lower token); the pages give no combine weight, so a
     chosen (token, expert) pair is weighted by the router probability
     softmax(g_t)_e, not renormalised, and a token no expert chose outputs 0.
+  * FP8 expert weights: the pages name FP8 storage but no encoding or scale;
+    taken here: OCP FP8 E4M3 (bias 7, no infinities, largest finite 448),
+    one fp32 scale per stored weight row s = max|w_row| / 448 (fp32
+    division), codes = round-to-nearest-even of the fp32 quotient w / s,
+    clamped to +-448; the weight the layer uses is s * decode(code).
 """
 from fractions import Fraction
 import math
@@ -49,6 +54,7 @@ __all__ = [
     "combine_per_token", "load_balance_loss", "aux_stats", "layer_forward",
     "affinity_f32", "v3_gate", "update_bias",
     "ec_capacity", "expert_choice", "ec_dispatch", "ec_combine",
+    "e4m3_decode", "e4m3_encode", "quantize_fp8_rows", "dequantize_fp8_rows",
 ]
 
 
@@ -231,6 +237,57 @@ def ec_combine(x, tokens, weights, load_expert, shared_out=None):
         for j, t in enumerate(tokens[e]):
             y[t] += weights[e, j] * out[j]
     return y
+
+
+# ----------------------------------------------- FP8 expert weights (N4) --
+
+def e4m3_decode(codes):
+    """Value of OCP FP8 E4M3 codes: sign bit, 4 exponent bits (bias 7), 3
+    mantissa bits; exponent 0 is subnormal (m * 2^-9); 0x7F / 0xFF are NaN
+    (never produced here)."""
+    c = np.asarray(codes, dtype=np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = c & 0x7
+    val = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    val = np.where((c & 0x7F) == 0x7F, np.nan, val)
+    return sign * val
+
+
+def e4m3_encode(v):
+    """Round-to-nearest-even of fp32 values to E4M3 codes, saturating at
+    +-448.  Exact on the fp32 input: |v| = q * step with step = 2^(E-3) the
+    grid spacing of its binade 2^E (2^-9 below 2^-6, the subnormals), so
+    rint(q) (ties to even) picks the nearest grid value."""
+    v = np.asarray(v, dtype=np.float32).astype(np.float64)
+    sign = np.signbit(v)
+    a = np.minimum(np.abs(v), 448.0)
+    _, ex = np.frexp(np.maximum(a, 2.0 ** -6))          # a = f 2^ex, f in [0.5, 1)
+    step = np.ldexp(1.0, ex - 4)                        # 2^(E-3) with E = ex - 1
+    val = np.rint(a / step) * step                      # nearest, ties to even
+    sub = val < 2.0 ** -6
+    _, ev = np.frexp(np.where(sub, 1.0, val))
+    E = ev - 1
+    m = np.where(sub, 0, np.rint(np.ldexp(val, -E) * 8) - 8)
+    code = np.where(sub, np.rint(val * 2.0 ** 9), ((E + 7) << 3) + m).astype(np.int64)
+    return np.where(sign, code | 0x80, code).astype(np.uint8)
+
+
+def quantize_fp8_rows(w):
+    """Per-row FP8 quantisation of a weight matrix (rows = the stored rows,
+    each one output feature): s = fp32(max|w_row|) / 448 in fp32, codes =
+    E4M3 RNE of fp32(w / s).  All-zero rows get s = 1.  Returns (codes,
+    scales)."""
+    w = np.asarray(w, dtype=np.float32)
+    amax = np.abs(w).max(axis=-1)
+    s = np.where(amax > 0, amax / np.float32(448.0), np.float32(1.0)).astype(np.float32)
+    q = (w / s[..., None]).astype(np.float32)
+    return e4m3_encode(q), s
+
+
+def dequantize_fp8_rows(codes, scales):
+    """The weights the FP8 layer computes with: s * decode(code), fp64."""
+    return e4m3_decode(codes) * np.asarray(scales, dtype=np.float64)[..., None]
 
 
 # --------------------------------------------------------------- dispatch --
