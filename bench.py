@@ -135,6 +135,10 @@ def main():
     ap.add_argument("--cpu-sample", type=int, default=4096,
                     help="tokens whose expert outputs the oracle computes")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--weights", default="bf16", choices=["bf16", "fp8"],
+                    help="expert weights as stored: bf16, or FP8 E4M3 codes with per-row "
+                         "scales (quantised by moe_quantize_fp8 before timing; decode "
+                         "steps, T <= 64)")
     ap.add_argument("--router", default="softmax", choices=["softmax", "v3", "ec"],
                     help="softmax top-k router (moe_route) or the DeepSeek-V3 gate "
                          "(moe_route_v3: 8 groups, 4 kept, scale 2.5, seeded bias in "
@@ -186,6 +190,40 @@ def main():
                            v3["topk_groups"], v3["route_scale"], b.logits, b.topk_idx,
                            b.topk_w, b.ws, stream)
 
+    fp8 = None
+    if args.weights == "fp8":
+        if T > 64 or args.router == "ec":
+            print("--weights fp8 runs decode steps (T <= 64) with token-choice routers",
+                  file=sys.stderr)
+            sys.exit(2)
+        fp8 = {}
+        for kind in [kd for kd in ("w1", "w3", "w2", "ws1", "ws3", "ws2") if kd in dev]:
+            w = dev[kind]
+            c = torch.empty(w.shape, dtype=torch.uint8, device="cuda")
+            sc = torch.empty(w.shape[:-1], dtype=torch.float32, device="cuda")
+            M.moe_quantize_fp8(w.reshape(-1, w.shape[-1]), c, sc)
+            fp8[kind] = (c, sc)
+        torch.cuda.synchronize()
+        # the bf16 stacks are not read by the FP8 step: free them
+        for kind in list(fp8):
+            del dev[kind]
+        torch.cuda.empty_cache()
+
+    def ffn():
+        if fp8 is None:
+            M.moe_expert_ffn(T, k, b.x_perm, b.offsets, dev["x"], dev["w1"], dev["w3"],
+                             dev["w2"], dev.get("ws1"), dev.get("ws3"), dev.get("ws2"),
+                             b.y_perm, b.y_shared, b.ws, stream)
+            return
+        sh = {}
+        if Es:
+            sh = dict(sq1=fp8["ws1"][0], sq3=fp8["ws3"][0], sq2=fp8["ws2"][0],
+                      ss1=fp8["ws1"][1], ss3=fp8["ws3"][1], ss2=fp8["ws2"][1],
+                      y_shared=b.y_shared)
+        M.moe_expert_ffn_fp8(T, k, b.x_perm, b.offsets, dev["x"], fp8["w1"][0], fp8["w3"][0],
+                             fp8["w2"][0], fp8["w1"][1], fp8["w3"][1], fp8["w2"][1], b.y_perm,
+                             b.ws, stream=stream, **sh)
+
     ec = None
     if args.router == "ec":
         cap = M.moe_ec_capacity(T, E, 1.0)
@@ -231,9 +269,7 @@ def main():
                       b.row_of_pair, b.drop_mask, b.x_perm, b.ws, stream)
         if timed:
             ev[2].record(stream)
-        M.moe_expert_ffn(T, k, b.x_perm, b.offsets, dev["x"], dev["w1"], dev["w3"], dev["w2"],
-                         dev.get("ws1"), dev.get("ws3"), dev.get("ws2"), b.y_perm, b.y_shared,
-                         b.ws, stream)
+        ffn()
         if timed:
             ev[3].record(stream)
         M.moe_combine(b.y_perm, b.y_shared, b.row_of_pair, b.topk_w, b.y, stream)
@@ -271,6 +307,10 @@ def main():
         cap = ec["cap"]
         counts = np.full(E, cap)
     flop, bytes_alg, touched, rows = gemm_work(cfg, counts, cap)
+    if fp8 is not None:
+        # one byte per weight plus the fp32 row scales (2F + d per expert)
+        wb = touched * 3.0 * d * F * cfg.bytes_per_el
+        bytes_alg = bytes_alg - wb + touched * (3.0 * d * F + 4.0 * (2 * F + d))
     ffn_ms = float(per_call[names.index("expert_ffn")])
     if cfg.T <= 256:      # decode-shaped: weight streaming, HBM-bound
         achieved = bytes_alg / (ffn_ms / 1e3) / 1e9
@@ -289,8 +329,10 @@ def main():
     src_hash = h.hexdigest()[:16]
     # counters were taken with the softmax router (the routing decides the rows)
     roof["traffic"] = (MEASURED_TRAFFIC.get((cfg.name, src_hash))
-                       if args.router == "softmax" else None)
-    roof["kernel"] = "moe_expert_ffn (grouped GEMM phase 1 + phase 2 + tile table)"
+                       if args.router == "softmax" and fp8 is None else None)
+    roof["kernel"] = ("moe_expert_ffn (grouped GEMM phase 1 + phase 2 + tile table)"
+                      if fp8 is None else
+                      "moe_expert_ffn_fp8 (weight streaming of E4M3 codes, phase 1 + phase 2)")
     roof["kernel_ms"] = round(ffn_ms, 4)
 
     extra = {}
@@ -313,7 +355,9 @@ def main():
         v3["bias"].copy_(saved)
 
     cpu = None
-    if not args.no_cpu_baseline and v3 is None and ec is None:
+    if fp8 is not None:
+        extra["weights"] = "fp8_e4m3_row_scaled"
+    if not args.no_cpu_baseline and v3 is None and ec is None and fp8 is None:
         log("timing the CPU oracle on a token sample")
         v, threads, n, dt = cpu_baseline(cfg, x, wg, host, args.cpu_sample)
         cpu = {"value": round(v, 3), "unit": "tokens/s", "cores": int(threads),

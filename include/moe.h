@@ -235,6 +235,44 @@ int moe_expert_ffn(int64_t T, int64_t d_model, int32_t E, int32_t E_shared,
                    void* y_shared, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * FP8 expert weights (the pages name FP8 expert storage, "CMU 11-868
+ * Lecture 17" section 1.4, without an encoding; this library uses OCP FP8
+ * E4M3 codes with one fp32 scale per stored weight row):
+ *   s_r = max_i |w[r][i]| / 448   (fp32, correctly rounded; 1 for a zero row)
+ *   codes[r][i] = E4M3 round-to-nearest-even of fp32(w[r][i] / s_r),
+ *                 magnitudes clamped to 448
+ *   the weight used is s_r * E4M3(codes[r][i])
+ *   w      [rows, cols] dtype in (bf16 or fp32)
+ *   codes  [rows, cols] uint8 out;  scales [rows] fp32 out
+ * Quantise w1, w3 as [E*F, d] (scales [E, F]) and w2 as [E*d, F] (scales
+ * [E, d]).  Rows must start 16-byte aligned for moe_expert_ffn_fp8, i.e.
+ * cols a multiple of 16 (d and F are multiples of 64).
+ */
+int moe_quantize_fp8(int64_t rows, int64_t cols, int32_t dtype, const void* w,
+                     uint8_t* codes, float* scales, void* stream);
+
+/*
+ * moe_expert_ffn with FP8 expert weights, for decode steps (T <= 64, so
+ * every segment has at most 64 rows and is weight-streamed): each weight
+ * byte is read once, half the bytes of bf16 weights.  Activations, H and
+ * outputs are bf16, accumulation fp32:
+ *   H = SiLU(s1 * (X q1^T)) (*) (s3 * (X q3^T)),  Y = s2 * (H q2^T)
+ * with the row scales applied to the summed dot products.
+ *   w1, w3 [E, F, d] uint8; s1, s3 [E, F] fp32; w2 [E, d, F] uint8;
+ *   s2 [E, d] fp32; ws1, ws3, ws2 / ss1, ss3, ss2: the shared experts'
+ *   (NULL if E_shared == 0); the other arguments as for moe_expert_ffn.
+ * Returns MOE_EUNSUPPORTED for T > 64.
+ */
+int moe_expert_ffn_fp8(int64_t T, int64_t d_model, int32_t E, int32_t E_shared,
+                       int32_t k, int64_t d_ff, const void* x_perm,
+                       const int32_t* offsets, const void* x, const uint8_t* w1,
+                       const uint8_t* w3, const uint8_t* w2, const float* s1,
+                       const float* s3, const float* s2, const uint8_t* ws1,
+                       const uint8_t* ws3, const uint8_t* ws2, const float* ss1,
+                       const float* ss3, const float* ss2, void* y_perm,
+                       void* y_shared, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * Weighted combine back to token order, "CMU 11-868 Lecture 17" section 2.2
  * (add back with the weights) and "MoE routing math" section 2.2 (shared
  * experts with weight 1):

@@ -163,3 +163,20 @@ def test_expert_choice_capacity_and_arguments(M):
     assert L.moe_permute_ec(100, 128, 8, 10, M.MOE_BF16, fake, fake, fake, fake, nil, fake, fake,
                             nil) == -1                                       # row_of_te NULL
     assert L.moe_ec_capacity(10, 2, -1.0, ctypes.byref(ctypes.c_int64())) == -1
+
+
+def test_fp8_arguments_are_checked(M):
+    L = M.lib()
+    nil = ctypes.c_void_p(0)
+    fake = ctypes.c_void_p(4096)
+    assert L.moe_quantize_fp8(0, 64, M.MOE_BF16, fake, fake, fake, nil) == -1
+    assert L.moe_quantize_fp8(4, 64, 9, fake, fake, fake, nil) == -2
+    assert L.moe_quantize_fp8(4, 64, M.MOE_BF16, fake, nil, fake, nil) == -1
+
+    def ffn(T=64, Es=1, s1=fake, ws=1 << 30):
+        return L.moe_expert_ffn_fp8(T, 7168, 256, Es, 8, 2048, fake, fake, fake, fake, fake, fake,
+                                    s1, fake, fake, fake, fake, fake, fake, fake, fake, fake,
+                                    fake, fake, ws, nil)
+    assert ffn(T=65) == -2 and "T must be <= 64" in L.moe_last_error().decode()
+    assert ffn(s1=nil) == -1
+    assert ffn(ws=1024) == -4

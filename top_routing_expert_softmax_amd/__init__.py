@@ -21,7 +21,8 @@ MOE_BF16 = 1
 # Symbols declared in include/moe.h.
 EXPORTS = ("moe_strerror", "moe_last_error", "moe_capacity", "moe_workspace_size",
            "moe_route", "moe_route_v3", "moe_update_bias", "moe_ec_capacity", "moe_route_ec",
-           "moe_permute_ec", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_aux_stats")
+           "moe_permute_ec", "moe_quantize_fp8", "moe_expert_ffn_fp8", "moe_permute",
+           "moe_expert_ffn", "moe_combine", "moe_aux_stats")
 
 _lib = None
 
@@ -66,6 +67,11 @@ def lib():
     L.moe_route_ec.argtypes = [i64, i64, i32, i64, i32, vp, vp, vp, vp, vp, vp, sz, vp]
     L.moe_permute_ec.restype = ctypes.c_int
     L.moe_permute_ec.argtypes = [i64, i64, i32, i64, i32, vp, vp, vp, vp, vp, vp, vp, vp]
+    L.moe_quantize_fp8.restype = ctypes.c_int
+    L.moe_quantize_fp8.argtypes = [i64, i64, i32, vp, vp, vp, vp]
+    L.moe_expert_ffn_fp8.restype = ctypes.c_int
+    L.moe_expert_ffn_fp8.argtypes = [i64, i64, i32, i32, i32, i64, vp, vp, vp, vp, vp, vp, vp,
+                                     vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.moe_permute.restype = ctypes.c_int
     L.moe_permute.argtypes = [i64, i64, i32, i32, f64, i32, vp, vp, vp, vp, vp, vp, vp, vp,
                               vp, sz, vp]
@@ -174,6 +180,27 @@ def ec_ffn_k(T, E, cap):
     """The k to pass moe_expert_ffn / moe_workspace_size for expert choice:
     its row bound T * k must cover the E * cap rows."""
     return max(1, -(-(E * cap) // T))
+
+
+def moe_quantize_fp8(w, codes, scales, stream=None):
+    """Per-row FP8 E4M3 codes and fp32 scales of a [rows, cols] weight
+    tensor (any leading dims are flattened into rows)."""
+    cols = w.shape[-1]
+    rows = w.numel() // cols
+    _check("moe_quantize_fp8", lib().moe_quantize_fp8(rows, cols, _dtype_code(w), _ptr(w),
+                                                      _ptr(codes), _ptr(scales), _stream(stream)))
+
+
+def moe_expert_ffn_fp8(T, k, x_perm, offsets, x, q1, q3, q2, s1, s3, s2, y_perm, ws,
+                       sq1=None, sq3=None, sq2=None, ss1=None, ss3=None, ss2=None, y_shared=None,
+                       stream=None):
+    E, F, d = q1.shape
+    Es = 0 if sq1 is None else sq1.shape[0]
+    _check("moe_expert_ffn_fp8", lib().moe_expert_ffn_fp8(
+        T, d, E, Es, k, F, _ptr(x_perm), _ptr(offsets), _ptr(x), _ptr(q1), _ptr(q3), _ptr(q2),
+        _ptr(s1), _ptr(s3), _ptr(s2), _ptr(sq1), _ptr(sq3), _ptr(sq2), _ptr(ss1), _ptr(ss3),
+        _ptr(ss2), _ptr(y_perm), _ptr(y_shared), _ptr(ws), ws.numel() * ws.element_size(),
+        _stream(stream)))
 
 
 def moe_permute(topk_idx, x, E, CF, counts, offsets, token_of_row, row_of_pair, drop_mask,

@@ -21,6 +21,15 @@
 // step; accumulator element v of lane l is token 4 * (l / 16) + v, weight
 // row l % 16.  Token rows past the segment read its last row; their sums
 // are never stored.
+//
+// FP8 weights (OCP E4M3 codes with one fp32 scale per weight row; the
+// pages name FP8 expert storage, "CMU 11-868 Lecture 17" section 1.4, but
+// no encoding): a lane loads 16 codes (16 consecutive contracted indices of
+// a 64-wide step), converts them to bf16 in registers (exact: every E4M3
+// value is a bf16 value) and feeds two MFMAs, the A operand taking the
+// same 16 indices of the token rows.  The row scale multiplies the summed
+// dot product (s * sum_k x_k q_k = sum_k x_k (s q_k)).  Half the bytes of
+// the bf16 weights cross HBM.
 #include "moe_device.h"
 #include "moe_internal.h"
 
@@ -62,10 +71,86 @@ struct StreamArgs {
   void* H;
   void* y_perm;
   void* y_shared;
+  const float* sc1;       // FP8 row scales: [E, F] for W1 / W3, [E, d] for W2
+  const float* sc3;
+  const float* sc2;
+  const float* ssc1;      // shared experts' scales, same layouts
+  const float* ssc3;
+  const float* ssc2;
   int T, d, E, Es, k, F;
 };
 
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// Eight E4M3 codes (two words, lowest byte first) as eight bf16 values.
+__device__ __forceinline__ bf16x8_t e4m3x8_to_bf16(uint32_t w0, uint32_t w1) {
+  const bf16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(static_cast<int>(w0), 1.0f, false);
+  const bf16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(static_cast<int>(w0), 1.0f, true);
+  const bf16x2_t c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(static_cast<int>(w1), 1.0f, false);
+  const bf16x2_t d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(static_cast<int>(w1), 1.0f, true);
+  return bf16x8_t{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
 __device__ __forceinline__ float silu_s(float g) { return g / (1.0f + __expf(-g)); }
+
+// Sum the four quarters of a block in wave order, one token group at a
+// time (wave tg % 4 finishes group tg), scale (FP8) and store.
+template <int PHASE, int TG, bool FP8>
+__device__ __forceinline__ void stream_finish(const StreamArgs& a, f32x4_t (&acc)[TG][kSNB],
+                                              int seg, int rows, int arow0, int hrow0, int n0,
+                                              float* red) {
+  const bool routed = seg < a.E;
+  const int e = routed ? seg : seg - a.E;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  float scale[kSNB] = {1.0f, 1.0f};
+  if (FP8) {
+    if (PHASE == 1) {
+      const int64_t at = static_cast<int64_t>(e) * a.F + n0 + (lane & 15);
+      scale[0] = (routed ? a.sc1 : a.ssc1)[at];
+      scale[1] = (routed ? a.sc3 : a.ssc3)[at];
+    } else {
+#pragma unroll
+      for (int b = 0; b < kSNB; ++b)
+        scale[b] = (routed ? a.sc2 : a.ssc2)[static_cast<int64_t>(e) * a.d + n0 + b * 16 +
+                                              (lane & 15)];
+    }
+  }
+  f32x4_t* R = reinterpret_cast<f32x4_t*>(red);
+#pragma unroll
+  for (int tg = 0; tg < TG; ++tg) {
+#pragma unroll
+    for (int b = 0; b < kSNB; ++b) R[(wave * kSNB + b) * kWave + lane] = acc[tg][b];
+    __syncthreads();
+    if (wave == (tg & (kSWaves - 1))) {
+      f32x4_t v[kSNB];
+#pragma unroll
+      for (int b = 0; b < kSNB; ++b) {
+        v[b] = R[b * kWave + lane];
+#pragma unroll
+        for (int w = 1; w < kSWaves; ++w) v[b] += R[(w * kSNB + b) * kWave + lane];
+        v[b] *= scale[b];
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int m = tg * 16 + 4 * (lane >> 4) + q;
+        if (m >= rows) continue;
+        if (PHASE == 1) {
+          uint16_t* Hout = static_cast<uint16_t*>(a.H) + static_cast<int64_t>(hrow0 + m) * a.F;
+          Hout[n0 + (lane & 15)] = f32_to_bf16(silu_s(v[0][q]) * v[1][q]);
+        } else {
+          uint16_t* Y = routed
+              ? static_cast<uint16_t*>(a.y_perm) + static_cast<int64_t>(arow0 + m) * a.d
+              : static_cast<uint16_t*>(a.y_shared) +
+                    static_cast<int64_t>(hrow0 - a.T * a.k + m) * a.d;
+#pragma unroll
+          for (int b = 0; b < kSNB; ++b) Y[n0 + b * 16 + (lane & 15)] = f32_to_bf16(v[b][q]);
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
 
 // One block, TG groups of 16 tokens.  U = K steps loaded per batch.
 template <int PHASE, int TG>
@@ -167,46 +252,131 @@ __device__ __forceinline__ void stream_block(const StreamArgs& a, int seg, int r
         acc[tg][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[tg], fb[b], acc[tg][b], 0, 0, 0);
   }
 
-  // Sum the four quarters in wave order, one token group at a time; wave
-  // (tg % 4) finishes group tg.
-  f32x4_t* R = reinterpret_cast<f32x4_t*>(red);
+  stream_finish<PHASE, TG, false>(a, acc, seg, rows, arow0, hrow0, n0, red);
+}
+
+// FP8 weights: as stream_block, on 64-wide K steps of E4M3 codes.
+template <int PHASE, int TG>
+__device__ __forceinline__ void stream_block_fp8(const StreamArgs& a, int seg, int rows,
+                                                 int arow0, int hrow0, float* red) {
+  constexpr int U = TG == 1 ? 2 : 1;     // 64-wide K steps per batch
+  const bool routed = seg < a.E;
+  const int e = routed ? seg : seg - a.E;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int K = PHASE == 1 ? a.d : a.F;
+  const int64_t wstride = static_cast<int64_t>(a.F) * a.d;     // codes per expert matrix
+
+  const uint8_t* wrow[kSNB];
+  int n0;
+  if (PHASE == 1) {
+    n0 = blockIdx.x * 16;
+    const uint8_t* W1 = static_cast<const uint8_t*>(routed ? a.w1 : a.ws1) + e * wstride;
+    const uint8_t* W3 = static_cast<const uint8_t*>(routed ? a.w3 : a.ws3) + e * wstride;
+    wrow[0] = W1 + static_cast<int64_t>(n0 + (lane & 15)) * K;
+    wrow[1] = W3 + static_cast<int64_t>(n0 + (lane & 15)) * K;
+  } else {
+    n0 = blockIdx.x * 32;
+    const uint8_t* W2 = static_cast<const uint8_t*>(routed ? a.w2 : a.ws2) + e * wstride;
+    wrow[0] = W2 + static_cast<int64_t>(n0 + (lane & 15)) * K;
+    wrow[1] = W2 + static_cast<int64_t>(n0 + 16 + (lane & 15)) * K;
+  }
+  const uint16_t* arow[TG];
+  const uint16_t* Abase = PHASE == 1
+      ? static_cast<const uint16_t*>(routed ? a.x_perm : a.x) + static_cast<int64_t>(arow0) * K
+      : static_cast<const uint16_t*>(a.H) + static_cast<int64_t>(hrow0) * K;
 #pragma unroll
   for (int tg = 0; tg < TG; ++tg) {
+    const int m = min(tg * 16 + (lane & 15), rows - 1);
+    arow[tg] = Abase + static_cast<int64_t>(m) * K;
+  }
+  const int kq = 16 * (lane >> 4);       // the lane's 16 indices of a 64-wide step
+
+  f32x4_t acc[TG][kSNB];
 #pragma unroll
-    for (int b = 0; b < kSNB; ++b) R[(wave * kSNB + b) * kWave + lane] = acc[tg][b];
-    __syncthreads();
-    if (wave == (tg & (kSWaves - 1))) {
-      f32x4_t v[kSNB];
+  for (int tg = 0; tg < TG; ++tg)
 #pragma unroll
-      for (int b = 0; b < kSNB; ++b) {
-        v[b] = R[b * kWave + lane];
+    for (int b = 0; b < kSNB; ++b) acc[tg][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  const int nsteps = K / 64;
+  const int s0 = wave * nsteps / kSWaves;
+  const int s1 = (wave + 1) * nsteps / kSWaves;
+  int s = s0;
+#define MOE_FLOAD(FQ, FA, S0)                                                              \
+  _Pragma("unroll") for (int u = 0; u < U; ++u) {                                         \
+    const int kk = ((S0) + u) * 64 + kq;                                                  \
+    _Pragma("unroll") for (int b = 0; b < kSNB; ++b)                                      \
+      FQ[u][b] = *reinterpret_cast<const u32x4_t*>(wrow[b] + kk);                         \
+    _Pragma("unroll") for (int tg = 0; tg < TG; ++tg) {                                   \
+      FA[u][tg][0] = *reinterpret_cast<const bf16x8_t*>(arow[tg] + kk);                   \
+      FA[u][tg][1] = *reinterpret_cast<const bf16x8_t*>(arow[tg] + kk + 8);               \
+    }                                                                                      \
+  }
+#define MOE_FMFMA(FQ, FA)                                                                  \
+  _Pragma("unroll") for (int u = 0; u < U; ++u)                                           \
+    _Pragma("unroll") for (int b = 0; b < kSNB; ++b) {                                    \
+      const bf16x8_t lo = e4m3x8_to_bf16(FQ[u][b][0], FQ[u][b][1]);                       \
+      const bf16x8_t hi = e4m3x8_to_bf16(FQ[u][b][2], FQ[u][b][3]);                       \
+      _Pragma("unroll") for (int tg = 0; tg < TG; ++tg) {                                 \
+        acc[tg][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(FA[u][tg][0], lo, acc[tg][b], \
+                                                              0, 0, 0);                    \
+        acc[tg][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(FA[u][tg][1], hi, acc[tg][b], \
+                                                              0, 0, 0);                    \
+      }                                                                                    \
+    }
+  if (s + 2 * U <= s1) {
+    u32x4_t q0[U][kSNB], q1[U][kSNB];
+    bf16x8_t x0[U][TG][2], x1[U][TG][2];
+    MOE_FLOAD(q0, x0, s);
+    s += U;
+    for (; s + 2 * U <= s1; s += 2 * U) {
+      MOE_FLOAD(q1, x1, s);
+      MOE_FMFMA(q0, x0);
+      MOE_FLOAD(q0, x0, s + U);
+      MOE_FMFMA(q1, x1);
+    }
+    MOE_FMFMA(q0, x0);
+  }
+  for (; s + U <= s1; s += U) {
+    u32x4_t q[U][kSNB];
+    bf16x8_t xa[U][TG][2];
+    MOE_FLOAD(q, xa, s);
+    MOE_FMFMA(q, xa);
+  }
+  if constexpr (U > 1) {
+    for (; s < s1; ++s) {
+      u32x4_t q[1][kSNB];
+      bf16x8_t xa[1][TG][2];
+      {
+        const int kk = s * 64 + kq;
 #pragma unroll
-        for (int w = 1; w < kSWaves; ++w) v[b] += R[(w * kSNB + b) * kWave + lane];
+        for (int b = 0; b < kSNB; ++b) q[0][b] = *reinterpret_cast<const u32x4_t*>(wrow[b] + kk);
+#pragma unroll
+        for (int tg = 0; tg < TG; ++tg) {
+          xa[0][tg][0] = *reinterpret_cast<const bf16x8_t*>(arow[tg] + kk);
+          xa[0][tg][1] = *reinterpret_cast<const bf16x8_t*>(arow[tg] + kk + 8);
+        }
       }
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int m = tg * 16 + 4 * (lane >> 4) + q;
-        if (m >= rows) continue;
-        if (PHASE == 1) {
-          uint16_t* Hout = static_cast<uint16_t*>(a.H) + static_cast<int64_t>(hrow0 + m) * a.F;
-          Hout[n0 + (lane & 15)] = f32_to_bf16(silu_s(v[0][q]) * v[1][q]);
-        } else {
-          uint16_t* Y = routed
-              ? static_cast<uint16_t*>(a.y_perm) + static_cast<int64_t>(arow0 + m) * a.d
-              : static_cast<uint16_t*>(a.y_shared) +
-                    static_cast<int64_t>(hrow0 - a.T * a.k + m) * a.d;
+      for (int b = 0; b < kSNB; ++b) {
+        const bf16x8_t lo = e4m3x8_to_bf16(q[0][b][0], q[0][b][1]);
+        const bf16x8_t hi = e4m3x8_to_bf16(q[0][b][2], q[0][b][3]);
 #pragma unroll
-          for (int b = 0; b < kSNB; ++b) Y[n0 + b * 16 + (lane & 15)] = f32_to_bf16(v[b][q]);
+        for (int tg = 0; tg < TG; ++tg) {
+          acc[tg][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[0][tg][0], lo, acc[tg][b], 0, 0, 0);
+          acc[tg][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[0][tg][1], hi, acc[tg][b], 0, 0, 0);
         }
       }
     }
-    __syncthreads();
   }
+#undef MOE_FLOAD
+#undef MOE_FMFMA
+  stream_finish<PHASE, TG, true>(a, acc, seg, rows, arow0, hrow0, n0, red);
 }
 
 // Grid: x = weight-row group, y = segment (routed experts, then shared).
 // Segments with no rows, or more than kStreamMaxRows rows, exit at once.
-template <int PHASE>
+template <int PHASE, bool FP8>
 __global__ __launch_bounds__(kSWaves * kWave) void ffn_stream_kernel(StreamArgs a) {
   __shared__ f32x4_t red[kSWaves * kSNB * kWave];
   const int seg = blockIdx.y;
@@ -222,11 +392,20 @@ __global__ __launch_bounds__(kSWaves * kWave) void ffn_stream_kernel(StreamArgs 
   }
   if (rows <= 0 || rows > kStreamMaxRows) return;
   float* r = reinterpret_cast<float*>(red);
-  switch ((rows + 15) / 16) {
-    case 1: stream_block<PHASE, 1>(a, seg, rows, arow0, hrow0, r); break;
-    case 2: stream_block<PHASE, 2>(a, seg, rows, arow0, hrow0, r); break;
-    case 3: stream_block<PHASE, 3>(a, seg, rows, arow0, hrow0, r); break;
-    default: stream_block<PHASE, 4>(a, seg, rows, arow0, hrow0, r); break;
+  if constexpr (FP8) {
+    switch ((rows + 15) / 16) {
+      case 1: stream_block_fp8<PHASE, 1>(a, seg, rows, arow0, hrow0, r); break;
+      case 2: stream_block_fp8<PHASE, 2>(a, seg, rows, arow0, hrow0, r); break;
+      case 3: stream_block_fp8<PHASE, 3>(a, seg, rows, arow0, hrow0, r); break;
+      default: stream_block_fp8<PHASE, 4>(a, seg, rows, arow0, hrow0, r); break;
+    }
+  } else {
+    switch ((rows + 15) / 16) {
+      case 1: stream_block<PHASE, 1>(a, seg, rows, arow0, hrow0, r); break;
+      case 2: stream_block<PHASE, 2>(a, seg, rows, arow0, hrow0, r); break;
+      case 3: stream_block<PHASE, 3>(a, seg, rows, arow0, hrow0, r); break;
+      default: stream_block<PHASE, 4>(a, seg, rows, arow0, hrow0, r); break;
+    }
   }
 }
 
@@ -236,16 +415,23 @@ hipError_t launch_ffn_stream(int phase, int64_t T, int64_t d, int E, int E_share
                              int64_t F, const void* x_perm, const int32_t* offsets,
                              const void* x, const void* w1, const void* w3, const void* w2,
                              const void* ws1, const void* ws3, const void* ws2, void* H,
-                             void* y_perm, void* y_shared, hipStream_t s) {
+                             void* y_perm, void* y_shared, hipStream_t s, const float* sc1,
+                             const float* sc3, const float* sc2, const float* ssc1,
+                             const float* ssc3, const float* ssc2) {
   StreamArgs a{x_perm, x, offsets, w1, w3, w2, ws1, ws3, ws2, H, y_perm, y_shared,
+               sc1, sc3, sc2, ssc1, ssc3, ssc2,
                static_cast<int>(T), static_cast<int>(d), E, E_shared, k, static_cast<int>(F)};
+  const bool fp8 = sc1 != nullptr;
   const unsigned nseg = static_cast<unsigned>(E + E_shared);
+  const dim3 block(kSWaves * kWave);
   if (phase == 1) {
-    hipLaunchKernelGGL(ffn_stream_kernel<1>, dim3(static_cast<unsigned>(F / 16), nseg),
-                       dim3(kSWaves * kWave), 0, s, a);
+    const dim3 grid(static_cast<unsigned>(F / 16), nseg);
+    if (fp8) hipLaunchKernelGGL((ffn_stream_kernel<1, true>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((ffn_stream_kernel<1, false>), grid, block, 0, s, a);
   } else {
-    hipLaunchKernelGGL(ffn_stream_kernel<2>, dim3(static_cast<unsigned>(d / 32), nseg),
-                       dim3(kSWaves * kWave), 0, s, a);
+    const dim3 grid(static_cast<unsigned>(d / 32), nseg);
+    if (fp8) hipLaunchKernelGGL((ffn_stream_kernel<2, true>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((ffn_stream_kernel<2, false>), grid, block, 0, s, a);
   }
   return hipGetLastError();
 }

@@ -294,6 +294,69 @@ int moe_permute_ec(int64_t T, int64_t d_model, int32_t E, int64_t cap, int32_t d
                   "moe_permute_ec");
 }
 
+int moe_quantize_fp8(int64_t rows, int64_t cols, int32_t dtype, const void* w, uint8_t* codes,
+                     float* scales, void* stream) {
+  REQUIRE(rows >= 1 && rows < (int64_t(1) << 31), "rows must be in [1, 2^31)");
+  REQUIRE(cols >= 1 && cols < (int64_t(1) << 31), "cols must be in [1, 2^31)");
+  if (int r = check_dtype(dtype)) return r;
+  REQUIRE_PTR(w);
+  REQUIRE_PTR(codes);
+  REQUIRE_PTR(scales);
+  (void)hipGetLastError();
+  return launched(moe::launch_quantize_fp8(rows, cols, dtype == MOE_BF16, w, codes, scales,
+                                           static_cast<hipStream_t>(stream)),
+                  "moe_quantize_fp8");
+}
+
+int moe_expert_ffn_fp8(int64_t T, int64_t d_model, int32_t E, int32_t E_shared, int32_t k,
+                       int64_t d_ff, const void* x_perm, const int32_t* offsets, const void* x,
+                       const uint8_t* w1, const uint8_t* w3, const uint8_t* w2, const float* s1,
+                       const float* s3, const float* s2, const uint8_t* ws1, const uint8_t* ws3,
+                       const uint8_t* ws2, const float* ss1, const float* ss3, const float* ss2,
+                       void* y_perm, void* y_shared, void* ws, size_t ws_bytes, void* stream) {
+  if (int r = check_common(T, E, k)) return r;
+  if (int r = check_dim("d_model", d_model)) return r;
+  if (int r = check_dim("d_ff", d_ff)) return r;
+  REQUIRE(E_shared >= 0 && E_shared <= 16, "E_shared must be in [0, 16]");
+  if (T > moe::kStreamMaxRows)
+    return fail(MOE_EUNSUPPORTED, "moe_expert_ffn_fp8 runs decode steps: T must be <= %d "
+                "(got %lld)", moe::kStreamMaxRows, static_cast<long long>(T));
+  REQUIRE_PTR(x_perm);
+  REQUIRE_PTR(offsets);
+  REQUIRE_PTR(w1);
+  REQUIRE_PTR(w3);
+  REQUIRE_PTR(w2);
+  REQUIRE_PTR(s1);
+  REQUIRE_PTR(s3);
+  REQUIRE_PTR(s2);
+  REQUIRE_PTR(y_perm);
+  REQUIRE_PTR(ws);
+  if (E_shared > 0) {
+    REQUIRE_PTR(x);
+    REQUIRE_PTR(ws1);
+    REQUIRE_PTR(ws3);
+    REQUIRE_PTR(ws2);
+    REQUIRE_PTR(ss1);
+    REQUIRE_PTR(ss3);
+    REQUIRE_PTR(ss2);
+    REQUIRE_PTR(y_shared);
+  }
+  const size_t need = static_cast<size_t>(T * k + static_cast<int64_t>(E_shared) * T) * d_ff * 2;
+  if (ws_bytes < need)
+    return fail(MOE_EWORKSPACE, "moe_expert_ffn_fp8 needs %zu workspace bytes, got %zu", need,
+                ws_bytes);
+  (void)hipGetLastError();
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t err = moe::launch_ffn_stream(1, T, d_model, E, E_shared, k, d_ff, x_perm, offsets,
+                                          x, w1, w3, w2, ws1, ws3, ws2, ws, y_perm, y_shared, st,
+                                          s1, s3, s2, ss1, ss3, ss2);
+  if (err == hipSuccess)
+    err = moe::launch_ffn_stream(2, T, d_model, E, E_shared, k, d_ff, x_perm, offsets, x, w1, w3,
+                                 w2, ws1, ws3, ws2, ws, y_perm, y_shared, st, s1, s3, s2, ss1,
+                                 ss3, ss2);
+  return launched(err, "moe_expert_ffn_fp8");
+}
+
 int moe_permute(int64_t T, int64_t d_model, int32_t E, int32_t k, double CF, int32_t dtype,
                 const int32_t* topk_idx, const void* x, int32_t* counts, int32_t* offsets,
                 int32_t* token_of_row, int32_t* row_of_pair, uint8_t* drop_mask, void* x_perm,

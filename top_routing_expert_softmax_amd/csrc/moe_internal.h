@@ -81,11 +81,19 @@ hipError_t launch_expert_ffn(int64_t T, int64_t d, int E, int E_shared, int k,
 
 // One phase (1: H = SiLU(X W1^T) * (X W3^T), 2: Y = H W2^T) of the
 // weight-streaming FFN over the segments with 1 .. kStreamMaxRows rows.
+// With row scales (sc1 non-null) the weights are FP8 E4M3 codes.
 hipError_t launch_ffn_stream(int phase, int64_t T, int64_t d, int E, int E_shared, int k,
                              int64_t F, const void* x_perm, const int32_t* offsets,
                              const void* x, const void* w1, const void* w3, const void* w2,
                              const void* ws1, const void* ws3, const void* ws2, void* H,
-                             void* y_perm, void* y_shared, hipStream_t s);
+                             void* y_perm, void* y_shared, hipStream_t s,
+                             const float* sc1 = nullptr, const float* sc3 = nullptr,
+                             const float* sc2 = nullptr, const float* ssc1 = nullptr,
+                             const float* ssc3 = nullptr, const float* ssc2 = nullptr);
+
+// Per-row FP8 E4M3 quantisation (quant.hip).
+hipError_t launch_quantize_fp8(int64_t rows, int64_t cols, bool bf16, const void* w,
+                               uint8_t* codes, float* scales, hipStream_t s);
 
 hipError_t launch_combine(int64_t T, int64_t d, int E_shared, int k, bool bf16,
                           const void* y_perm, const void* y_shared,
