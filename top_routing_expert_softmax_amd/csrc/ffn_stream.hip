@@ -37,7 +37,14 @@ namespace moe {
 namespace {
 
 constexpr int kSWaves = 4;               // waves per block (K quarters)
-constexpr int kSNB = 2;                  // 16-row weight fragments per K step
+constexpr int kSNB = 2;                  // 16-row weight fragments per K step (bf16)
+#ifndef MOE_STREAM_NB8
+#define MOE_STREAM_NB8 4
+#endif
+#ifndef MOE_STREAM_U8
+#define MOE_STREAM_U8 2
+#endif
+constexpr int kSNB8 = MOE_STREAM_NB8;    // fragments per K step (FP8): half gate, half up
 
 #ifndef MOE_STREAM_NT
 #define MOE_STREAM_NT 0
@@ -95,40 +102,43 @@ __device__ __forceinline__ float silu_s(float g) { return g / (1.0f + __expf(-g)
 
 // Sum the four quarters of a block in wave order, one token group at a
 // time (wave tg % 4 finishes group tg), scale (FP8) and store.
-template <int PHASE, int TG, bool FP8>
-__device__ __forceinline__ void stream_finish(const StreamArgs& a, f32x4_t (&acc)[TG][kSNB],
+template <int PHASE, int TG, bool FP8, int NB>
+__device__ __forceinline__ void stream_finish(const StreamArgs& a, f32x4_t (&acc)[TG][NB],
                                               int seg, int rows, int arow0, int hrow0, int n0,
                                               float* red) {
+  // Phase 1: fragments b < NB/2 hold gate (W1) rows n0 + 16 b, the others
+  // the same rows of W3.  Phase 2: fragment b holds W2 rows n0 + 16 b.
   const bool routed = seg < a.E;
   const int e = routed ? seg : seg - a.E;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
-  float scale[kSNB] = {1.0f, 1.0f};
-  if (FP8) {
-    if (PHASE == 1) {
-      const int64_t at = static_cast<int64_t>(e) * a.F + n0 + (lane & 15);
-      scale[0] = (routed ? a.sc1 : a.ssc1)[at];
-      scale[1] = (routed ? a.sc3 : a.ssc3)[at];
-    } else {
+  float scale[NB];
 #pragma unroll
-      for (int b = 0; b < kSNB; ++b)
+  for (int b = 0; b < NB; ++b) {
+    scale[b] = 1.0f;
+    if (FP8) {
+      if (PHASE == 1) {
+        const int64_t at = static_cast<int64_t>(e) * a.F + n0 + 16 * (b % (NB / 2)) + (lane & 15);
+        scale[b] = b < NB / 2 ? (routed ? a.sc1 : a.ssc1)[at] : (routed ? a.sc3 : a.ssc3)[at];
+      } else {
         scale[b] = (routed ? a.sc2 : a.ssc2)[static_cast<int64_t>(e) * a.d + n0 + b * 16 +
-                                              (lane & 15)];
+                                             (lane & 15)];
+      }
     }
   }
   f32x4_t* R = reinterpret_cast<f32x4_t*>(red);
 #pragma unroll
   for (int tg = 0; tg < TG; ++tg) {
 #pragma unroll
-    for (int b = 0; b < kSNB; ++b) R[(wave * kSNB + b) * kWave + lane] = acc[tg][b];
+    for (int b = 0; b < NB; ++b) R[(wave * NB + b) * kWave + lane] = acc[tg][b];
     __syncthreads();
     if (wave == (tg & (kSWaves - 1))) {
-      f32x4_t v[kSNB];
+      f32x4_t v[NB];
 #pragma unroll
-      for (int b = 0; b < kSNB; ++b) {
+      for (int b = 0; b < NB; ++b) {
         v[b] = R[b * kWave + lane];
 #pragma unroll
-        for (int w = 1; w < kSWaves; ++w) v[b] += R[(w * kSNB + b) * kWave + lane];
+        for (int w = 1; w < kSWaves; ++w) v[b] += R[(w * NB + b) * kWave + lane];
         v[b] *= scale[b];
       }
 #pragma unroll
@@ -137,14 +147,16 @@ __device__ __forceinline__ void stream_finish(const StreamArgs& a, f32x4_t (&acc
         if (m >= rows) continue;
         if (PHASE == 1) {
           uint16_t* Hout = static_cast<uint16_t*>(a.H) + static_cast<int64_t>(hrow0 + m) * a.F;
-          Hout[n0 + (lane & 15)] = f32_to_bf16(silu_s(v[0][q]) * v[1][q]);
+#pragma unroll
+          for (int b = 0; b < NB / 2; ++b)
+            Hout[n0 + 16 * b + (lane & 15)] = f32_to_bf16(silu_s(v[b][q]) * v[b + NB / 2][q]);
         } else {
           uint16_t* Y = routed
               ? static_cast<uint16_t*>(a.y_perm) + static_cast<int64_t>(arow0 + m) * a.d
               : static_cast<uint16_t*>(a.y_shared) +
                     static_cast<int64_t>(hrow0 - a.T * a.k + m) * a.d;
 #pragma unroll
-          for (int b = 0; b < kSNB; ++b) Y[n0 + b * 16 + (lane & 15)] = f32_to_bf16(v[b][q]);
+          for (int b = 0; b < NB; ++b) Y[n0 + b * 16 + (lane & 15)] = f32_to_bf16(v[b][q]);
         }
       }
     }
@@ -252,14 +264,15 @@ __device__ __forceinline__ void stream_block(const StreamArgs& a, int seg, int r
         acc[tg][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[tg], fb[b], acc[tg][b], 0, 0, 0);
   }
 
-  stream_finish<PHASE, TG, false>(a, acc, seg, rows, arow0, hrow0, n0, red);
+  stream_finish<PHASE, TG, false, kSNB>(a, acc, seg, rows, arow0, hrow0, n0, red);
 }
 
 // FP8 weights: as stream_block, on 64-wide K steps of E4M3 codes.
 template <int PHASE, int TG>
 __device__ __forceinline__ void stream_block_fp8(const StreamArgs& a, int seg, int rows,
                                                  int arow0, int hrow0, float* red) {
-  constexpr int U = TG == 1 ? 2 : 1;     // 64-wide K steps per batch
+  constexpr int NB = kSNB8;
+  constexpr int U = TG == 1 ? MOE_STREAM_U8 : 1;     // 64-wide K steps per batch
   const bool routed = seg < a.E;
   const int e = routed ? seg : seg - a.E;
   const int lane = threadIdx.x & (kWave - 1);
@@ -267,19 +280,21 @@ __device__ __forceinline__ void stream_block_fp8(const StreamArgs& a, int seg, i
   const int K = PHASE == 1 ? a.d : a.F;
   const int64_t wstride = static_cast<int64_t>(a.F) * a.d;     // codes per expert matrix
 
-  const uint8_t* wrow[kSNB];
+  const uint8_t* wrow[NB];
   int n0;
   if (PHASE == 1) {
-    n0 = blockIdx.x * 16;
+    n0 = blockIdx.x * 8 * NB;                    // NB/2 gate and NB/2 up fragments
     const uint8_t* W1 = static_cast<const uint8_t*>(routed ? a.w1 : a.ws1) + e * wstride;
     const uint8_t* W3 = static_cast<const uint8_t*>(routed ? a.w3 : a.ws3) + e * wstride;
-    wrow[0] = W1 + static_cast<int64_t>(n0 + (lane & 15)) * K;
-    wrow[1] = W3 + static_cast<int64_t>(n0 + (lane & 15)) * K;
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+      wrow[b] = (b < NB / 2 ? W1 : W3) +
+                static_cast<int64_t>(n0 + 16 * (b % (NB / 2)) + (lane & 15)) * K;
   } else {
-    n0 = blockIdx.x * 32;
+    n0 = blockIdx.x * 16 * NB;
     const uint8_t* W2 = static_cast<const uint8_t*>(routed ? a.w2 : a.ws2) + e * wstride;
-    wrow[0] = W2 + static_cast<int64_t>(n0 + (lane & 15)) * K;
-    wrow[1] = W2 + static_cast<int64_t>(n0 + 16 + (lane & 15)) * K;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) wrow[b] = W2 + static_cast<int64_t>(n0 + 16 * b + (lane & 15)) * K;
   }
   const uint16_t* arow[TG];
   const uint16_t* Abase = PHASE == 1
@@ -292,11 +307,11 @@ __device__ __forceinline__ void stream_block_fp8(const StreamArgs& a, int seg, i
   }
   const int kq = 16 * (lane >> 4);       // the lane's 16 indices of a 64-wide step
 
-  f32x4_t acc[TG][kSNB];
+  f32x4_t acc[TG][NB];
 #pragma unroll
   for (int tg = 0; tg < TG; ++tg)
 #pragma unroll
-    for (int b = 0; b < kSNB; ++b) acc[tg][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int b = 0; b < NB; ++b) acc[tg][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   const int nsteps = K / 64;
   const int s0 = wave * nsteps / kSWaves;
@@ -305,7 +320,7 @@ __device__ __forceinline__ void stream_block_fp8(const StreamArgs& a, int seg, i
 #define MOE_FLOAD(FQ, FA, S0)                                                              \
   _Pragma("unroll") for (int u = 0; u < U; ++u) {                                         \
     const int kk = ((S0) + u) * 64 + kq;                                                  \
-    _Pragma("unroll") for (int b = 0; b < kSNB; ++b)                                      \
+    _Pragma("unroll") for (int b = 0; b < NB; ++b)                                      \
       FQ[u][b] = *reinterpret_cast<const u32x4_t*>(wrow[b] + kk);                         \
     _Pragma("unroll") for (int tg = 0; tg < TG; ++tg) {                                   \
       FA[u][tg][0] = *reinterpret_cast<const bf16x8_t*>(arow[tg] + kk);                   \
@@ -314,7 +329,7 @@ __device__ __forceinline__ void stream_block_fp8(const StreamArgs& a, int seg, i
   }
 #define MOE_FMFMA(FQ, FA)                                                                  \
   _Pragma("unroll") for (int u = 0; u < U; ++u)                                           \
-    _Pragma("unroll") for (int b = 0; b < kSNB; ++b) {                                    \
+    _Pragma("unroll") for (int b = 0; b < NB; ++b) {                                    \
       const bf16x8_t lo = e4m3x8_to_bf16(FQ[u][b][0], FQ[u][b][1]);                       \
       const bf16x8_t hi = e4m3x8_to_bf16(FQ[u][b][2], FQ[u][b][3]);                       \
       _Pragma("unroll") for (int tg = 0; tg < TG; ++tg) {                                 \
@@ -325,7 +340,7 @@ __device__ __forceinline__ void stream_block_fp8(const StreamArgs& a, int seg, i
       }                                                                                    \
     }
   if (s + 2 * U <= s1) {
-    u32x4_t q0[U][kSNB], q1[U][kSNB];
+    u32x4_t q0[U][NB], q1[U][NB];
     bf16x8_t x0[U][TG][2], x1[U][TG][2];
     MOE_FLOAD(q0, x0, s);
     s += U;
@@ -338,19 +353,19 @@ __device__ __forceinline__ void stream_block_fp8(const StreamArgs& a, int seg, i
     MOE_FMFMA(q0, x0);
   }
   for (; s + U <= s1; s += U) {
-    u32x4_t q[U][kSNB];
+    u32x4_t q[U][NB];
     bf16x8_t xa[U][TG][2];
     MOE_FLOAD(q, xa, s);
     MOE_FMFMA(q, xa);
   }
   if constexpr (U > 1) {
     for (; s < s1; ++s) {
-      u32x4_t q[1][kSNB];
+      u32x4_t q[1][NB];
       bf16x8_t xa[1][TG][2];
       {
         const int kk = s * 64 + kq;
 #pragma unroll
-        for (int b = 0; b < kSNB; ++b) q[0][b] = *reinterpret_cast<const u32x4_t*>(wrow[b] + kk);
+        for (int b = 0; b < NB; ++b) q[0][b] = *reinterpret_cast<const u32x4_t*>(wrow[b] + kk);
 #pragma unroll
         for (int tg = 0; tg < TG; ++tg) {
           xa[0][tg][0] = *reinterpret_cast<const bf16x8_t*>(arow[tg] + kk);
@@ -358,7 +373,7 @@ __device__ __forceinline__ void stream_block_fp8(const StreamArgs& a, int seg, i
         }
       }
 #pragma unroll
-      for (int b = 0; b < kSNB; ++b) {
+      for (int b = 0; b < NB; ++b) {
         const bf16x8_t lo = e4m3x8_to_bf16(q[0][b][0], q[0][b][1]);
         const bf16x8_t hi = e4m3x8_to_bf16(q[0][b][2], q[0][b][3]);
 #pragma unroll
@@ -371,14 +386,14 @@ __device__ __forceinline__ void stream_block_fp8(const StreamArgs& a, int seg, i
   }
 #undef MOE_FLOAD
 #undef MOE_FMFMA
-  stream_finish<PHASE, TG, true>(a, acc, seg, rows, arow0, hrow0, n0, red);
+  stream_finish<PHASE, TG, true, NB>(a, acc, seg, rows, arow0, hrow0, n0, red);
 }
 
 // Grid: x = weight-row group, y = segment (routed experts, then shared).
 // Segments with no rows, or more than kStreamMaxRows rows, exit at once.
 template <int PHASE, bool FP8>
 __global__ __launch_bounds__(kSWaves * kWave) void ffn_stream_kernel(StreamArgs a) {
-  __shared__ f32x4_t red[kSWaves * kSNB * kWave];
+  __shared__ f32x4_t red[kSWaves * (kSNB8 > kSNB ? kSNB8 : kSNB) * kWave];
   const int seg = blockIdx.y;
   int rows, arow0, hrow0;
   if (seg < a.E) {
@@ -424,12 +439,15 @@ hipError_t launch_ffn_stream(int phase, int64_t T, int64_t d, int E, int E_share
   const bool fp8 = sc1 != nullptr;
   const unsigned nseg = static_cast<unsigned>(E + E_shared);
   const dim3 block(kSWaves * kWave);
+  // H columns per block: 8 * fragments (half gate, half up); output
+  // columns per block: 16 * fragments
+  const int nb = fp8 ? kSNB8 : kSNB;
   if (phase == 1) {
-    const dim3 grid(static_cast<unsigned>(F / 16), nseg);
+    const dim3 grid(static_cast<unsigned>(F / (8 * nb)), nseg);
     if (fp8) hipLaunchKernelGGL((ffn_stream_kernel<1, true>), grid, block, 0, s, a);
     else hipLaunchKernelGGL((ffn_stream_kernel<1, false>), grid, block, 0, s, a);
   } else {
-    const dim3 grid(static_cast<unsigned>(d / 32), nseg);
+    const dim3 grid(static_cast<unsigned>(d / (16 * nb)), nseg);
     if (fp8) hipLaunchKernelGGL((ffn_stream_kernel<2, true>), grid, block, 0, s, a);
     else hipLaunchKernelGGL((ffn_stream_kernel<2, false>), grid, block, 0, s, a);
   }
