@@ -41,6 +41,10 @@ Readings where the pages are silent or disagree (each is listed in the design doc):
     one fp32 scale per stored weight row s = max|w_row| / 448 (fp32
     division), codes = round-to-nearest-even of the fp32 quotient w / s,
     clamped to +-448; the weight the layer uses is s * decode(code).
+  * backward: the loss is L = sum(dy * y) + alpha * L_balance + beta * z;
+    the balance loss reaches the router through P_i only (f_i are counts);
+    a dropped pair contributes nothing, but its weight stays in the
+    softmax over the token's selected logits that p~ is.
 """
 from fractions import Fraction
 import math
@@ -55,6 +59,7 @@ __all__ = [
     "affinity_f32", "v3_gate", "update_bias",
     "ec_capacity", "expert_choice", "ec_dispatch", "ec_combine",
     "e4m3_decode", "e4m3_encode", "quantize_fp8_rows", "dequantize_fp8_rows",
+    "silu_grad", "swiglu_expert_backward", "layer_backward",
 ]
 
 
@@ -480,3 +485,86 @@ def layer_forward(x, w_gate, k, CF, load_expert, E, E_shared=0,
     out.update(counts=counts, cap=cap, y=y, tokens=tok, **disp)
     out.update(stats)
     return out
+
+
+# ------------------------------------------------------------ backward (N2) --
+
+def silu_grad(z):
+    """d/dz SiLU(z) = sigma(z) (1 + z (1 - sigma(z)))."""
+    z = _f64(z)
+    sg = 1.0 / (1.0 + np.exp(-z))
+    return sg * (1.0 + z * (1.0 - sg))
+
+
+def swiglu_expert_backward(xr, w1, w3, w2, dout):
+    """Chain rule through Expert(x) = (SiLU(x W1) (*) x W3) W2 for rows xr
+    and output gradient dout (storage layouts w1, w3 [F, d], w2 [d, F]).
+    Returns dx, dw1, dw3, dw2 (same layouts)."""
+    xr, w1, w3, w2, dout = (_f64(a) for a in (xr, w1, w3, w2, dout))
+    a = xr @ w1.T
+    b = xr @ w3.T
+    s = silu(a)
+    h = s * b
+    dh = dout @ w2                     # [n, F]
+    dw2 = dout.T @ h                   # [d, F]
+    da = dh * b * silu_grad(a)
+    db = dh * s
+    dw1 = da.T @ xr                    # [F, d]
+    dw3 = db.T @ xr
+    dx = da @ w1 + db @ w3
+    return dx, dw1, dw3, dw2
+
+
+def layer_backward(x, w_gate, k, CF, load_expert, E, dy, alpha=0.0, beta=0.0,
+                   E_shared=0, load_shared=None):
+    """Gradients of L = sum(dy * y) + alpha * L_balance + beta * z_loss of
+    one layer with respect to x, W_gate and every expert's weights.
+
+    Routes (the pages'): y_t = sum_s Shared_s(x_t) + sum_{kept j} p~_tj
+    o_tj; p~_t = softmax of the token's selected logits ([RM] 2.1), so
+    dg_tS = p~ (dp~ - <p~, dp~>) over the selected set; a dropped pair has
+    dp~ = 0 and no expert gradient ([L17] 2.4); L_balance = E sum f_i P_i
+    with f_i constant and dL/dp_ti = alpha E f_i / T through softmax(g_t)
+    ([RM] 3.4, [L17] 3.2); z = mean_t lse_t^2 gives dg_t = 2 beta lse_t
+    p_t / T ([SA] router_z_loss); finally dW_gate = x^T dg and dx += dg
+    W_gate^T."""
+    x = _f64(x)
+    dy = _f64(dy)
+    wg = _f64(w_gate)
+    T, d = x.shape
+    r = route(x, wg, k)
+    counts = expert_counts(r["idx"], E)
+    cap = capacity(T, E, k, CF)
+    disp = dispatch(r["idx"], E, cap)
+    kept = disp["drop"] == 0
+    pt = r["weights"]
+    dx = np.zeros_like(x)
+    dpt = np.zeros_like(pt)
+    dws = []
+    for e in range(E):
+        tt, jj = np.nonzero((r["idx"] == e) & kept)
+        w1, w3, w2 = (_f64(a) for a in load_expert(e))
+        if len(tt) == 0:
+            dws.append((np.zeros_like(w1), np.zeros_like(w3), np.zeros_like(w2)))
+            continue
+        out = swiglu_expert(x[tt], w1, w3, w2)
+        dpt[tt, jj] = np.sum(dy[tt] * out, axis=1)
+        dxe, dw1, dw3, dw2 = swiglu_expert_backward(x[tt], w1, w3, w2,
+                                                    pt[tt, jj][:, None] * dy[tt])
+        dx[tt] += dxe                  # a token picks an expert at most once
+        dws.append((dw1, dw3, dw2))
+    dshared = []
+    for s_ in range(E_shared):
+        dxs, dw1, dw3, dw2 = swiglu_expert_backward(x, *load_shared(s_), dy)
+        dx += dxs
+        dshared.append((dw1, dw3, dw2))
+    p = r["probs"]
+    dg = np.zeros((T, E))
+    inner = np.sum(pt * dpt, axis=1, keepdims=True)
+    np.add.at(dg, (np.arange(T)[:, None], r["idx"]), pt * (dpt - inner))
+    c = alpha * E * (counts / float(T)) / float(T)
+    dg += p * (c[None, :] - (p * c[None, :]).sum(axis=1, keepdims=True))
+    dg += beta * 2.0 * r["lse"][:, None] * p / float(T)
+    dx += dg @ wg.T
+    return {"dx": dx, "dw_gate": x.T @ dg, "dw": dws, "dw_shared": dshared,
+            "dtopk_w": dpt, "dg": dg, "route": r, "disp": disp, "counts": counts}
