@@ -308,6 +308,76 @@ int moe_aux_stats(int64_t T, int32_t E, int32_t k, double CF,
                   float* P, double* scalars, void* ws, size_t ws_bytes,
                   void* stream);
 
+/*
+ * Backward pass of the layer (bf16).  With an output
+ * gradient dy and the loss L = sum(dy * y) + alpha * L_balance + beta * z
+ * (the statistics of moe_aux_stats):
+ *   combine ("CMU 11-868 Lecture 17" 2.2; "MoE routing math" 2.2):
+ *     dO_tj = p~_tj dy_t on the row of each kept pair; dp~_tj = <dy_t, o_tj>
+ *     (0 for a dropped pair); every shared expert's output gradient is dy;
+ *   experts (the SwiGLU chain rule, "CMU 11-868 Lecture 17" 5.2):
+ *     dH = dO W2, dA = dH (*) B (*) SiLU'(A), dB = dH (*) SiLU(A),
+ *     dX = dA W1 + dB W3, dW1 = dA^T X, dW3 = dB^T X, dW2 = dO^T H;
+ *   router ("MoE routing math" 2.1, 3.4; "Mixture of Experts architecture"
+ *   router_z_loss): p~_t is the softmax of the selected logits, the
+ *   balance loss reaches g only through P_i (f_i are counts), and
+ *     dg = p~ (dp~ - <p~, dp~>) + p (*) (c - <p, c>) + 2 beta lse p / T,
+ *     c_i = alpha E f_i / T;   dW_gate = x^T dg;
+ *     dx_t = sum_s dX_shared[s][t] + sum_j dX_perm[row(t, j)] + dg_t W_gate^T.
+ * The calls take the forward's saved tensors (x, logits, topk_idx, topk_w,
+ * counts, offsets, row_of_pair, x_perm, y_perm) and one workspace of
+ * moe_backward_workspace_size() bytes; weight gradients are fp32.
+ */
+int moe_backward_workspace_size(int64_t T, int64_t d_model, int32_t E,
+                                int32_t E_shared, int32_t k, int64_t d_ff,
+                                int32_t dtype, size_t* bytes);
+
+/*
+ *   dy [T, d] bf16 in; y_perm [T*k, d] bf16 in (moe_expert_ffn's output);
+ *   row_of_pair, topk_w [T, k] in;
+ *   dy_perm [T*k + E_shared*T, d] bf16 out: rows of kept pairs = p~ dy_t,
+ *     rows T*k + s*T + t = dy_t (shared experts); other rows unwritten;
+ *   dtopk_w [T, k] fp32 out.
+ */
+int moe_combine_backward(int64_t T, int64_t d_model, int32_t E_shared, int32_t k,
+                         int32_t dtype, const void* dy, const void* y_perm,
+                         const int32_t* row_of_pair, const float* topk_w,
+                         void* dy_perm, float* dtopk_w, void* stream);
+
+/*
+ *   x_perm, offsets, x, w1, w3, w2, ws1, ws3, ws2: as for moe_expert_ffn;
+ *   dy_perm from moe_combine_backward;
+ *   dx_perm [T*k, d] bf16 out (rows of kept pairs); dx_shared [E_shared, T, d]
+ *   bf16 out (NULL if E_shared == 0);
+ *   dw1, dw3 [E, F, d], dw2 [E, d, F] fp32 out (zero for an expert with no
+ *   rows); dws1, dws3, dws2 the shared experts' (NULL if E_shared == 0).
+ */
+int moe_expert_ffn_backward(int64_t T, int64_t d_model, int32_t E, int32_t E_shared,
+                            int32_t k, int64_t d_ff, int32_t dtype,
+                            const void* x_perm, const int32_t* offsets,
+                            const void* x, const void* w1, const void* w3,
+                            const void* w2, const void* ws1, const void* ws3,
+                            const void* ws2, const void* dy_perm, void* dx_perm,
+                            void* dx_shared, float* dw1, float* dw3, float* dw2,
+                            float* dws1, float* dws3, float* dws2, void* ws,
+                            size_t ws_bytes, void* stream);
+
+/*
+ *   x [T, d], w_gate [d, E] bf16 in; logits [T, E], topk_w, dtopk_w [T, k]
+ *   fp32 in; topk_idx, row_of_pair [T, k], counts [E] int32 in;
+ *   dx_perm, dx_shared from moe_expert_ffn_backward; alpha, beta: the loss
+ *   weights of L_balance and z;
+ *   dx [T, d] bf16 out; dw_gate [d, E] fp32 out.
+ */
+int moe_route_backward(int64_t T, int64_t d_model, int32_t E, int32_t E_shared,
+                       int32_t k, int32_t dtype, const void* x, const void* w_gate,
+                       const float* logits, const int32_t* topk_idx,
+                       const float* topk_w, const float* dtopk_w,
+                       const int32_t* counts, const int32_t* row_of_pair,
+                       const void* dx_perm, const void* dx_shared, float alpha,
+                       float beta, void* dx, float* dw_gate, void* ws,
+                       size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

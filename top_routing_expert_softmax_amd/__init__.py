@@ -22,7 +22,8 @@ MOE_BF16 = 1
 EXPORTS = ("moe_strerror", "moe_last_error", "moe_capacity", "moe_workspace_size",
            "moe_route", "moe_route_v3", "moe_update_bias", "moe_ec_capacity", "moe_route_ec",
            "moe_permute_ec", "moe_quantize_fp8", "moe_expert_ffn_fp8", "moe_permute",
-           "moe_expert_ffn", "moe_combine", "moe_aux_stats")
+           "moe_expert_ffn", "moe_combine", "moe_aux_stats", "moe_backward_workspace_size",
+           "moe_combine_backward", "moe_expert_ffn_backward", "moe_route_backward")
 
 _lib = None
 
@@ -72,6 +73,17 @@ def lib():
     L.moe_expert_ffn_fp8.restype = ctypes.c_int
     L.moe_expert_ffn_fp8.argtypes = [i64, i64, i32, i32, i32, i64, vp, vp, vp, vp, vp, vp, vp,
                                      vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.moe_backward_workspace_size.restype = ctypes.c_int
+    L.moe_backward_workspace_size.argtypes = [i64, i64, i32, i32, i32, i64, i32,
+                                              ctypes.POINTER(sz)]
+    L.moe_combine_backward.restype = ctypes.c_int
+    L.moe_combine_backward.argtypes = [i64, i64, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp]
+    L.moe_expert_ffn_backward.restype = ctypes.c_int
+    L.moe_expert_ffn_backward.argtypes = [i64, i64, i32, i32, i32, i64, i32] + [vp] * 19 + \
+        [sz, vp]
+    L.moe_route_backward.restype = ctypes.c_int
+    L.moe_route_backward.argtypes = [i64, i64, i32, i32, i32, i32] + [vp] * 10 + [f32, f32] + \
+        [vp, vp, vp, sz, vp]
     L.moe_permute.restype = ctypes.c_int
     L.moe_permute.argtypes = [i64, i64, i32, i32, f64, i32, vp, vp, vp, vp, vp, vp, vp, vp,
                               vp, sz, vp]
@@ -238,6 +250,78 @@ def moe_aux_stats(logits, counts, k, CF, f, P, scalars, ws, stream=None):
     _check("moe_aux_stats", lib().moe_aux_stats(
         T, E, k, 0.0 if CF is None else float(CF), _ptr(logits), _ptr(counts), _ptr(f),
         _ptr(P), _ptr(scalars), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def moe_backward_workspace_size(T, d_model, E, E_shared, k, d_ff):
+    n = ctypes.c_size_t()
+    _check("moe_backward_workspace_size", lib().moe_backward_workspace_size(
+        T, d_model, E, E_shared, k, d_ff, MOE_BF16, ctypes.byref(n)))
+    return n.value
+
+
+def moe_combine_backward(dy, y_perm, row_of_pair, topk_w, dy_perm, dtopk_w, E_shared=0,
+                         stream=None):
+    T, d = dy.shape
+    k = row_of_pair.shape[1]
+    _check("moe_combine_backward", lib().moe_combine_backward(
+        T, d, E_shared, k, _dtype_code(dy), _ptr(dy), _ptr(y_perm), _ptr(row_of_pair),
+        _ptr(topk_w), _ptr(dy_perm), _ptr(dtopk_w), _stream(stream)))
+
+
+def moe_expert_ffn_backward(T, k, x_perm, offsets, x, w1, w3, w2, dy_perm, dx_perm, dw1, dw3,
+                            dw2, ws, ws1=None, ws3=None, ws2=None, dx_shared=None, dws1=None,
+                            dws3=None, dws2=None, stream=None):
+    E, F, d = w1.shape
+    Es = 0 if ws1 is None else ws1.shape[0]
+    _check("moe_expert_ffn_backward", lib().moe_expert_ffn_backward(
+        T, d, E, Es, k, F, _dtype_code(x_perm), _ptr(x_perm), _ptr(offsets), _ptr(x), _ptr(w1),
+        _ptr(w3), _ptr(w2), _ptr(ws1), _ptr(ws3), _ptr(ws2), _ptr(dy_perm), _ptr(dx_perm),
+        _ptr(dx_shared), _ptr(dw1), _ptr(dw3), _ptr(dw2), _ptr(dws1), _ptr(dws3), _ptr(dws2),
+        _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def moe_route_backward(x, w_gate, logits, topk_idx, topk_w, dtopk_w, counts, row_of_pair,
+                       dx_perm, dx_shared, alpha, beta, dx, dw_gate, ws, E_shared=0,
+                       stream=None):
+    T, d = x.shape
+    E = w_gate.shape[1]
+    k = topk_idx.shape[1]
+    _check("moe_route_backward", lib().moe_route_backward(
+        T, d, E, E_shared, k, _dtype_code(x), _ptr(x), _ptr(w_gate), _ptr(logits),
+        _ptr(topk_idx), _ptr(topk_w), _ptr(dtopk_w), _ptr(counts), _ptr(row_of_pair),
+        _ptr(dx_perm), _ptr(dx_shared), float(alpha), float(beta), _ptr(dx), _ptr(dw_gate),
+        _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def layer_backward(x, w_gate, w1, w3, w2, k, dy, alpha, beta, fwd, ws1=None, ws3=None,
+                   ws2=None, ws=None, stream=None):
+    """Backward of a layer_forward() run (its buffers `fwd`): returns dx,
+    dw_gate, (dw1, dw3, dw2) and the shared experts' (or None)."""
+    T, d = x.shape
+    E, F, _ = w1.shape
+    Es = 0 if ws1 is None else ws1.shape[0]
+    dev = x.device
+    if ws is None:
+        ws = torch.empty(moe_backward_workspace_size(T, d, E, Es, k, F), dtype=torch.uint8,
+                         device=dev)
+    dy_perm = torch.empty((T * k + Es * T, d), dtype=x.dtype, device=dev)
+    dtopk_w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    dx_perm = torch.empty((T * k, d), dtype=x.dtype, device=dev)
+    dx_shared = torch.empty((Es, T, d), dtype=x.dtype, device=dev) if Es else None
+    dw = [torch.empty(w.shape, dtype=torch.float32, device=dev) for w in (w1, w3, w2)]
+    dws = ([torch.empty(w.shape, dtype=torch.float32, device=dev) for w in (ws1, ws3, ws2)]
+           if Es else [None, None, None])
+    dx = torch.empty_like(x)
+    dw_gate = torch.empty((d, E), dtype=torch.float32, device=dev)
+    moe_combine_backward(dy, fwd.y_perm, fwd.row_of_pair, fwd.topk_w, dy_perm, dtopk_w, Es,
+                         stream)
+    moe_expert_ffn_backward(T, k, fwd.x_perm, fwd.offsets, x, w1, w3, w2, dy_perm, dx_perm,
+                            dw[0], dw[1], dw[2], ws, ws1, ws3, ws2, dx_shared, dws[0], dws[1],
+                            dws[2], stream)
+    moe_route_backward(x, w_gate, fwd.logits, fwd.topk_idx, fwd.topk_w, dtopk_w, fwd.counts,
+                       fwd.row_of_pair, dx_perm, dx_shared, alpha, beta, dx, dw_gate, ws, Es,
+                       stream)
+    return dx, dw_gate, tuple(dw), (tuple(dws) if Es else None)
 
 
 # ------------------------------------------------------ whole-layer helper --

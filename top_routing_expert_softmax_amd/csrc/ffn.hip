@@ -441,7 +441,10 @@ void gemm_big_kernel(FfnArgs a, int NT, int ncu) {
   // depend on arrival order) and runs the epilogue.
   const int MT = *a.ntiles;
   const int L = MT * NT;
-  const int K = PHASE == 1 ? a.d : a.F;
+  // PHASE 3 is phase 1 with the gate and up products stored apart (the
+  // recompute of the backward pass)
+  constexpr bool P1 = PHASE != 2;
+  const int K = P1 ? a.d : a.F;
   const int nk_all = K / BKT;
   const int r = L % ncu;
   int S = 1;
@@ -489,9 +492,9 @@ void gemm_big_kernel(FfnArgs a, int NT, int ncu) {
   const int wave = tid / kWave;
   const int wm = wave / WN, wn = wave % WN;
 
-  const int N = PHASE == 1 ? a.F : a.d;
-  const int n0 = nt * (PHASE == 1 ? kBN2 / 2 : kBN2);
-  const uint16_t* A = PHASE == 1
+  const int N = P1 ? a.F : a.d;
+  const int n0 = nt * (P1 ? kBN2 / 2 : kBN2);
+  const uint16_t* A = P1
       ? static_cast<const uint16_t*>(routed ? a.x_perm : a.x) + static_cast<int64_t>(arow0) * K
       : static_cast<const uint16_t*>(a.H) + static_cast<int64_t>(hrow0) * K;
   const int64_t wstride = static_cast<int64_t>(a.F) * a.d;
@@ -515,7 +518,7 @@ void gemm_big_kernel(FfnArgs a, int NT, int ncu) {
     const int lchunk = (lane % G::CH) ^ ((r / G::RPL) % G::CH);
     int col;
     const uint16_t* W;
-    if (PHASE == 1) {
+    if (P1) {
       col = n0 + (r & 127);
       W = static_cast<const uint16_t*>(r < 128 ? (routed ? a.w1 : a.ws1) : (routed ? a.w3 : a.ws3));
     } else {
@@ -544,7 +547,7 @@ void gemm_big_kernel(FfnArgs a, int NT, int ncu) {
   for (int mi = 0; mi < MI; ++mi) a_off[mi] = (wm * WR + mi * 32 + (lane & 31)) * G::ROW;
 #pragma unroll
   for (int ni = 0; ni < NB; ++ni) {
-    const int r = PHASE == 1
+    const int r = P1
         ? ((ni / (NB / 2)) * 128 + wn * (128 / WN) + (ni % (NB / 2)) * 32 + (lane & 31))
         : (wn * (kBN2 / WN) + ni * 32 + (lane & 31));
     b_off[ni] = BMT * G::ROW + r * G::ROW;
@@ -590,9 +593,13 @@ void gemm_big_kernel(FfnArgs a, int NT, int ncu) {
     __threadfence();
     __syncthreads();
     int* flag = reinterpret_cast<int*>(lds_bytes);
-    if (tid == 0)
-      *flag = atomicAdd(&a.sk_count[(PHASE - 1) * kMaxCUs + tile_sk], 1u) ==
-              static_cast<unsigned>(S - 1);
+    unsigned* count = &a.sk_count[(PHASE == 2 ? kMaxCUs : 0) + tile_sk];
+    if (tid == 0) {
+      const bool last = atomicAdd(count, 1u) == static_cast<unsigned>(S - 1);
+      // the last part leaves the counter at zero for the next launch
+      if (last) *count = 0u;
+      *flag = last;
+    }
     __syncthreads();
     if (*flag == 0) return;
     __threadfence();            // acquire: the other parts' partials
@@ -614,7 +621,26 @@ void gemm_big_kernel(FfnArgs a, int NT, int ncu) {
 
   // ---- epilogue (accumulator element v of lane l: row 8*(v/4) + 4*(l/32)
   // + v%4, column l%32 of its 32 x 32 block)
-  if (PHASE == 1) {
+  if (PHASE == 3) {
+    // gate to columns 0..F-1, up to F..2F-1 of a [rows, 2F] buffer
+    uint16_t* G = static_cast<uint16_t*>(a.H) + static_cast<int64_t>(hrow0) * 2 * a.F;
+#pragma unroll
+    for (int ni = 0; ni < NB / 2; ++ni) {
+      const int col = n0 + wn * (128 / WN) + ni * 32 + (lane & 31);
+      if (col >= N) continue;
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int row = wm * WR + mi * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+          if (row < mrows) {
+            G[static_cast<int64_t>(row) * 2 * a.F + col] = f32_to_bf16(acc[mi][ni][v]);
+            G[static_cast<int64_t>(row) * 2 * a.F + a.F + col] =
+                f32_to_bf16(acc[mi][ni + NB / 2][v]);
+          }
+        }
+    }
+  } else if (PHASE == 1) {
     uint16_t* Hout = static_cast<uint16_t*>(a.H) + static_cast<int64_t>(hrow0) * a.F;
 #pragma unroll
     for (int ni = 0; ni < NB / 2; ++ni) {
@@ -777,6 +803,115 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(FfnArgs a) {
   }
 }
 
+// ------------------------------------------------- weight gradients --
+//
+// C_s[M, N] (fp32) = A_s[M, K_s] B_s[N, K_s]^T for every segment s (routed
+// experts, then shared), from K-major copies of the backward's activations:
+// A and B are [rows][ld] with segment s in columns poff[s] .. poff[s+1]
+// (its rows, zero-padded to a multiple of 64).  256 x 256 tiles, the LDS
+// ring main loop of the forward; one block per (segment, tile), all of K.
+struct WgradArgs {
+  const uint16_t* A;
+  const uint16_t* B;
+  int64_t ld;
+  const int* poff;          // [nseg + 1]
+  float* C_routed;          // segment s < E: C_routed + s * M * N
+  float* C_shared;          // segment s >= E: C_shared + (s - E) * M * N
+  int M, N, E, NT;
+};
+
+template <int BKT, int NST, int WAVES>
+__global__ __launch_bounds__(WAVES * kWave) __attribute__((amdgpu_waves_per_eu(WAVES / 4, WAVES / 4)))
+void gemm_wgrad_kernel(WgradArgs a) {
+  constexpr int BMT = 256;
+  using G = SliceGeom<BKT, BMT>;
+  constexpr int WN = WAVES / 2;
+  constexpr int WR = BMT / 2;
+  constexpr int MI = WR / 32;
+  constexpr int NB = kBN2 / WN / 32;
+  constexpr int AROWS = BMT / WAVES;
+  constexpr int BROWS = kBN2 / WAVES;
+  constexpr int NIA = AROWS / G::RPI;
+  constexpr int NIB = BROWS / G::RPI;
+  extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
+
+  const int seg = blockIdx.y;
+  const int mt = blockIdx.x / a.NT, nt = blockIdx.x % a.NT;
+  const int m0 = mt * BMT, n0 = nt * kBN2;
+  const int k0 = a.poff[seg];
+  const int nk = (a.poff[seg + 1] - k0) / BKT;
+  float* C = seg < a.E ? a.C_routed + static_cast<int64_t>(seg) * a.M * a.N
+                       : a.C_shared + static_cast<int64_t>(seg - a.E) * a.M * a.N;
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const int wm = wave / WN, wn = wave % WN;
+
+  const uint16_t* asrc[NIA];
+  const uint16_t* bsrc[NIB];
+#pragma unroll
+  for (int i = 0; i < NIA; ++i) {
+    const int r = wave * AROWS + i * G::RPI + lane / G::CH;
+    const int lchunk = (lane % G::CH) ^ ((r / G::RPL) % G::CH);
+    const int row = min(m0 + r, a.M - 1);
+    asrc[i] = a.A + static_cast<int64_t>(row) * a.ld + k0 + lchunk * 8;
+  }
+#pragma unroll
+  for (int i = 0; i < NIB; ++i) {
+    const int r = wave * BROWS + i * G::RPI + lane / G::CH;
+    const int lchunk = (lane % G::CH) ^ ((r / G::RPL) % G::CH);
+    const int row = min(n0 + r, a.N - 1);
+    bsrc[i] = a.B + static_cast<int64_t>(row) * a.ld + k0 + lchunk * 8;
+  }
+  char* lds_bytes = reinterpret_cast<char*>(lds);
+  const int a_dst = wave * AROWS * G::ROW;
+  const int b_dst = BMT * G::ROW + wave * BROWS * G::ROW;
+  f32x16_t acc[MI][NB];
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int jn = 0; jn < NB; ++jn)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][jn][v] = 0.f;
+  int a_off[MI], b_off[NB];
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi) a_off[mi] = (wm * WR + mi * 32 + (lane & 31)) * G::ROW;
+#pragma unroll
+  for (int ni = 0; ni < NB; ++ni)
+    b_off[ni] = BMT * G::ROW + (wn * (kBN2 / WN) + ni * 32 + (lane & 31)) * G::ROW;
+  if (nk > 0)
+    gemm_mainloop<BKT, BMT, NST, NIA, NIB, MI, NB, MI>(acc, asrc, bsrc, lds_bytes, a_dst, b_dst,
+                                                       a_off, b_off, lane, nk);
+  // (a segment with no rows stores zeros)
+#pragma unroll
+  for (int ni = 0; ni < NB; ++ni) {
+    const int col = n0 + wn * (kBN2 / WN) + ni * 32 + (lane & 31);
+    if (col >= a.N) continue;
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int row = m0 + wm * WR + mi * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        if (row < a.M) C[static_cast<int64_t>(row) * a.N + col] = acc[mi][ni][v];
+      }
+  }
+}
+
+hipError_t launch_wgrad(const WgradArgs& a0, int nseg, hipStream_t s) {
+  WgradArgs a = a0;
+  a.NT = (a.N + kBN2 - 1) / kBN2;
+  const int MT = (a.M + 255) / 256;
+  constexpr size_t lds = static_cast<size_t>(kNSTsel) * SliceGeom<kBKsel, 256>::STAGE;
+  auto kern = &gemm_wgrad_kernel<kBKsel, kNSTsel, kWavesSel>;
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+      static_cast<int>(lds));
+  if (attr != hipSuccess) return attr;
+  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(MT * a.NT), static_cast<unsigned>(nseg)),
+                     dim3(kWavesSel * kWave), lds, s, a);
+  return hipGetLastError();
+}
+
 int64_t max_tiles(int64_t T, int E, int Es, int k, int BM) {
   return (T * k + BM - 1) / BM + E + static_cast<int64_t>(Es) * ((T + BM - 1) / BM);
 }
@@ -868,6 +1003,134 @@ hipError_t launch_expert_ffn(int64_t T, int64_t d, int E, int E_shared, int k, i
                        dim3(kThreads), 0, s, a);
   }
   return hipGetLastError();
+}
+
+// ------------------------------------------------------------- backward --
+
+namespace {
+
+// Workspace of the backward, after the forward's tile table and split-K
+// region: segment info, transposed weights (W2^T per expert, [W1; W3]^T),
+// the recomputed (A, B) -> (dA, dB) buffer, dH -> H, and the K-major
+// copies of X, dO, H and (dA, dB) for the weight gradients.
+struct BwdLayout {
+  size_t seg, w2t, w13t, g13, dh, xt, dot, ht, dabt, total;
+  int64_t rows, ld;       // H-indexed rows; K-major row length (padded)
+};
+
+BwdLayout bwd_layout(int64_t T, int64_t d, int E, int Es, int k, int64_t F) {
+  BwdLayout L;
+  const int64_t tiles_cap = max_tiles(T, E, Es, k, kBMf);
+  size_t at = 256 + align256(static_cast<size_t>(tiles_cap) * sizeof(int4)) + ffn_sk_bytes(2);
+  L.rows = T * k + static_cast<int64_t>(Es) * T;
+  L.ld = (L.rows + 64LL * (E + Es) + 63) / 64 * 64;
+  const int G = E + Es;
+  auto take = [&](size_t bytes) { const size_t p = at; at += align256(bytes); return p; };
+  L.seg = take(3 * sizeof(int) * (G + 1));
+  L.w2t = take(static_cast<size_t>(G) * F * d * 2);
+  L.w13t = take(static_cast<size_t>(G) * d * 2 * F * 2);
+  L.g13 = take(static_cast<size_t>(L.rows) * 2 * F * 2);
+  L.dh = take(static_cast<size_t>(L.rows) * F * 2);
+  L.xt = take(static_cast<size_t>(d) * L.ld * 2);
+  L.dot = take(static_cast<size_t>(d) * L.ld * 2);
+  L.ht = take(static_cast<size_t>(F) * L.ld * 2);
+  L.dabt = take(static_cast<size_t>(2 * F) * L.ld * 2);
+  L.total = at;
+  return L;
+}
+
+}  // namespace
+
+size_t ffn_backward_workspace_bytes(int64_t T, int64_t d, int E, int E_shared, int k,
+                                    int64_t d_ff) {
+  return bwd_layout(T, d, E, E_shared, k, d_ff).total;
+}
+
+hipError_t launch_expert_ffn_backward(int64_t T, int64_t d, int E, int E_shared, int k,
+                                      int64_t F, const void* x_perm, const int32_t* offsets,
+                                      const void* x, const void* w1, const void* w3,
+                                      const void* w2, const void* ws1, const void* ws3,
+                                      const void* ws2, const void* dy_perm, void* dx_perm,
+                                      void* dx_shared, float* dw1, float* dw3, float* dw2,
+                                      float* dws1, float* dws3, float* dws2, void* ws,
+                                      hipStream_t s) {
+  const BwdLayout L = bwd_layout(T, d, E, E_shared, k, F);
+  char* base = static_cast<char*>(ws);
+  int* ntiles = reinterpret_cast<int*>(base);
+  int4* tiles = reinterpret_cast<int4*>(base + 256);
+  const int64_t tiles_cap = max_tiles(T, E, E_shared, k, kBMf);
+  char* sk = base + 256 + align256(static_cast<size_t>(tiles_cap) * sizeof(int4));
+  float* sk_partial = reinterpret_cast<float*>(sk);
+  unsigned* sk_count =
+      reinterpret_cast<unsigned*>(sk + static_cast<size_t>(kMaxCUs) * kBM2 * kBN2 * 4);
+  const int G = E + E_shared;
+  int* poff = reinterpret_cast<int*>(base + L.seg);
+  int* hstart = poff + (G + 1);
+  int* nrows = hstart + (G + 1);
+  uint16_t* w2t = reinterpret_cast<uint16_t*>(base + L.w2t);
+  uint16_t* w13t = reinterpret_cast<uint16_t*>(base + L.w13t);
+  void* g13 = base + L.g13;
+  void* dh = base + L.dh;
+  const int64_t wsz = F * d;                     // elements of one expert matrix
+  const int Fi = static_cast<int>(F), di = static_cast<int>(d);
+
+  hipError_t err = hipSuccess;
+  auto ok = [&](hipError_t e) { if (err == hipSuccess) err = e; return err == hipSuccess; };
+  // tiles of the large-tile kernel (and zeroed split-K counters), segment info
+  hipLaunchKernelGGL(tile_table_kernel, dim3(1), dim3(kWave), 0, s, offsets, tiles, ntiles, E,
+                     E_shared, static_cast<int>(T), k, kBM2, sk_count);
+  ok(launch_seg_info(offsets, poff, hstart, nrows, E, E_shared, T, k, s));
+  // transposed weights: W2^T [G][F][d]; [W1; W3]^T [G][d][2F]
+  ok(launch_transpose_batched(w2, w2t, E, di, Fi, d, 0, s));
+  ok(launch_transpose_batched(w1, w13t, E, Fi, di, 2 * F, 0, s));
+  ok(launch_transpose_batched(w3, w13t, E, Fi, di, 2 * F, Fi, s));
+  if (E_shared > 0) {
+    ok(launch_transpose_batched(ws2, w2t + E * wsz, E_shared, di, Fi, d, 0, s));
+    ok(launch_transpose_batched(ws1, w13t + 2 * E * wsz, E_shared, Fi, di, 2 * F, 0, s));
+    ok(launch_transpose_batched(ws3, w13t + 2 * E * wsz, E_shared, Fi, di, 2 * F, Fi, s));
+  }
+  int dev = 0, ncu = 0;
+  if (ok(hipGetDevice(&dev))) ok(hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev));
+  if (err != hipSuccess) return err;
+  ncu = max(kXcds, min(ncu, kMaxCUs));
+  const int64_t mt = max_tiles(T, E, E_shared, k, kBM2);
+  auto nt_of = [](int64_t n, int cols) { return static_cast<int>((n + cols - 1) / cols); };
+  // 1. recompute A = X W1^T and B = X W3^T into (A, B) rows of g13
+  FfnArgs a3{x_perm, x, offsets, w1, w3, w2, ws1, ws3, ws2, g13, nullptr, nullptr, tiles, ntiles,
+             sk_partial, sk_count, static_cast<int>(T), di, E, E_shared, k, Fi};
+  ok(launch_gemm_big<3>(a3, nt_of(F, kBN2 / 2), mt, ncu, s));
+  // 2. dH = dO W2: the phase-2 form with K = d and N = F (W2^T rows)
+  FfnArgs ah{nullptr, nullptr, offsets, nullptr, nullptr, w2t, nullptr, nullptr,
+             w2t + E * wsz, const_cast<void*>(dy_perm), dh,
+             static_cast<uint16_t*>(dh) + T * k * F, tiles, ntiles, sk_partial, sk_count,
+             static_cast<int>(T), Fi, E, E_shared, k, di};
+  ok(launch_gemm_big<2>(ah, nt_of(F, kBN2), mt, ncu, s));
+  // 3. (A, B), dH -> (dA, dB), H, in place
+  ok(launch_swiglu_bwd(g13, dh, offsets, E, T * k, L.rows, F, s));
+  // 4. dX = [dA dB] [W1; W3]: the phase-2 form with K = 2F and N = d
+  FfnArgs ax{nullptr, nullptr, offsets, nullptr, nullptr, w13t, nullptr, nullptr,
+             w13t + 2 * E * wsz, g13, dx_perm, dx_shared, tiles, ntiles, sk_partial, sk_count,
+             static_cast<int>(T), di, E, E_shared, k, 2 * Fi};
+  ok(launch_gemm_big<2>(ax, nt_of(d, kBN2), mt, ncu, s));
+  // 5. K-major copies for the weight gradients
+  uint16_t* xt = reinterpret_cast<uint16_t*>(base + L.xt);
+  uint16_t* dot = reinterpret_cast<uint16_t*>(base + L.dot);
+  uint16_t* ht = reinterpret_cast<uint16_t*>(base + L.ht);
+  uint16_t* dabt = reinterpret_cast<uint16_t*>(base + L.dabt);
+  ok(launch_transpose_seg(x_perm, x, xt, poff, hstart, nrows, di, L.ld, E, E_shared, T, k, s));
+  ok(launch_transpose_seg(dy_perm, nullptr, dot, poff, hstart, nrows, di, L.ld, E, E_shared, T,
+                          k, s));
+  ok(launch_transpose_seg(dh, nullptr, ht, poff, hstart, nrows, Fi, L.ld, E, E_shared, T, k, s));
+  ok(launch_transpose_seg(g13, nullptr, dabt, poff, hstart, nrows, 2 * Fi, L.ld, E, E_shared, T,
+                          k, s));
+  // 6. dW1 = dA^T X, dW3 = dB^T X  ([F, d]),  dW2 = dO^T H  ([d, F])
+  WgradArgs g1{dabt, xt, L.ld, poff, dw1, dws1, Fi, di, E, 0};
+  ok(launch_wgrad(g1, G, s));
+  WgradArgs g3{dabt + F * L.ld, xt, L.ld, poff, dw3, dws3, Fi, di, E, 0};
+  ok(launch_wgrad(g3, G, s));
+  WgradArgs g2{dot, ht, L.ld, poff, dw2, dws2, di, Fi, E, 0};
+  ok(launch_wgrad(g2, G, s));
+  return err;
 }
 
 }  // namespace moe

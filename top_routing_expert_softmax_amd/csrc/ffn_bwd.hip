@@ -1,0 +1,193 @@
+// Helpers of the expert-FFN backward pass (bf16): segment offsets, the
+// transposes that put every GEMM of the backward in the "both operands
+// K-contiguous" form of the forward kernel, and the elementwise SwiGLU
+// step.
+//
+// For one expert with rows X (the gathered tokens), A = X W1^T, B = X W3^T,
+// H = SiLU(A) (*) B, O = H W2^T, and output gradient dO:
+//   dH = dO W2,  dA = dH (*) B (*) SiLU'(A),  dB = dH (*) SiLU(A)
+//   dX = dA W1 + dB W3 = [dA dB] [W1; W3]
+//   dW1 = dA^T X,  dW3 = dB^T X,  dW2 = dO^T H
+// (the chain rule of the SwiGLU expert, "CMU 11-868 Lecture 17" section
+// 5.2).  Rows are "H-indexed": routed rows 0 .. R-1 as in x_perm, shared
+// expert s's rows at T*k + s*T.
+#include <math.h>
+
+#include <algorithm>
+
+#include "moe_device.h"
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+constexpr int kTile = 64;   // transpose tile (64 x 64 bf16)
+
+// One wavefront: for segment s (routed e < E, then shared), its first
+// H-indexed row, its row count and its column offset in the K-major copies
+// (a prefix sum of the counts rounded up to 64).
+__global__ __launch_bounds__(kWave) void seg_info_kernel(const int32_t* __restrict__ offsets,
+                                                        int* __restrict__ poff,
+                                                        int* __restrict__ hstart,
+                                                        int* __restrict__ nrows, int E, int Es,
+                                                        int T, int k) {
+  const int lane = threadIdx.x;
+  const int nseg = E + Es;
+  constexpr int kPer = 5;                        // nseg <= 272 < 64 * 5
+  int pad[kPer];
+  int tot = 0;
+#pragma unroll
+  for (int q = 0; q < kPer; ++q) {
+    const int s = lane * kPer + q;
+    int n = 0, h = 0;
+    if (s < E) {
+      h = offsets[s];
+      n = offsets[s + 1] - h;
+    } else if (s < nseg) {
+      h = T * k + (s - E) * T;
+      n = T;
+    }
+    if (s < nseg) {
+      hstart[s] = h;
+      nrows[s] = n;
+    }
+    pad[q] = (n + 63) / 64 * 64;
+    tot += pad[q];
+  }
+  int incl = tot;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int n = __shfl_up(incl, off, kWave);
+    if (lane >= off) incl += n;
+  }
+  int base = incl - tot;
+#pragma unroll
+  for (int q = 0; q < kPer; ++q) {
+    const int s = lane * kPer + q;
+    if (s < nseg) poff[s] = base;
+    base += pad[q];
+  }
+  if (lane == kWave - 1) poff[nseg] = incl;
+}
+
+// dst[g][c][col0 + r] = src[g][r][c] for a batch of G matrices src [R][C]
+// (dst rows hold ld elements): the weights' transposes.
+__global__ __launch_bounds__(256) void transpose_batched_kernel(const uint16_t* __restrict__ src,
+                                                                uint16_t* __restrict__ dst,
+                                                                int R, int C, int64_t ld,
+                                                                int col0) {
+  __shared__ uint16_t tile[kTile][kTile + 2];
+  const int g = blockIdx.z;
+  const int r0 = blockIdx.y * kTile, c0 = blockIdx.x * kTile;
+  const uint16_t* S = src + static_cast<int64_t>(g) * R * C;
+  uint16_t* D = dst + static_cast<int64_t>(g) * C * ld;
+  const int tx = threadIdx.x % kTile, ty = threadIdx.x / kTile;   // 64 x 4
+  for (int i = ty; i < kTile; i += 4) {
+    const int r = r0 + i, c = c0 + tx;
+    if (r < R && c < C) tile[i][tx] = S[static_cast<int64_t>(r) * C + c];
+  }
+  __syncthreads();
+  for (int i = ty; i < kTile; i += 4) {
+    const int c = c0 + i, r = r0 + tx;
+    if (r < R && c < C) D[static_cast<int64_t>(c) * ld + col0 + r] = tile[tx][i];
+  }
+}
+
+// K-major copy of H-indexed activations: dst[c][poff[s] + j] = row
+// hstart[s] + j of the source (column c), for j < nrows[s], and 0 up to the
+// next multiple of 64.  Routed rows come from src; shared rows from
+// src_shared[(row - T*k) mod T] when given (x), else from src (H-indexed).
+__global__ __launch_bounds__(256) void transpose_seg_kernel(
+    const uint16_t* __restrict__ src, const uint16_t* __restrict__ src_shared,
+    uint16_t* __restrict__ dst, const int* __restrict__ poff, const int* __restrict__ hstart,
+    const int* __restrict__ nrows, int C, int64_t ld, int E, int T, int k) {
+  __shared__ uint16_t tile[kTile][kTile + 2];
+  const int s = blockIdx.z;
+  const int n = nrows[s];
+  const int npad = poff[s + 1] - poff[s];
+  const int j0 = blockIdx.y * kTile, c0 = blockIdx.x * kTile;
+  if (j0 >= npad) return;
+  const int h = hstart[s];
+  const int tx = threadIdx.x % kTile, ty = threadIdx.x / kTile;
+  for (int i = ty; i < kTile; i += 4) {
+    const int j = j0 + i, c = c0 + tx;
+    uint16_t v = 0;
+    if (j < n && c < C) {
+      const int row = h + j;
+      const uint16_t* S = (s >= E && src_shared != nullptr)
+          ? src_shared + static_cast<int64_t>((row - T * k) % T) * C
+          : src + static_cast<int64_t>(row) * C;
+      v = S[c];
+    }
+    tile[i][tx] = v;
+  }
+  __syncthreads();
+  for (int i = ty; i < kTile; i += 4) {
+    const int c = c0 + i, j = j0 + tx;
+    if (c < C && j < npad) dst[static_cast<int64_t>(c) * ld + poff[s] + j] = tile[tx][i];
+  }
+}
+
+// In place, per valid H-indexed row (one block per row): g13 [2F] =
+// (A, B) -> (dA, dB) and dh [F] -> H = SiLU(A) (*) B.
+__global__ __launch_bounds__(256) void swiglu_bwd_kernel(uint16_t* __restrict__ g13,
+                                                         uint16_t* __restrict__ dh,
+                                                         const int32_t* __restrict__ offsets,
+                                                         int E, int64_t Tk, int F) {
+  const int64_t row = blockIdx.x;
+  if (row < Tk && row >= offsets[E]) return;     // routed rows past R are unused
+  uint16_t* G = g13 + row * 2 * F;
+  uint16_t* D = dh + row * F;
+  for (int f = threadIdx.x; f < F; f += blockDim.x) {
+    const float a = bf16_to_f32(G[f]), b = bf16_to_f32(G[F + f]), d = bf16_to_f32(D[f]);
+    const float sg = 1.0f / (1.0f + __expf(-a));
+    const float s = a * sg;
+    G[f] = f32_to_bf16(d * b * sg * (1.0f + a * (1.0f - sg)));
+    G[F + f] = f32_to_bf16(d * s);
+    D[f] = f32_to_bf16(s * b);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_seg_info(const int32_t* offsets, int* poff, int* hstart, int* nrows, int E,
+                           int Es, int64_t T, int k, hipStream_t s) {
+  hipLaunchKernelGGL(seg_info_kernel, dim3(1), dim3(kWave), 0, s, offsets, poff, hstart, nrows,
+                     E, Es, static_cast<int>(T), k);
+  return hipGetLastError();
+}
+
+hipError_t launch_transpose_batched(const void* src, void* dst, int G, int R, int C, int64_t ld,
+                                    int col0, hipStream_t s) {
+  if (G == 0) return hipSuccess;
+  const dim3 grid(static_cast<unsigned>((C + kTile - 1) / kTile),
+                  static_cast<unsigned>((R + kTile - 1) / kTile), static_cast<unsigned>(G));
+  hipLaunchKernelGGL(transpose_batched_kernel, grid, dim3(256), 0, s,
+                     static_cast<const uint16_t*>(src), static_cast<uint16_t*>(dst), R, C, ld,
+                     col0);
+  return hipGetLastError();
+}
+
+hipError_t launch_transpose_seg(const void* src, const void* src_shared, void* dst,
+                                const int* poff, const int* hstart, const int* nrows, int C,
+                                int64_t ld, int E, int Es, int64_t T, int k, hipStream_t s) {
+  // a segment has at most T rows
+  const dim3 grid(static_cast<unsigned>((C + kTile - 1) / kTile),
+                  static_cast<unsigned>((T + kTile - 1) / kTile + 1),
+                  static_cast<unsigned>(E + Es));
+  hipLaunchKernelGGL(transpose_seg_kernel, grid, dim3(256), 0, s,
+                     static_cast<const uint16_t*>(src), static_cast<const uint16_t*>(src_shared),
+                     static_cast<uint16_t*>(dst), poff, hstart, nrows, C, ld, E,
+                     static_cast<int>(T), k);
+  return hipGetLastError();
+}
+
+hipError_t launch_swiglu_bwd(void* g13, void* dh, const int32_t* offsets, int E, int64_t Tk,
+                             int64_t rows_total, int64_t F, hipStream_t s) {
+  hipLaunchKernelGGL(swiglu_bwd_kernel, dim3(static_cast<unsigned>(rows_total)), dim3(256), 0, s,
+                     static_cast<uint16_t*>(g13), static_cast<uint16_t*>(dh), offsets, E, Tk,
+                     static_cast<int>(F));
+  return hipGetLastError();
+}
+
+}  // namespace moe

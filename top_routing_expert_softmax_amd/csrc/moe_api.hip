@@ -294,6 +294,125 @@ int moe_permute_ec(int64_t T, int64_t d_model, int32_t E, int64_t cap, int32_t d
                   "moe_permute_ec");
 }
 
+int moe_backward_workspace_size(int64_t T, int64_t d_model, int32_t E, int32_t E_shared,
+                                int32_t k, int64_t d_ff, int32_t dtype, size_t* bytes) {
+  if (int r = check_common(T, E, k)) return r;
+  if (int r = check_dim("d_model", d_model)) return r;
+  if (int r = check_dim("d_ff", d_ff)) return r;
+  REQUIRE(dtype == MOE_BF16, "the backward pass runs in bf16 (dtype MOE_BF16)");
+  REQUIRE(E_shared >= 0 && E_shared <= 16, "E_shared must be in [0, 16]");
+  REQUIRE(bytes != nullptr, "bytes is NULL");
+  *bytes = align256(std::max(moe::ffn_backward_workspace_bytes(T, d_model, E, E_shared, k, d_ff),
+                             moe::route_backward_workspace_bytes(T, E)));
+  return MOE_OK;
+}
+
+int moe_combine_backward(int64_t T, int64_t d_model, int32_t E_shared, int32_t k, int32_t dtype,
+                         const void* dy, const void* y_perm, const int32_t* row_of_pair,
+                         const float* topk_w, void* dy_perm, float* dtopk_w, void* stream) {
+  REQUIRE(T >= 1, "T must be >= 1");
+  REQUIRE(k >= 1 && k <= 64, "k must be in [1, 64]");
+  REQUIRE(dtype == MOE_BF16, "the backward pass runs in bf16 (dtype MOE_BF16)");
+  if (int r = check_dim("d_model", d_model)) return r;
+  REQUIRE(E_shared >= 0 && E_shared <= 16, "E_shared must be in [0, 16]");
+  REQUIRE(T * k + static_cast<int64_t>(E_shared) * T < (int64_t(1) << 31),
+          "T*k + E_shared*T must be < 2^31");
+  REQUIRE_PTR(dy);
+  REQUIRE_PTR(y_perm);
+  REQUIRE_PTR(row_of_pair);
+  REQUIRE_PTR(topk_w);
+  REQUIRE_PTR(dy_perm);
+  REQUIRE_PTR(dtopk_w);
+  (void)hipGetLastError();
+  return launched(moe::launch_combine_backward(T, d_model, E_shared, k, dy, y_perm, row_of_pair,
+                                               topk_w, dy_perm, dtopk_w,
+                                               static_cast<hipStream_t>(stream)),
+                  "moe_combine_backward");
+}
+
+int moe_expert_ffn_backward(int64_t T, int64_t d_model, int32_t E, int32_t E_shared, int32_t k,
+                            int64_t d_ff, int32_t dtype, const void* x_perm,
+                            const int32_t* offsets, const void* x, const void* w1,
+                            const void* w3, const void* w2, const void* ws1, const void* ws3,
+                            const void* ws2, const void* dy_perm, void* dx_perm, void* dx_shared,
+                            float* dw1, float* dw3, float* dw2, float* dws1, float* dws3,
+                            float* dws2, void* ws, size_t ws_bytes, void* stream) {
+  if (int r = check_common(T, E, k)) return r;
+  if (int r = check_dim("d_model", d_model)) return r;
+  if (int r = check_dim("d_ff", d_ff)) return r;
+  REQUIRE(dtype == MOE_BF16, "the backward pass runs in bf16 (dtype MOE_BF16)");
+  REQUIRE(E_shared >= 0 && E_shared <= 16, "E_shared must be in [0, 16]");
+  REQUIRE(T * k + static_cast<int64_t>(E_shared) * T < (int64_t(1) << 31),
+          "T*k + E_shared*T must be < 2^31");
+  REQUIRE_PTR(x_perm);
+  REQUIRE_PTR(offsets);
+  REQUIRE_PTR(w1);
+  REQUIRE_PTR(w3);
+  REQUIRE_PTR(w2);
+  REQUIRE_PTR(dy_perm);
+  REQUIRE_PTR(dx_perm);
+  REQUIRE_PTR(dw1);
+  REQUIRE_PTR(dw3);
+  REQUIRE_PTR(dw2);
+  REQUIRE_PTR(ws);
+  if (E_shared > 0) {
+    REQUIRE_PTR(x);
+    REQUIRE_PTR(ws1);
+    REQUIRE_PTR(ws3);
+    REQUIRE_PTR(ws2);
+    REQUIRE_PTR(dx_shared);
+    REQUIRE_PTR(dws1);
+    REQUIRE_PTR(dws3);
+    REQUIRE_PTR(dws2);
+  }
+  const size_t need = moe::ffn_backward_workspace_bytes(T, d_model, E, E_shared, k, d_ff);
+  if (ws_bytes < need)
+    return fail(MOE_EWORKSPACE, "moe_expert_ffn_backward needs %zu workspace bytes, got %zu",
+                need, ws_bytes);
+  (void)hipGetLastError();
+  return launched(moe::launch_expert_ffn_backward(T, d_model, E, E_shared, k, d_ff, x_perm,
+                                                  offsets, x, w1, w3, w2, ws1, ws3, ws2, dy_perm,
+                                                  dx_perm, dx_shared, dw1, dw3, dw2, dws1, dws3,
+                                                  dws2, ws, static_cast<hipStream_t>(stream)),
+                  "moe_expert_ffn_backward");
+}
+
+int moe_route_backward(int64_t T, int64_t d_model, int32_t E, int32_t E_shared, int32_t k,
+                       int32_t dtype, const void* x, const void* w_gate, const float* logits,
+                       const int32_t* topk_idx, const float* topk_w, const float* dtopk_w,
+                       const int32_t* counts, const int32_t* row_of_pair, const void* dx_perm,
+                       const void* dx_shared, float alpha, float beta, void* dx, float* dw_gate,
+                       void* ws, size_t ws_bytes, void* stream) {
+  if (int r = check_common(T, E, k)) return r;
+  if (int r = check_dim("d_model", d_model)) return r;
+  REQUIRE(dtype == MOE_BF16, "the backward pass runs in bf16 (dtype MOE_BF16)");
+  REQUIRE(E_shared >= 0 && E_shared <= 16, "E_shared must be in [0, 16]");
+  REQUIRE(isfinite(alpha) && isfinite(beta), "alpha and beta must be finite");
+  REQUIRE_PTR(x);
+  REQUIRE_PTR(w_gate);
+  REQUIRE_PTR(logits);
+  REQUIRE_PTR(topk_idx);
+  REQUIRE_PTR(topk_w);
+  REQUIRE_PTR(dtopk_w);
+  REQUIRE_PTR(counts);
+  REQUIRE_PTR(row_of_pair);
+  REQUIRE_PTR(dx_perm);
+  REQUIRE_PTR(dx);
+  REQUIRE_PTR(dw_gate);
+  REQUIRE_PTR(ws);
+  if (E_shared > 0) REQUIRE_PTR(dx_shared);
+  const size_t need = moe::route_backward_workspace_bytes(T, E);
+  if (ws_bytes < need)
+    return fail(MOE_EWORKSPACE, "moe_route_backward needs %zu workspace bytes, got %zu", need,
+                ws_bytes);
+  (void)hipGetLastError();
+  return launched(moe::launch_route_backward(T, d_model, E, E_shared, k, x, w_gate, logits,
+                                             topk_idx, topk_w, dtopk_w, counts, row_of_pair,
+                                             dx_perm, dx_shared, alpha, beta, dx, dw_gate, ws,
+                                             static_cast<hipStream_t>(stream)),
+                  "moe_route_backward");
+}
+
 int moe_quantize_fp8(int64_t rows, int64_t cols, int32_t dtype, const void* w, uint8_t* codes,
                      float* scales, void* stream) {
   REQUIRE(rows >= 1 && rows < (int64_t(1) << 31), "rows must be in [1, 2^31)");

@@ -91,6 +91,41 @@ hipError_t launch_ffn_stream(int phase, int64_t T, int64_t d, int E, int E_share
                              const float* sc2 = nullptr, const float* ssc1 = nullptr,
                              const float* ssc3 = nullptr, const float* ssc2 = nullptr);
 
+// Expert-FFN backward (ffn.hip orchestrates; helpers in ffn_bwd.hip).
+size_t ffn_backward_workspace_bytes(int64_t T, int64_t d, int E, int E_shared, int k,
+                                    int64_t d_ff);
+hipError_t launch_expert_ffn_backward(int64_t T, int64_t d, int E, int E_shared, int k,
+                                      int64_t F, const void* x_perm, const int32_t* offsets,
+                                      const void* x, const void* w1, const void* w3,
+                                      const void* w2, const void* ws1, const void* ws3,
+                                      const void* ws2, const void* dy_perm, void* dx_perm,
+                                      void* dx_shared, float* dw1, float* dw3, float* dw2,
+                                      float* dws1, float* dws3, float* dws2, void* ws,
+                                      hipStream_t s);
+hipError_t launch_seg_info(const int32_t* offsets, int* poff, int* hstart, int* nrows, int E,
+                           int Es, int64_t T, int k, hipStream_t s);
+hipError_t launch_transpose_batched(const void* src, void* dst, int G, int R, int C, int64_t ld,
+                                    int col0, hipStream_t s);
+hipError_t launch_transpose_seg(const void* src, const void* src_shared, void* dst,
+                                const int* poff, const int* hstart, const int* nrows, int C,
+                                int64_t ld, int E, int Es, int64_t T, int k, hipStream_t s);
+hipError_t launch_swiglu_bwd(void* g13, void* dh, const int32_t* offsets, int E, int64_t Tk,
+                             int64_t rows_total, int64_t F, hipStream_t s);
+
+// Combine and router backward (bwd.hip).
+hipError_t launch_combine_backward(int64_t T, int64_t d, int E_shared, int k, const void* dy,
+                                   const void* y_perm, const int32_t* row_of_pair,
+                                   const float* topk_w, void* dy_perm, float* dtopk_w,
+                                   hipStream_t s);
+size_t route_backward_workspace_bytes(int64_t T, int E);
+hipError_t launch_route_backward(int64_t T, int64_t d, int E, int E_shared, int k, const void* x,
+                                 const void* w_gate, const float* logits,
+                                 const int32_t* topk_idx, const float* topk_w,
+                                 const float* dtopk_w, const int32_t* counts,
+                                 const int32_t* row_of_pair, const void* dx_perm,
+                                 const void* dx_shared, float alpha, float beta, void* dx,
+                                 float* dw_gate, void* ws, hipStream_t s);
+
 // Per-row FP8 E4M3 quantisation (quant.hip).
 hipError_t launch_quantize_fp8(int64_t rows, int64_t cols, bool bf16, const void* w,
                                uint8_t* codes, float* scales, hipStream_t s);
