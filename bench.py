@@ -4,7 +4,8 @@
 
 One step is one pass of the whole layer (moe_route, moe_permute,
 moe_expert_ffn, moe_combine, moe_aux_stats) over one batch of seeded
-synthetic input already resident in HBM.  Prints one JSON line with the
+synthetic input already resident in HBM (--backward: a training step, the
+forward plus the three backward entry points).  Prints one JSON line with the
 whole-job tokens/s, the roofline of the grouped expert GEMM call (timed
 with HIP events on the launch stream) and the CPU oracle timed on a
 bounded token sample of the same workload.
@@ -139,6 +140,11 @@ def main():
                     help="expert weights as stored: bf16, or FP8 E4M3 codes with per-row "
                          "scales (quantised by moe_quantize_fp8 before timing; decode "
                          "steps, T <= 64)")
+    ap.add_argument("--backward", action="store_true",
+                    help="time a training step: the forward (moe_expert_ffn_train, which "
+                         "keeps the pre-activations) plus moe_combine_backward, "
+                         "moe_expert_ffn_backward and moe_route_backward (seeded dy, "
+                         "alpha = 0.01, beta = 0.001); bf16, softmax router")
     ap.add_argument("--router", default="softmax", choices=["softmax", "v3", "ec"],
                     help="softmax top-k router (moe_route) or the DeepSeek-V3 gate "
                          "(moe_route_v3: 8 groups, 4 kept, scale 2.5, seeded bias in "
@@ -168,7 +174,44 @@ def main():
     b = M.MoELayerBuffers(T, d, E, Es, k, F, dtype)
     stream = torch.cuda.current_stream()
     names = ["route", "permute", "expert_ffn", "combine", "aux_stats"]
+    if args.backward:
+        if cfg.dtype != "bf16" or args.router != "softmax" or args.weights != "bf16":
+            print("--backward runs the bf16 layer with the softmax router", file=sys.stderr)
+            sys.exit(2)
+        names += ["combine_bwd", "expert_ffn_bwd", "route_bwd"]
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+    bwd = None
+    if args.backward:
+        emp = lambda *shape, dt=torch.float32: torch.empty(shape, dtype=dt, device="cuda")  # noqa
+        g = torch.Generator(device="cuda")
+        g.manual_seed(cfg.seed)
+        bwd = {"dy": torch.randn((T, d), generator=g, device="cuda").to(dtype),
+               "dy_perm": emp(T * k + Es * T, d, dt=dtype), "dtw": emp(T, k),
+               "dx_perm": emp(T * k, d, dt=dtype),
+               "dx_sh": emp(Es, T, d, dt=dtype) if Es else None,
+               "dw": [emp(*dev[kd].shape) for kd in ("w1", "w3", "w2")],
+               "dws": [emp(*dev[kd].shape) for kd in ("ws1", "ws3", "ws2")] if Es else [None] * 3,
+               "dx": emp(T, d, dt=dtype), "dwg": emp(d, E),
+               "ws": torch.empty(M.moe_backward_workspace_size(T, d, E, Es, k, F),
+                                 dtype=torch.uint8, device="cuda"),
+               "ab": emp(T * k + Es * T, 2 * F, dt=dtype)}
+
+    def backward(timed):
+        M.moe_combine_backward(bwd["dy"], b.y_perm, b.row_of_pair, b.topk_w, bwd["dy_perm"],
+                               bwd["dtw"], Es, stream)
+        if timed:
+            ev[6].record(stream)
+        M.moe_expert_ffn_backward(T, k, b.x_perm, b.offsets, dev["x"], dev["w1"], dev["w3"],
+                                  dev["w2"], bwd["dy_perm"], bwd["dx_perm"], *bwd["dw"],
+                                  bwd["ws"], dev.get("ws1"), dev.get("ws3"), dev.get("ws2"),
+                                  bwd["dx_sh"], *bwd["dws"], stream=stream, ab=bwd["ab"])
+        if timed:
+            ev[7].record(stream)
+        M.moe_route_backward(dev["x"], dev["wg"], b.logits, b.topk_idx, b.topk_w, bwd["dtw"],
+                             b.counts, b.row_of_pair, bwd["dx_perm"], bwd["dx_sh"], 0.01, 0.001,
+                             bwd["dx"], bwd["dwg"], bwd["ws"], Es, stream)
+        if timed:
+            ev[8].record(stream)
 
     v3 = None
     if args.router == "v3":
@@ -210,6 +253,12 @@ def main():
         torch.cuda.empty_cache()
 
     def ffn():
+        if bwd is not None:
+            # the forward of a training step keeps A = X W1^T, B = X W3^T
+            M.moe_expert_ffn_train(T, k, b.x_perm, b.offsets, dev["x"], dev["w1"], dev["w3"],
+                                   dev["w2"], dev.get("ws1"), dev.get("ws3"), dev.get("ws2"),
+                                   b.y_perm, b.y_shared, bwd["ab"], b.ws, stream)
+            return
         if fp8 is None:
             M.moe_expert_ffn(T, k, b.x_perm, b.offsets, dev["x"], dev["w1"], dev["w3"],
                              dev["w2"], dev.get("ws1"), dev.get("ws3"), dev.get("ws2"),
@@ -278,6 +327,8 @@ def main():
         M.moe_aux_stats(b.logits, b.counts, k, cfg.CF, b.f, b.P, b.scalars, b.ws, stream)
         if timed:
             ev[5].record(stream)
+        if bwd is not None:
+            backward(timed)
 
     for _ in range(args.warmup):
         step(False)
@@ -312,7 +363,12 @@ def main():
         wb = touched * 3.0 * d * F * cfg.bytes_per_el
         bytes_alg = bytes_alg - wb + touched * (3.0 * d * F + 4.0 * (2 * F + d))
     ffn_ms = float(per_call[names.index("expert_ffn")])
-    if cfg.T <= 256:      # decode-shaped: weight streaming, HBM-bound
+    if bwd is not None:
+        # the backward's expert GEMMs from the kept pre-activations: dH (2),
+        # dX (4), dW1 + dW3 + dW2 (6), in units of d F flop per row
+        flop = flop / 6.0 * 12.0
+        ffn_ms = float(per_call[names.index("expert_ffn_bwd")])
+    if cfg.T <= 256 and bwd is None:      # decode-shaped: weight streaming, HBM-bound
         achieved = bytes_alg / (ffn_ms / 1e3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None}
@@ -333,9 +389,15 @@ def main():
     roof["kernel"] = ("moe_expert_ffn (grouped GEMM phase 1 + phase 2 + tile table)"
                       if fp8 is None else
                       "moe_expert_ffn_fp8 (weight streaming of E4M3 codes, phase 1 + phase 2)")
+    if bwd is not None:
+        roof["kernel"] = ("moe_expert_ffn_backward (dH, dX, weight gradients, transposes; "
+                          "pre-activations kept by the forward)")
+        roof["traffic"] = None
     roof["kernel_ms"] = round(ffn_ms, 4)
 
     extra = {}
+    if bwd is not None:
+        extra = {"step": "forward + backward (alpha = 0.01, beta = 0.001)"}
     if ec is not None:
         extra = {"router": "expert_choice", "ec_capacity": ec["cap"], "ec_ffn_k": ec["k"],
                  "tokens_unpicked": int(T - torch.unique(ec["tok"]).numel())}
@@ -357,7 +419,7 @@ def main():
     cpu = None
     if fp8 is not None:
         extra["weights"] = "fp8_e4m3_row_scaled"
-    if not args.no_cpu_baseline and v3 is None and ec is None and fp8 is None:
+    if not args.no_cpu_baseline and v3 is None and ec is None and fp8 is None and bwd is None:
         log("timing the CPU oracle on a token sample")
         v, threads, n, dt = cpu_baseline(cfg, x, wg, host, args.cpu_sample)
         cpu = {"value": round(v, 3), "unit": "tokens/s", "cores": int(threads),

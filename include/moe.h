@@ -235,6 +235,24 @@ int moe_expert_ffn(int64_t T, int64_t d_model, int32_t E, int32_t E_shared,
                    void* y_shared, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * The forward of a training step ("CMU 11-868 Lecture 17" 5.2, the SwiGLU
+ * expert, whose backward needs A = X W1^T and B = X W3^T): moe_expert_ffn
+ * on the large grouped tiles for any shape, bf16 only, that also writes
+ *   ab [T*k + E_shared*T, 2F] bf16 out: row r holds A (columns 0..F-1) and
+ *     B (F..2F-1) of H row r (kept routed rows 0..R-1, then each shared
+ *     expert's T rows at T*k + s*T); other routed rows unwritten.
+ * y_perm and y_shared are bit-identical to moe_expert_ffn's whenever that
+ * call takes the large tiles (T*k >= 64 E).  Same workspace; the caller owns
+ * ab and hands it to moe_expert_ffn_backward.
+ */
+int moe_expert_ffn_train(int64_t T, int64_t d_model, int32_t E, int32_t E_shared,
+                         int32_t k, int64_t d_ff, int32_t dtype, const void* x_perm,
+                         const int32_t* offsets, const void* x, const void* w1,
+                         const void* w3, const void* w2, const void* ws1, const void* ws3,
+                         const void* ws2, void* y_perm, void* y_shared, void* ab, void* ws,
+                         size_t ws_bytes, void* stream);
+
+/*
  * FP8 expert weights (the pages name FP8 expert storage, "CMU 11-868
  * Lecture 17" section 1.4, without an encoding; this library uses OCP FP8
  * E4M3 codes with one fp32 scale per stored weight row):
@@ -350,7 +368,10 @@ int moe_combine_backward(int64_t T, int64_t d_model, int32_t E_shared, int32_t k
  *   dx_perm [T*k, d] bf16 out (rows of kept pairs); dx_shared [E_shared, T, d]
  *   bf16 out (NULL if E_shared == 0);
  *   dw1, dw3 [E, F, d], dw2 [E, d, F] fp32 out (zero for an expert with no
- *   rows); dws1, dws3, dws2 the shared experts' (NULL if E_shared == 0).
+ *   rows); dws1, dws3, dws2 the shared experts' (NULL if E_shared == 0);
+ *   ab: the pre-activations moe_expert_ffn_train kept for this forward, or
+ *   NULL, in which case A = X W1^T and B = X W3^T are recomputed (one more
+ *   grouped GEMM; the gradients are the same bits either way).
  */
 int moe_expert_ffn_backward(int64_t T, int64_t d_model, int32_t E, int32_t E_shared,
                             int32_t k, int64_t d_ff, int32_t dtype,
@@ -359,8 +380,8 @@ int moe_expert_ffn_backward(int64_t T, int64_t d_model, int32_t E, int32_t E_sha
                             const void* w2, const void* ws1, const void* ws3,
                             const void* ws2, const void* dy_perm, void* dx_perm,
                             void* dx_shared, float* dw1, float* dw3, float* dw2,
-                            float* dws1, float* dws3, float* dws2, void* ws,
-                            size_t ws_bytes, void* stream);
+                            float* dws1, float* dws3, float* dws2, const void* ab,
+                            void* ws, size_t ws_bytes, void* stream);
 
 /*
  *   x [T, d], w_gate [d, E] bf16 in; logits [T, E], topk_w, dtopk_w [T, k]

@@ -59,7 +59,8 @@ __all__ = [
     "affinity_f32", "v3_gate", "update_bias",
     "ec_capacity", "expert_choice", "ec_dispatch", "ec_combine",
     "e4m3_decode", "e4m3_encode", "quantize_fp8_rows", "dequantize_fp8_rows",
-    "silu_grad", "swiglu_expert_backward", "layer_backward",
+    "silu_grad", "swiglu_expert_backward", "layer_backward", "router_logit_grad",
+    "layer_backward_sampled",
 ]
 
 
@@ -558,13 +559,83 @@ def layer_backward(x, w_gate, k, CF, load_expert, E, dy, alpha=0.0, beta=0.0,
         dxs, dw1, dw3, dw2 = swiglu_expert_backward(x, *load_shared(s_), dy)
         dx += dxs
         dshared.append((dw1, dw3, dw2))
+    dg = router_logit_grad(r, counts, dpt, E, alpha, beta)
+    dx += dg @ wg.T
+    return {"dx": dx, "dw_gate": x.T @ dg, "dw": dws, "dw_shared": dshared,
+            "dtopk_w": dpt, "dg": dg, "route": r, "disp": disp, "counts": counts}
+
+
+def router_logit_grad(r, counts, dpt, E, alpha, beta):
+    """dL/dg for all tokens from the routing r, the per-expert counts and
+    dp~ (dL/dp~ per (token, choice), 0 for a dropped pair): the selected
+    softmax ([RM] 2.1), the balance loss through P_i ([RM] 3.4) and the
+    z-loss ([SA] router_z_loss), as layer_backward states them."""
+    pt = r["weights"]
     p = r["probs"]
+    T = p.shape[0]
     dg = np.zeros((T, E))
     inner = np.sum(pt * dpt, axis=1, keepdims=True)
     np.add.at(dg, (np.arange(T)[:, None], r["idx"]), pt * (dpt - inner))
     c = alpha * E * (counts / float(T)) / float(T)
     dg += p * (c[None, :] - (p * c[None, :]).sum(axis=1, keepdims=True))
     dg += beta * 2.0 * r["lse"][:, None] * p / float(T)
-    dx += dg @ wg.T
-    return {"dx": dx, "dw_gate": x.T @ dg, "dw": dws, "dw_shared": dshared,
+    return dg
+
+
+def layer_backward_sampled(x, w_gate, k, CF, load_expert, E, dy, alpha, beta, tokens, units,
+                           E_shared=0, load_shared=None, shared_units=()):
+    """The gradients of layer_backward at a sample, for layers too large to
+    hold every weight gradient on the host: dx at the given tokens; for each
+    (e, f) in units, row f of dW1 and dW3 and column f of dW2 of routed
+    expert e (shared_units: the same for shared experts); dW_gate and dp~ in
+    full (dp~ needs every expert output).
+
+    Hidden unit f of a SwiGLU expert depends only on W1[f], W3[f] and
+    W2[:, f], so the gradients of those weights are those of the expert cut
+    down to the single unit f, which swiglu_expert_backward gives."""
+    x = _f64(x)
+    dy = _f64(dy)
+    wg = _f64(w_gate)
+    tokens = np.asarray(tokens)
+    T, d = x.shape
+    r = route(x, wg, k)
+    counts = expert_counts(r["idx"], E)
+    disp = dispatch(r["idx"], E, capacity(T, E, k, CF))
+    kept = disp["drop"] == 0
+    pt = r["weights"]
+    dx = np.zeros((len(tokens), d))
+    dpt = np.zeros_like(pt)
+    where = {int(t): i for i, t in enumerate(tokens)}
+    dw_units = {}
+    for e in range(E):
+        tt, jj = np.nonzero((r["idx"] == e) & kept)
+        mine = [(e_, f) for (e_, f) in units if e_ == e]
+        if len(tt) == 0:
+            for (_, f) in mine:
+                dw_units[(e, f)] = (np.zeros(d), np.zeros(d), np.zeros(d))
+            continue
+        w1, w3, w2 = (_f64(a) for a in load_expert(e))
+        dpt[tt, jj] = np.sum(dy[tt] * swiglu_expert(x[tt], w1, w3, w2), axis=1)
+        dout = pt[tt, jj][:, None] * dy[tt]
+        sel = np.array([i for i, t in enumerate(tt) if int(t) in where], dtype=np.int64)
+        if len(sel):
+            dxe = swiglu_expert_backward(x[tt[sel]], w1, w3, w2, dout[sel])[0]
+            for i, row in zip(sel, dxe):
+                dx[where[int(tt[i])]] += row
+        for (_, f) in mine:
+            _, g1, g3, g2 = swiglu_expert_backward(x[tt], w1[f:f + 1], w3[f:f + 1],
+                                                   w2[:, f:f + 1], dout)
+            dw_units[(e, f)] = (g1[0], g3[0], g2[:, 0])
+    dws_units = {}
+    for s_ in range(E_shared):
+        w1, w3, w2 = (_f64(a) for a in load_shared(s_))
+        dx += swiglu_expert_backward(x[tokens], w1, w3, w2, dy[tokens])[0]
+        for (s2, f) in shared_units:
+            if s2 == s_:
+                _, g1, g3, g2 = swiglu_expert_backward(x, w1[f:f + 1], w3[f:f + 1],
+                                                       w2[:, f:f + 1], dy)
+                dws_units[(s_, f)] = (g1[0], g3[0], g2[:, 0])
+    dg = router_logit_grad(r, counts, dpt, E, alpha, beta)
+    dx += dg[tokens] @ wg.T
+    return {"dx": dx, "dw_units": dw_units, "dws_units": dws_units, "dw_gate": x.T @ dg,
             "dtopk_w": dpt, "dg": dg, "route": r, "disp": disp, "counts": counts}

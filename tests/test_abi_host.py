@@ -180,3 +180,29 @@ def test_fp8_arguments_are_checked(M):
     assert ffn(T=65) == -2 and "T must be <= 64" in L.moe_last_error().decode()
     assert ffn(s1=nil) == -1
     assert ffn(ws=1024) == -4
+
+
+def test_training_forward_and_backward_arguments_are_checked(M):
+    L = M.lib()
+    nil = ctypes.c_void_p(0)
+    fake = ctypes.c_void_p(4096)
+
+    def train(dtype=M.MOE_BF16, ab=fake, ws=1 << 34, d=4096):
+        return L.moe_expert_ffn_train(4096, d, 8, 0, 2, 14336, dtype, fake, fake, fake, fake,
+                                      fake, fake, nil, nil, nil, fake, nil, ab, fake, ws, nil)
+    assert train(dtype=M.MOE_F32) == -1 and "bf16" in L.moe_last_error().decode()
+    assert train(ab=nil) == -1 and "ab" in L.moe_last_error().decode()
+    assert train(ws=1024) == -4
+    assert train(d=100) == -1                                # not a multiple of 64
+
+    def bwd(dtype=M.MOE_BF16, ws=1 << 36, dw1=fake):
+        return L.moe_expert_ffn_backward(4096, 4096, 8, 0, 2, 14336, dtype, fake, fake, fake,
+                                         fake, fake, fake, nil, nil, nil, fake, fake, nil, dw1,
+                                         fake, fake, nil, nil, nil, nil, fake, ws, nil)
+    assert bwd(dtype=M.MOE_F32) == -1
+    assert bwd(dw1=nil) == -1
+    assert bwd(ws=1024) == -4 and "workspace" in L.moe_last_error().decode()
+    n = ctypes.c_size_t()
+    assert L.moe_backward_workspace_size(4096, 4096, 8, 0, 2, 14336, M.MOE_BF16,
+                                         ctypes.byref(n)) == 0
+    assert n.value > 3 * 8 * 4096 * 14336 * 2               # holds the transposed weights

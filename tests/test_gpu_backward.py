@@ -29,12 +29,14 @@ def _close(name, got, ref):
     assert mr <= 5e-3, f"{name}: mean relative error {mr:.3e} > 5e-3"
 
 
-def _backward_case(cfg, alpha, beta, seed=9):
+def _backward_case(cfg, alpha, beta, seed=9, save_ab=False):
     import top_routing_expert_softmax_amd as M
-    H.log(f"backward: {cfg}")
+    H.log(f"backward (save_ab={save_ab}): {cfg}")
     inp = H.LayerInputs(cfg)
     dd = inp.dev
-    b = H.run_gpu(inp)
+    b = M.layer_forward(inp.x_dev, inp.wg_dev, dd["w1"], dd["w3"], dd["w2"], cfg.k, cfg.CF,
+                        dd.get("ws1"), dd.get("ws3"), dd.get("ws2"), save_ab=save_ab)
+    torch.cuda.synchronize()
     rng = np.random.default_rng(seed)
     dy32 = rng.standard_normal((cfg.T, cfg.d_model)).astype(np.float32)
     dy_dev = torch.from_numpy(dy32).cuda().to(torch.bfloat16)
@@ -63,6 +65,124 @@ def test_backward_small_with_drops_and_shared():
     _backward_case(cfg, alpha=0.1, beta=0.01)
 
 
+def test_backward_small_from_kept_preactivations():
+    cfg = get_config("dsmoe16b_prefill", T=300, d_model=256, E=8, E_shared=1, k=2, d_ff=320,
+                     CF=1.0)
+    _backward_case(cfg, alpha=0.1, beta=0.01, save_ab=True)
+
+
+@pytest.mark.parametrize("shape", [
+    dict(T=300, d_model=256, E=8, E_shared=1, k=2, d_ff=320, CF=1.0),     # drops, shared
+    dict(T=40, d_model=192, E=16, E_shared=2, k=4, d_ff=128, CF=None),     # decode-sized
+])
+def test_training_forward_keeps_preactivations(shape):
+    """moe_expert_ffn_train: y is the same bits as moe_expert_ffn on the
+    large tiles (the decode-sized shape takes other kernels there, so only
+    parity is asked), A and B match the oracle's X W1^T and X W3^T on every
+    kept row, and the backward from the kept (A, B) is the same bits as the
+    backward that recomputes them."""
+    import top_routing_expert_softmax_amd as M
+    cfg = get_config("dsmoe16b_prefill", **shape)
+    H.log(f"training forward: {cfg}")
+    inp = H.LayerInputs(cfg)
+    dd = inp.dev
+    args = (inp.x_dev, inp.wg_dev, dd["w1"], dd["w3"], dd["w2"], cfg.k, cfg.CF, dd.get("ws1"),
+            dd.get("ws3"), dd.get("ws2"))
+    b0 = M.layer_forward(*args)
+    y0 = b0.y.clone()
+    b1 = M.layer_forward(*args, save_ab=True)
+    torch.cuda.synchronize()
+    large = cfg.T * cfg.k >= 64 * cfg.E
+    if large:
+        assert torch.equal(b1.y, y0)
+    else:
+        g = H.host(b1)
+        r, counts, cap, disp, stats = H.oracle_routing(inp)
+        H.check_y(cfg, g["y"], H.oracle_y(inp, r, disp, np.arange(cfg.T)))
+    # A and B against the oracle on every kept routed row and shared row
+    R = int(b1.offsets[-1].item())
+    tor = b1.token_of_row[:R].cpu().numpy()
+    offs = b1.offsets.cpu().numpy()
+    ab = b1.ab.float().cpu().numpy()
+    F = cfg.d_ff
+    got, ref = [], []
+    for e in range(cfg.E):
+        rows = np.arange(offs[e], offs[e + 1])
+        if len(rows) == 0:
+            continue
+        w1, w3, _ = inp.load_routed(e)
+        xr = inp.x[tor[rows]].astype(np.float64)
+        got.append(ab[rows])
+        ref.append(np.concatenate([xr @ w1.T, xr @ w3.T], axis=1))
+    for s_ in range(cfg.E_shared):
+        w1, w3, _ = (a.astype(np.float64) for a in inp.load_shared(s_))
+        rows = cfg.T * cfg.k + s_ * cfg.T + np.arange(cfg.T)
+        got.append(ab[rows])
+        xr = inp.x.astype(np.float64)
+        ref.append(np.concatenate([xr @ w1.T, xr @ w3.T], axis=1))
+    _close("A, B", np.concatenate(got), np.concatenate(ref))
+    # backward: kept (A, B) versus recomputed, bit for bit
+    rng = np.random.default_rng(5)
+    dy = torch.from_numpy(rng.standard_normal((cfg.T, cfg.d_model)).astype(np.float32)).cuda()
+    dy = dy.to(torch.bfloat16)
+    ab_keep = b1.ab
+    g1 = M.layer_backward(inp.x_dev, inp.wg_dev, dd["w1"], dd["w3"], dd["w2"], cfg.k, dy, 0.1,
+                          0.01, b1, dd.get("ws1"), dd.get("ws3"), dd.get("ws2"))
+    b1.ab = None
+    g0 = M.layer_backward(inp.x_dev, inp.wg_dev, dd["w1"], dd["w3"], dd["w2"], cfg.k, dy, 0.1,
+                          0.01, b1, dd.get("ws1"), dd.get("ws3"), dd.get("ws2"))
+    b1.ab = ab_keep
+    torch.cuda.synchronize()
+    assert torch.equal(g1[0], g0[0]), "dx differs"
+    assert torch.equal(g1[1], g0[1]), "dw_gate differs"
+    for m in range(3):
+        assert torch.equal(g1[2][m], g0[2][m]), f"expert weight gradient {m} differs"
+        if cfg.E_shared:
+            assert torch.equal(g1[3][m], g0[3][m]), f"shared weight gradient {m} differs"
+
+
 def test_backward_mid_size():
     cfg = get_config("mixtral_prefill", T=1024, d_model=1024, E=8, k=2, d_ff=2048, CF=1.25)
     _backward_case(cfg, alpha=0.01, beta=0.001)
+
+
+def test_backward_full_size_sampled():
+    """The Mixtral-shaped prefill layer (T=4096, d=4096, E=8, k=2, F=14336)
+    in the launch configuration the training-step benchmark times (forward
+    keeping the pre-activations, backward from them): dW_gate
+    in full, dx on sampled tokens and the weight gradients of sampled hidden
+    units (rows of dW1, dW3, columns of dW2), against the oracle's sampled
+    backward."""
+    import top_routing_expert_softmax_amd as M
+    from workloads import storage_bits
+    cfg = get_config("mixtral_prefill")
+    alpha, beta = 0.01, 0.001
+    H.log(f"backward full size: {cfg}")
+    inp = H.LayerInputs(cfg)
+    dd = inp.dev
+    b = M.layer_forward(inp.x_dev, inp.wg_dev, dd["w1"], dd["w3"], dd["w2"], cfg.k, cfg.CF,
+                        save_ab=True)
+    rng = np.random.default_rng(cfg.seed + 1)
+    dy_bits = storage_bits(cfg, rng.standard_normal((cfg.T, cfg.d_model)).astype(np.float32))
+    dy_dev = H.to_device(cfg, dy_bits)
+    dy = bf16_bits_to_f32(dy_bits).astype(np.float64)
+    dx, dwg, dw, _ = M.layer_backward(inp.x_dev, inp.wg_dev, dd["w1"], dd["w3"], dd["w2"], cfg.k,
+                                      dy_dev, alpha, beta, b)
+    torch.cuda.synchronize()
+    tokens = np.unique(np.concatenate([rng.choice(cfg.T, size=24, replace=False),
+                                       [0, cfg.T - 1]]))
+    units = [(0, 0), (cfg.E - 1, cfg.d_ff - 1)] + [
+        (int(rng.integers(cfg.E)), int(rng.integers(cfg.d_ff))) for _ in range(6)]
+    got_dx = dx[torch.from_numpy(tokens).cuda()].float().cpu().numpy()
+    got_u = [tuple(t.cpu().numpy() for t in (dw[0][e, f], dw[1][e, f], dw[2][e, :, f]))
+             for (e, f) in units]
+    got_dwg = dwg.cpu().numpy()
+    del b, dx, dw
+    H.log(f"oracle: {len(tokens)} tokens, {len(units)} hidden units, dW_gate in full")
+    g = O.layer_backward_sampled(inp.x, inp.wg, cfg.k, cfg.CF, inp.load_routed, cfg.E, dy, alpha,
+                                 beta, tokens, units)
+    _close("dx (sampled tokens)", got_dx, g["dx"])
+    _close("dw_gate", got_dwg, g["dw_gate"])
+    for m, name in enumerate(("dw1 rows", "dw3 rows", "dw2 columns")):
+        _close(name, np.stack([u[m] for u in got_u]),
+               np.stack([g["dw_units"][u][m] for u in units]))

@@ -81,3 +81,32 @@ def test_dense_swiglu_mlp_against_torch_autograd():
         np.testing.assert_allclose(got, want.numpy(), rtol=1e-12, atol=1e-12)
     # a single expert always gets weight 1: no gradient reaches the router
     np.testing.assert_allclose(g["dw_gate"], 0.0, atol=1e-12)
+
+
+@pytest.mark.parametrize("seed,CF", [(3, 0.75), (4, None)])
+def test_sampled_backward_equals_full(seed, CF):
+    """layer_backward_sampled (unit-by-unit weight gradients, dx at a token
+    sample) gives the entries of the finite-difference-pinned layer_backward."""
+    x, wg, experts, shared, dy = _setup(seed, T=11, d=6, E=4, k=2, F=5, n_shared=1)
+    k, alpha, beta = 2, 0.3, 0.2
+    E = wg.shape[1]
+    full = O.layer_backward(x, wg, k, CF, lambda e: experts[e], E, dy, alpha, beta,
+                            len(shared), lambda s: shared[s])
+    tokens = np.array([0, 3, 4, 10])
+    units = [(0, 0), (1, 4), (3, 2), (2, 1)]
+    sh_units = [(0, 3)]
+    smp = O.layer_backward_sampled(x, wg, k, CF, lambda e: experts[e], E, dy, alpha, beta,
+                                   tokens, units, len(shared), lambda s: shared[s], sh_units)
+    assert np.allclose(smp["dx"], full["dx"][tokens], rtol=1e-12, atol=1e-12)
+    assert np.allclose(smp["dw_gate"], full["dw_gate"], rtol=1e-12, atol=1e-12)
+    assert np.allclose(smp["dtopk_w"], full["dtopk_w"], rtol=1e-12, atol=1e-12)
+    for (e, f), (g1, g3, g2) in smp["dw_units"].items():
+        dw1, dw3, dw2 = full["dw"][e]
+        assert np.allclose(g1, dw1[f], rtol=1e-12, atol=1e-12)
+        assert np.allclose(g3, dw3[f], rtol=1e-12, atol=1e-12)
+        assert np.allclose(g2, dw2[:, f], rtol=1e-12, atol=1e-12)
+    for (s_, f), (g1, g3, g2) in smp["dws_units"].items():
+        dw1, dw3, dw2 = full["dw_shared"][s_]
+        assert np.allclose(g1, dw1[f], rtol=1e-12, atol=1e-12)
+        assert np.allclose(g3, dw3[f], rtol=1e-12, atol=1e-12)
+        assert np.allclose(g2, dw2[:, f], rtol=1e-12, atol=1e-12)

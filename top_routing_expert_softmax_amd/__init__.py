@@ -22,7 +22,8 @@ MOE_BF16 = 1
 EXPORTS = ("moe_strerror", "moe_last_error", "moe_capacity", "moe_workspace_size",
            "moe_route", "moe_route_v3", "moe_update_bias", "moe_ec_capacity", "moe_route_ec",
            "moe_permute_ec", "moe_quantize_fp8", "moe_expert_ffn_fp8", "moe_permute",
-           "moe_expert_ffn", "moe_combine", "moe_aux_stats", "moe_backward_workspace_size",
+           "moe_expert_ffn", "moe_expert_ffn_train", "moe_combine", "moe_aux_stats",
+           "moe_backward_workspace_size",
            "moe_combine_backward", "moe_expert_ffn_backward", "moe_route_backward")
 
 _lib = None
@@ -79,7 +80,7 @@ def lib():
     L.moe_combine_backward.restype = ctypes.c_int
     L.moe_combine_backward.argtypes = [i64, i64, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp]
     L.moe_expert_ffn_backward.restype = ctypes.c_int
-    L.moe_expert_ffn_backward.argtypes = [i64, i64, i32, i32, i32, i64, i32] + [vp] * 19 + \
+    L.moe_expert_ffn_backward.argtypes = [i64, i64, i32, i32, i32, i64, i32] + [vp] * 20 + \
         [sz, vp]
     L.moe_route_backward.restype = ctypes.c_int
     L.moe_route_backward.argtypes = [i64, i64, i32, i32, i32, i32] + [vp] * 10 + [f32, f32] + \
@@ -90,6 +91,9 @@ def lib():
     L.moe_expert_ffn.restype = ctypes.c_int
     L.moe_expert_ffn.argtypes = [i64, i64, i32, i32, i32, i64, i32, vp, vp, vp, vp, vp, vp,
                                  vp, vp, vp, vp, vp, vp, sz, vp]
+    L.moe_expert_ffn_train.restype = ctypes.c_int
+    L.moe_expert_ffn_train.argtypes = [i64, i64, i32, i32, i32, i64, i32] + [vp] * 13 + \
+        [sz, vp]
     L.moe_combine.restype = ctypes.c_int
     L.moe_combine.argtypes = [i64, i64, i32, i32, i32, vp, vp, vp, vp, vp, vp]
     L.moe_aux_stats.restype = ctypes.c_int
@@ -236,6 +240,16 @@ def moe_expert_ffn(T, k, x_perm, offsets, x, w1, w3, w2, ws1, ws3, ws2, y_perm, 
         _ptr(y_shared), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
 
 
+def moe_expert_ffn_train(T, k, x_perm, offsets, x, w1, w3, w2, ws1, ws3, ws2, y_perm, y_shared,
+                         ab, ws, stream=None):
+    E, F, d = w1.shape
+    Es = 0 if ws1 is None else ws1.shape[0]
+    _check("moe_expert_ffn_train", lib().moe_expert_ffn_train(
+        T, d, E, Es, k, F, _dtype_code(x_perm), _ptr(x_perm), _ptr(offsets), _ptr(x),
+        _ptr(w1), _ptr(w3), _ptr(w2), _ptr(ws1), _ptr(ws3), _ptr(ws2), _ptr(y_perm),
+        _ptr(y_shared), _ptr(ab), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
 def moe_combine(y_perm, y_shared, row_of_pair, topk_w, y, stream=None):
     T, k = row_of_pair.shape
     d = y.shape[1]
@@ -270,14 +284,14 @@ def moe_combine_backward(dy, y_perm, row_of_pair, topk_w, dy_perm, dtopk_w, E_sh
 
 def moe_expert_ffn_backward(T, k, x_perm, offsets, x, w1, w3, w2, dy_perm, dx_perm, dw1, dw3,
                             dw2, ws, ws1=None, ws3=None, ws2=None, dx_shared=None, dws1=None,
-                            dws3=None, dws2=None, stream=None):
+                            dws3=None, dws2=None, stream=None, ab=None):
     E, F, d = w1.shape
     Es = 0 if ws1 is None else ws1.shape[0]
     _check("moe_expert_ffn_backward", lib().moe_expert_ffn_backward(
         T, d, E, Es, k, F, _dtype_code(x_perm), _ptr(x_perm), _ptr(offsets), _ptr(x), _ptr(w1),
         _ptr(w3), _ptr(w2), _ptr(ws1), _ptr(ws3), _ptr(ws2), _ptr(dy_perm), _ptr(dx_perm),
         _ptr(dx_shared), _ptr(dw1), _ptr(dw3), _ptr(dw2), _ptr(dws1), _ptr(dws3), _ptr(dws2),
-        _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+        _ptr(ab), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def moe_route_backward(x, w_gate, logits, topk_idx, topk_w, dtopk_w, counts, row_of_pair,
@@ -296,7 +310,8 @@ def moe_route_backward(x, w_gate, logits, topk_idx, topk_w, dtopk_w, counts, row
 def layer_backward(x, w_gate, w1, w3, w2, k, dy, alpha, beta, fwd, ws1=None, ws3=None,
                    ws2=None, ws=None, stream=None):
     """Backward of a layer_forward() run (its buffers `fwd`): returns dx,
-    dw_gate, (dw1, dw3, dw2) and the shared experts' (or None)."""
+    dw_gate, (dw1, dw3, dw2) and the shared experts' (or None).  Uses the
+    pre-activations the forward kept (save_ab=True), else recomputes them."""
     T, d = x.shape
     E, F, _ = w1.shape
     Es = 0 if ws1 is None else ws1.shape[0]
@@ -317,7 +332,7 @@ def layer_backward(x, w_gate, w1, w3, w2, k, dy, alpha, beta, fwd, ws1=None, ws3
                          stream)
     moe_expert_ffn_backward(T, k, fwd.x_perm, fwd.offsets, x, w1, w3, w2, dy_perm, dx_perm,
                             dw[0], dw[1], dw[2], ws, ws1, ws3, ws2, dx_shared, dws[0], dws[1],
-                            dws[2], stream)
+                            dws[2], stream, ab=getattr(fwd, "ab", None))
     moe_route_backward(x, w_gate, fwd.logits, fwd.topk_idx, fwd.topk_w, dtopk_w, fwd.counts,
                        fwd.row_of_pair, dx_perm, dx_shared, alpha, beta, dx, dw_gate, ws, Es,
                        stream)
@@ -351,11 +366,14 @@ class MoELayerBuffers:
         self.scalars = torch.empty(3, dtype=torch.float64, device=dev)
         nbytes = moe_workspace_size(T, d_model, E, E_shared, k, d_ff, dtype)
         self.ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        self.ab = None          # pre-activations, when a training forward keeps them
 
 
 def layer_forward(x, w_gate, w1, w3, w2, k, CF, ws1=None, ws3=None, ws2=None, bufs=None,
-                  stream=None):
-    """Run the five entry points in order on one stream; returns the buffers."""
+                  stream=None, save_ab=False):
+    """Run the five entry points in order on one stream; returns the buffers.
+    save_ab: run moe_expert_ffn_train and keep the pre-activations in
+    bufs.ab for layer_backward."""
     T, d = x.shape
     E, F, _ = w1.shape
     Es = 0 if ws1 is None else ws1.shape[0]
@@ -365,8 +383,15 @@ def layer_forward(x, w_gate, w1, w3, w2, k, CF, ws1=None, ws3=None, ws2=None, bu
     moe_route(x, w_gate, k, b.logits, b.topk_idx, b.topk_w, b.ws, stream)
     moe_permute(b.topk_idx, x, E, CF, b.counts, b.offsets, b.token_of_row, b.row_of_pair,
                 b.drop_mask, b.x_perm, b.ws, stream)
-    moe_expert_ffn(T, k, b.x_perm, b.offsets, x, w1, w3, w2, ws1, ws3, ws2, b.y_perm,
-                   b.y_shared, b.ws, stream)
+    if save_ab:
+        if b.ab is None:
+            b.ab = torch.empty((T * k + Es * T, 2 * F), dtype=x.dtype, device=x.device)
+        moe_expert_ffn_train(T, k, b.x_perm, b.offsets, x, w1, w3, w2, ws1, ws3, ws2, b.y_perm,
+                             b.y_shared, b.ab, b.ws, stream)
+    else:
+        b.ab = None
+        moe_expert_ffn(T, k, b.x_perm, b.offsets, x, w1, w3, w2, ws1, ws3, ws2, b.y_perm,
+                       b.y_shared, b.ws, stream)
     moe_combine(b.y_perm, b.y_shared, b.row_of_pair, b.topk_w, b.y, stream)
     moe_aux_stats(b.logits, b.counts, k, CF, b.f, b.P, b.scalars, b.ws, stream)
     return b

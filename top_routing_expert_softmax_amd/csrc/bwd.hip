@@ -14,6 +14,8 @@
 //   dW_gate = x^T dg,  dx_t = sum_s dX_s,t + sum_j dX_tj + dg_t W_gate^T.
 #include <math.h>
 
+#include <algorithm>
+
 #include "moe_device.h"
 #include "moe_internal.h"
 
@@ -179,27 +181,66 @@ __global__ __launch_bounds__(256) void dx_kernel(
   }
 }
 
-// dw_gate[i][e] = sum_t x[t][i] dg[t][e]: thread i, experts e0 .. e0+7, t in
-// order.
+// dw_gate[i][e] = sum_t x[t][i] dg[t][e] over the token slice blockIdx.z
+// (t in order): thread i, experts e0 .. e0+7.  With several slices the
+// partial sums go to part[slice] and dwgate_sum_kernel adds them in slice
+// order, so the result does not depend on the schedule.
 __global__ __launch_bounds__(256) void dwgate_kernel(const uint16_t* __restrict__ x,
                                                      const float* __restrict__ dg,
-                                                     float* __restrict__ dwg, int T, int d,
-                                                     int E) {
+                                                     float* __restrict__ part, int T, int d,
+                                                     int E, int chunk) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   const int e0 = blockIdx.y * 8;
   if (i >= d) return;
+  const int t0 = blockIdx.z * chunk;
+  const int t1 = min(T, t0 + chunk);
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int t = 0; t < T; ++t) {
+  constexpr int kU = 8;                          // x loads in flight per thread
+  int t = t0;
+  for (; t + kU <= t1; t += kU) {
+    float xv[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) xv[u] = bf16_to_f32(x[static_cast<int64_t>(t + u) * d + i]);
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const float* g = dg + static_cast<int64_t>(t + u) * E + e0;
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        if (e0 + q < E) acc[q] = fmaf(xv[u], g[q], acc[q]);
+    }
+  }
+  for (; t < t1; ++t) {
     const float xv = bf16_to_f32(x[static_cast<int64_t>(t) * d + i]);
     const float* g = dg + static_cast<int64_t>(t) * E + e0;
 #pragma unroll
     for (int q = 0; q < 8; ++q)
       if (e0 + q < E) acc[q] = fmaf(xv, g[q], acc[q]);
   }
+  float* out = part + static_cast<int64_t>(blockIdx.z) * d * E;
 #pragma unroll
   for (int q = 0; q < 8; ++q)
-    if (e0 + q < E) dwg[static_cast<int64_t>(i) * E + e0 + q] = acc[q];
+    if (e0 + q < E) out[static_cast<int64_t>(i) * E + e0 + q] = acc[q];
 }
+
+__global__ __launch_bounds__(256) void dwgate_sum_kernel(const float* __restrict__ part,
+                                                         float* __restrict__ dwg, int64_t n,
+                                                         int S) {
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (idx >= n) return;
+  float s = 0.f;
+  for (int q = 0; q < S; ++q) s += part[q * n + idx];
+  dwg[idx] = s;
+}
+
+// Token slices of dwgate_kernel: about 2048 blocks in all, at least 64
+// tokens a slice.
+int dwgate_slices(int64_t T, int64_t d, int E) {
+  const int64_t blocks0 = ((d + 255) / 256) * ((E + 7) / 8);
+  const int64_t s = std::min<int64_t>((T + 63) / 64, (2048 + blocks0 - 1) / blocks0);
+  return static_cast<int>(std::max<int64_t>(1, s));
+}
+
+size_t align256b(size_t n) { return (n + 255) & ~static_cast<size_t>(255); }
 
 }  // namespace
 
@@ -229,15 +270,28 @@ hipError_t launch_route_backward(int64_t T, int64_t d, int E, int E_shared, int 
                      static_cast<const u32x4_t*>(dx_shared), row_of_pair, dg,
                      static_cast<const uint16_t*>(w_gate), static_cast<u32x4_t*>(dx),
                      static_cast<int>(T), E, k, E_shared, static_cast<int>(d / 8));
+  const int S = dwgate_slices(T, d, E);
+  const int chunk = static_cast<int>((T + S - 1) / S);
+  float* part = S > 1 ? reinterpret_cast<float*>(static_cast<char*>(ws) +
+                                                 align256b(static_cast<size_t>(T) * E * 4))
+                      : dw_gate;
   hipLaunchKernelGGL(dwgate_kernel,
-                     dim3(static_cast<unsigned>((d + 255) / 256), static_cast<unsigned>((E + 7) / 8)),
-                     dim3(256), 0, s, static_cast<const uint16_t*>(x), dg, dw_gate,
-                     static_cast<int>(T), static_cast<int>(d), E);
+                     dim3(static_cast<unsigned>((d + 255) / 256), static_cast<unsigned>((E + 7) / 8),
+                          static_cast<unsigned>(S)),
+                     dim3(256), 0, s, static_cast<const uint16_t*>(x), dg, part,
+                     static_cast<int>(T), static_cast<int>(d), E, chunk);
+  if (S > 1) {
+    const int64_t n = d * E;
+    hipLaunchKernelGGL(dwgate_sum_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256),
+                       0, s, part, dw_gate, n, S);
+  }
   return hipGetLastError();
 }
 
-size_t route_backward_workspace_bytes(int64_t T, int E) {
-  return static_cast<size_t>(T) * E * sizeof(float);
+size_t route_backward_workspace_bytes(int64_t T, int64_t d, int E) {
+  const int S = dwgate_slices(T, d, E);
+  const size_t dg = align256b(static_cast<size_t>(T) * E * sizeof(float));
+  return dg + (S > 1 ? static_cast<size_t>(S) * d * E * sizeof(float) : 0);
 }
 
 }  // namespace moe

@@ -76,6 +76,7 @@ struct FfnArgs {
   float* sk_partial;     // split-K partial tiles of the last wave (fp32)
   unsigned* sk_count;    // arrivals per split tile: [2][kMaxCUs], phase 1 then 2
   int T, d, E, Es, k, F;
+  void* ab;              // PHASE 4: the pre-activations (A, B) as [rows, 2F]
 };
 
 // ---------------------------------------------------------------- tiling --
@@ -442,7 +443,8 @@ void gemm_big_kernel(FfnArgs a, int NT, int ncu) {
   const int MT = *a.ntiles;
   const int L = MT * NT;
   // PHASE 3 is phase 1 with the gate and up products stored apart (the
-  // recompute of the backward pass)
+  // recompute of the backward pass); PHASE 4 stores both H and the two
+  // products (a forward that keeps what its backward needs)
   constexpr bool P1 = PHASE != 2;
   const int K = P1 ? a.d : a.F;
   const int nk_all = K / BKT;
@@ -640,8 +642,10 @@ void gemm_big_kernel(FfnArgs a, int NT, int ncu) {
           }
         }
     }
-  } else if (PHASE == 1) {
+  } else if (PHASE == 1 || PHASE == 4) {
     uint16_t* Hout = static_cast<uint16_t*>(a.H) + static_cast<int64_t>(hrow0) * a.F;
+    uint16_t* G = PHASE == 4 ? static_cast<uint16_t*>(a.ab) + static_cast<int64_t>(hrow0) * 2 * a.F
+                             : nullptr;
 #pragma unroll
     for (int ni = 0; ni < NB / 2; ++ni) {
       const int col = n0 + wn * (128 / WN) + ni * 32 + (lane & 31);
@@ -654,6 +658,11 @@ void gemm_big_kernel(FfnArgs a, int NT, int ncu) {
           if (row < mrows) {
             const float h = silu_f(acc[mi][ni][v]) * acc[mi][ni + NB / 2][v];
             Hout[static_cast<int64_t>(row) * a.F + col] = f32_to_bf16(h);
+            if constexpr (PHASE == 4) {
+              G[static_cast<int64_t>(row) * 2 * a.F + col] = f32_to_bf16(acc[mi][ni][v]);
+              G[static_cast<int64_t>(row) * 2 * a.F + a.F + col] =
+                  f32_to_bf16(acc[mi][ni + NB / 2][v]);
+            }
           }
         }
     }
@@ -936,6 +945,60 @@ size_t ffn_workspace_bytes(int64_t T, int E, int E_shared, int k, int64_t d_ff,
          static_cast<size_t>(hrows) * d_ff * elem_bytes;
 }
 
+namespace {
+
+// Compute units of the current device (one large-tile block fits a CU).
+hipError_t device_cus(int* ncu) {
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err == hipSuccess)
+    err = hipDeviceGetAttribute(ncu, hipDeviceAttributeMultiprocessorCount, dev);
+  if (err == hipSuccess) *ncu = max(kXcds, min(*ncu, kMaxCUs));
+  return err;
+}
+
+// Both phases on the large tiles (the tile table has been built with
+// BM = kBM2); P1 = 1 (H only) or 4 (H and the pre-activations).
+template <int P1>
+hipError_t run_big_ffn(const FfnArgs& a, hipStream_t s) {
+  const int nt1 = (a.F + kBN2 / 2 - 1) / (kBN2 / 2);
+  const int nt2 = (a.d + kBN2 - 1) / kBN2;
+  const int64_t mt = max_tiles(a.T, a.E, a.Es, a.k, kBM2);
+  int ncu = 0;
+  hipError_t err = device_cus(&ncu);
+  if (err != hipSuccess) return err;
+  err = launch_gemm_big<P1>(a, nt1, mt, ncu, s);
+  if (err != hipSuccess) return err;
+  return launch_gemm_big<2>(a, nt2, mt, ncu, s);
+}
+
+}  // namespace
+
+hipError_t launch_expert_ffn_train(int64_t T, int64_t d, int E, int E_shared, int k, int64_t F,
+                                   const void* x_perm, const int32_t* offsets, const void* x,
+                                   const void* w1, const void* w3, const void* w2,
+                                   const void* ws1, const void* ws3, const void* ws2,
+                                   void* y_perm, void* y_shared, void* ab, void* ws,
+                                   hipStream_t s) {
+  char* base = static_cast<char*>(ws);
+  int* ntiles = reinterpret_cast<int*>(base);
+  int4* tiles = reinterpret_cast<int4*>(base + 256);
+  const int64_t tiles_cap = max_tiles(T, E, E_shared, k, kBMf);
+  char* sk = base + 256 + align256(static_cast<size_t>(tiles_cap) * sizeof(int4));
+  float* sk_partial = reinterpret_cast<float*>(sk);
+  unsigned* sk_count =
+      reinterpret_cast<unsigned*>(sk + static_cast<size_t>(kMaxCUs) * kBM2 * kBN2 * 4);
+  void* H = sk + ffn_sk_bytes(2);
+  hipLaunchKernelGGL(tile_table_kernel, dim3(1), dim3(kWave), 0, s, offsets, tiles, ntiles, E,
+                     E_shared, static_cast<int>(T), k, kBM2, sk_count);
+  FfnArgs a{x_perm, x, offsets, w1, w3, w2, ws1, ws3, ws2, H, y_perm, y_shared, tiles, ntiles,
+            sk_partial, sk_count,
+            static_cast<int>(T), static_cast<int>(d), E, E_shared, k, static_cast<int>(F), ab};
+  hipError_t err = run_big_ffn<4>(a, s);
+  if (err != hipSuccess) return err;
+  return hipGetLastError();
+}
+
 hipError_t launch_expert_ffn(int64_t T, int64_t d, int E, int E_shared, int k, int64_t F,
                              bool bf16, const void* x_perm, const int32_t* offsets,
                              const void* x, const void* w1, const void* w3, const void* w2,
@@ -965,19 +1028,7 @@ hipError_t launch_expert_ffn(int64_t T, int64_t d, int E, int E_shared, int k, i
             static_cast<int>(T), static_cast<int>(d), E, E_shared, k, static_cast<int>(F)};
   const unsigned gx = static_cast<unsigned>(max_tiles(T, E, E_shared, k, BM));
   if (bf16 && BM == kBM2) {
-    const int nt1 = static_cast<int>((F + kBN2 / 2 - 1) / (kBN2 / 2));
-    const int nt2 = static_cast<int>((d + kBN2 - 1) / kBN2);
-    const int64_t mt = max_tiles(T, E, E_shared, k, kBM2);
-    // compute units of the current device: one large-tile block fits a CU
-    int dev = 0, ncu = 0;
-    hipError_t err = hipGetDevice(&dev);
-    if (err == hipSuccess)
-      err = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
-    if (err != hipSuccess) return err;
-    ncu = max(kXcds, min(ncu, kMaxCUs));
-    err = launch_gemm_big<1>(a, nt1, mt, ncu, s);
-    if (err != hipSuccess) return err;
-    err = launch_gemm_big<2>(a, nt2, mt, ncu, s);
+    hipError_t err = run_big_ffn<1>(a, s);
     if (err != hipSuccess) return err;
   } else if (bf16) {
     // Decode-sized: segments of at most kStreamMaxRows rows stream their
@@ -1052,8 +1103,8 @@ hipError_t launch_expert_ffn_backward(int64_t T, int64_t d, int E, int E_shared,
                                       const void* w2, const void* ws1, const void* ws3,
                                       const void* ws2, const void* dy_perm, void* dx_perm,
                                       void* dx_shared, float* dw1, float* dw3, float* dw2,
-                                      float* dws1, float* dws3, float* dws2, void* ws,
-                                      hipStream_t s) {
+                                      float* dws1, float* dws3, float* dws2, const void* ab,
+                                      void* ws, hipStream_t s) {
   const BwdLayout L = bwd_layout(T, d, E, E_shared, k, F);
   char* base = static_cast<char*>(ws);
   int* ntiles = reinterpret_cast<int*>(base);
@@ -1089,24 +1140,25 @@ hipError_t launch_expert_ffn_backward(int64_t T, int64_t d, int E, int E_shared,
     ok(launch_transpose_batched(ws1, w13t + 2 * E * wsz, E_shared, Fi, di, 2 * F, 0, s));
     ok(launch_transpose_batched(ws3, w13t + 2 * E * wsz, E_shared, Fi, di, 2 * F, Fi, s));
   }
-  int dev = 0, ncu = 0;
-  if (ok(hipGetDevice(&dev))) ok(hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev));
-  if (err != hipSuccess) return err;
-  ncu = max(kXcds, min(ncu, kMaxCUs));
+  int ncu = 0;
+  if (!ok(device_cus(&ncu))) return err;
   const int64_t mt = max_tiles(T, E, E_shared, k, kBM2);
   auto nt_of = [](int64_t n, int cols) { return static_cast<int>((n + cols - 1) / cols); };
-  // 1. recompute A = X W1^T and B = X W3^T into (A, B) rows of g13
-  FfnArgs a3{x_perm, x, offsets, w1, w3, w2, ws1, ws3, ws2, g13, nullptr, nullptr, tiles, ntiles,
-             sk_partial, sk_count, static_cast<int>(T), di, E, E_shared, k, Fi};
-  ok(launch_gemm_big<3>(a3, nt_of(F, kBN2 / 2), mt, ncu, s));
+  // 1. A = X W1^T and B = X W3^T: kept by the forward (ab), else recomputed
+  //    into the (A, B) rows of g13
+  if (ab == nullptr) {
+    FfnArgs a3{x_perm, x, offsets, w1, w3, w2, ws1, ws3, ws2, g13, nullptr, nullptr, tiles,
+               ntiles, sk_partial, sk_count, static_cast<int>(T), di, E, E_shared, k, Fi};
+    ok(launch_gemm_big<3>(a3, nt_of(F, kBN2 / 2), mt, ncu, s));
+  }
   // 2. dH = dO W2: the phase-2 form with K = d and N = F (W2^T rows)
   FfnArgs ah{nullptr, nullptr, offsets, nullptr, nullptr, w2t, nullptr, nullptr,
              w2t + E * wsz, const_cast<void*>(dy_perm), dh,
              static_cast<uint16_t*>(dh) + T * k * F, tiles, ntiles, sk_partial, sk_count,
              static_cast<int>(T), Fi, E, E_shared, k, di};
   ok(launch_gemm_big<2>(ah, nt_of(F, kBN2), mt, ncu, s));
-  // 3. (A, B), dH -> (dA, dB), H, in place
-  ok(launch_swiglu_bwd(g13, dh, offsets, E, T * k, L.rows, F, s));
+  // 3. (A, B), dH -> (dA, dB) in g13, H in place of dH
+  ok(launch_swiglu_bwd(ab != nullptr ? ab : g13, g13, dh, offsets, E, T * k, L.rows, F, s));
   // 4. dX = [dA dB] [W1; W3]: the phase-2 form with K = 2F and N = d
   FfnArgs ax{nullptr, nullptr, offsets, nullptr, nullptr, w13t, nullptr, nullptr,
              w13t + 2 * E * wsz, g13, dx_perm, dx_shared, tiles, ntiles, sk_partial, sk_count,

@@ -70,76 +70,135 @@ __global__ __launch_bounds__(kWave) void seg_info_kernel(const int32_t* __restri
   if (lane == kWave - 1) poff[nseg] = incl;
 }
 
+// 64 x 64 bf16 tile transpose through LDS, 256 threads.  Loads: 512
+// 16-byte chunks (row r, chunk cc), two per thread, stored with the chunk
+// index XOR-ed by r/8 so that the column reads below hit 64 distinct banks.
+// Then thread (rb = tid % 8, cp = tid / 8) reads the dwords (columns 2cp,
+// 2cp+1) of rows 8rb .. 8rb+7 and writes 16 bytes (8 rows) of output rows
+// 2cp and 2cp+1; eight consecutive lanes fill one 128-byte output run.
+struct TileT {
+  uint32_t w[kTile][kTile / 2];
+};
+
+__device__ __forceinline__ void tile_store_chunk(TileT& t, int r, int cc, const u32x4_t v) {
+  const int p = (cc ^ (r >> 3)) * 4;
+  *reinterpret_cast<u32x4_t*>(&t.w[r][p]) = v;
+}
+
+// The two output chunks of thread tid: rows 2cp and 2cp+1 of the
+// transposed tile, columns 8rb .. 8rb+7.
+__device__ __forceinline__ void tile_read_pair(const TileT& t, int tid, u32x4_t& o0, u32x4_t& o1) {
+  const int rb = tid & 7, cp = tid >> 3;
+  const int flip = (cp >> 2) & 1;               // half of the lanes start on odd rows
+  uint32_t D[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const int qq = q ^ flip;
+    const int r = rb * 8 + qq;
+    D[qq] = t.w[r][cp ^ (rb * 4)];
+  }
+  uint32_t a[4], b[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    a[j] = (D[2 * j] & 0xFFFFu) | (D[2 * j + 1] << 16);
+    b[j] = (D[2 * j] >> 16) | (D[2 * j + 1] & 0xFFFF0000u);
+  }
+  o0 = u32x4_t{a[0], a[1], a[2], a[3]};
+  o1 = u32x4_t{b[0], b[1], b[2], b[3]};
+}
+
 // dst[g][c][col0 + r] = src[g][r][c] for a batch of G matrices src [R][C]
-// (dst rows hold ld elements): the weights' transposes.
+// (dst rows hold ld elements): the weights' transposes.  R, C, ld and col0
+// are multiples of 64.
 __global__ __launch_bounds__(256) void transpose_batched_kernel(const uint16_t* __restrict__ src,
                                                                 uint16_t* __restrict__ dst,
                                                                 int R, int C, int64_t ld,
                                                                 int col0) {
-  __shared__ uint16_t tile[kTile][kTile + 2];
+  __shared__ TileT tile;
   const int g = blockIdx.z;
   const int r0 = blockIdx.y * kTile, c0 = blockIdx.x * kTile;
   const uint16_t* S = src + static_cast<int64_t>(g) * R * C;
   uint16_t* D = dst + static_cast<int64_t>(g) * C * ld;
-  const int tx = threadIdx.x % kTile, ty = threadIdx.x / kTile;   // 64 x 4
-  for (int i = ty; i < kTile; i += 4) {
-    const int r = r0 + i, c = c0 + tx;
-    if (r < R && c < C) tile[i][tx] = S[static_cast<int64_t>(r) * C + c];
+  const int tid = threadIdx.x;
+  u32x4_t v[2];
+#pragma unroll
+  for (int it = 0; it < 2; ++it) {
+    const int idx = tid + 256 * it, r = idx >> 3, cc = idx & 7;
+    v[it] = *reinterpret_cast<const u32x4_t*>(S + static_cast<int64_t>(r0 + r) * C + c0 + cc * 8);
+  }
+#pragma unroll
+  for (int it = 0; it < 2; ++it) {
+    const int idx = tid + 256 * it;
+    tile_store_chunk(tile, idx >> 3, idx & 7, v[it]);
   }
   __syncthreads();
-  for (int i = ty; i < kTile; i += 4) {
-    const int c = c0 + i, r = r0 + tx;
-    if (r < R && c < C) D[static_cast<int64_t>(c) * ld + col0 + r] = tile[tx][i];
-  }
+  u32x4_t o0, o1;
+  tile_read_pair(tile, tid, o0, o1);
+  const int rb = tid & 7, c = c0 + 2 * (tid >> 3);
+  uint16_t* out = D + static_cast<int64_t>(c) * ld + col0 + r0 + rb * 8;
+  *reinterpret_cast<u32x4_t*>(out) = o0;
+  *reinterpret_cast<u32x4_t*>(out + ld) = o1;
 }
 
 // K-major copy of H-indexed activations: dst[c][poff[s] + j] = row
 // hstart[s] + j of the source (column c), for j < nrows[s], and 0 up to the
 // next multiple of 64.  Routed rows come from src; shared rows from
 // src_shared[(row - T*k) mod T] when given (x), else from src (H-indexed).
+// C is a multiple of 64.
 __global__ __launch_bounds__(256) void transpose_seg_kernel(
     const uint16_t* __restrict__ src, const uint16_t* __restrict__ src_shared,
     uint16_t* __restrict__ dst, const int* __restrict__ poff, const int* __restrict__ hstart,
     const int* __restrict__ nrows, int C, int64_t ld, int E, int T, int k) {
-  __shared__ uint16_t tile[kTile][kTile + 2];
+  __shared__ TileT tile;
   const int s = blockIdx.z;
   const int n = nrows[s];
   const int npad = poff[s + 1] - poff[s];
   const int j0 = blockIdx.y * kTile, c0 = blockIdx.x * kTile;
   if (j0 >= npad) return;
   const int h = hstart[s];
-  const int tx = threadIdx.x % kTile, ty = threadIdx.x / kTile;
-  for (int i = ty; i < kTile; i += 4) {
-    const int j = j0 + i, c = c0 + tx;
-    uint16_t v = 0;
-    if (j < n && c < C) {
+  const int tid = threadIdx.x;
+  u32x4_t v[2];
+#pragma unroll
+  for (int it = 0; it < 2; ++it) {
+    const int idx = tid + 256 * it, j = j0 + (idx >> 3), cc = idx & 7;
+    v[it] = u32x4_t{0u, 0u, 0u, 0u};
+    if (j < n) {
       const int row = h + j;
       const uint16_t* S = (s >= E && src_shared != nullptr)
           ? src_shared + static_cast<int64_t>((row - T * k) % T) * C
           : src + static_cast<int64_t>(row) * C;
-      v = S[c];
+      v[it] = *reinterpret_cast<const u32x4_t*>(S + c0 + cc * 8);
     }
-    tile[i][tx] = v;
+  }
+#pragma unroll
+  for (int it = 0; it < 2; ++it) {
+    const int idx = tid + 256 * it;
+    tile_store_chunk(tile, idx >> 3, idx & 7, v[it]);
   }
   __syncthreads();
-  for (int i = ty; i < kTile; i += 4) {
-    const int c = c0 + i, j = j0 + tx;
-    if (c < C && j < npad) dst[static_cast<int64_t>(c) * ld + poff[s] + j] = tile[tx][i];
-  }
+  u32x4_t o0, o1;
+  tile_read_pair(tile, tid, o0, o1);
+  const int rb = tid & 7, c = c0 + 2 * (tid >> 3);
+  uint16_t* out = dst + static_cast<int64_t>(c) * ld + poff[s] + j0 + rb * 8;
+  *reinterpret_cast<u32x4_t*>(out) = o0;
+  *reinterpret_cast<u32x4_t*>(out + ld) = o1;
 }
 
-// In place, per valid H-indexed row (one block per row): g13 [2F] =
-// (A, B) -> (dA, dB) and dh [F] -> H = SiLU(A) (*) B.
-__global__ __launch_bounds__(256) void swiglu_bwd_kernel(uint16_t* __restrict__ g13,
+// Per valid H-indexed row (one block per row): (A, B) from ab [2F] and dH
+// from dh [F] give (dA, dB) in g13 [2F] and H = SiLU(A) (*) B in place of
+// dH.  ab may be g13 itself (each element is read before it is written, by
+// the same thread).
+__global__ __launch_bounds__(256) void swiglu_bwd_kernel(const uint16_t* ab, uint16_t* g13,
                                                          uint16_t* __restrict__ dh,
                                                          const int32_t* __restrict__ offsets,
                                                          int E, int64_t Tk, int F) {
   const int64_t row = blockIdx.x;
   if (row < Tk && row >= offsets[E]) return;     // routed rows past R are unused
+  const uint16_t* I = ab + row * 2 * F;
   uint16_t* G = g13 + row * 2 * F;
   uint16_t* D = dh + row * F;
   for (int f = threadIdx.x; f < F; f += blockDim.x) {
-    const float a = bf16_to_f32(G[f]), b = bf16_to_f32(G[F + f]), d = bf16_to_f32(D[f]);
+    const float a = bf16_to_f32(I[f]), b = bf16_to_f32(I[F + f]), d = bf16_to_f32(D[f]);
     const float sg = 1.0f / (1.0f + __expf(-a));
     const float s = a * sg;
     G[f] = f32_to_bf16(d * b * sg * (1.0f + a * (1.0f - sg)));
@@ -182,11 +241,11 @@ hipError_t launch_transpose_seg(const void* src, const void* src_shared, void* d
   return hipGetLastError();
 }
 
-hipError_t launch_swiglu_bwd(void* g13, void* dh, const int32_t* offsets, int E, int64_t Tk,
-                             int64_t rows_total, int64_t F, hipStream_t s) {
+hipError_t launch_swiglu_bwd(const void* ab, void* g13, void* dh, const int32_t* offsets, int E,
+                             int64_t Tk, int64_t rows_total, int64_t F, hipStream_t s) {
   hipLaunchKernelGGL(swiglu_bwd_kernel, dim3(static_cast<unsigned>(rows_total)), dim3(256), 0, s,
-                     static_cast<uint16_t*>(g13), static_cast<uint16_t*>(dh), offsets, E, Tk,
-                     static_cast<int>(F));
+                     static_cast<const uint16_t*>(ab), static_cast<uint16_t*>(g13),
+                     static_cast<uint16_t*>(dh), offsets, E, Tk, static_cast<int>(F));
   return hipGetLastError();
 }
 

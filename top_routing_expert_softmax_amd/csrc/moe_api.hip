@@ -303,7 +303,7 @@ int moe_backward_workspace_size(int64_t T, int64_t d_model, int32_t E, int32_t E
   REQUIRE(E_shared >= 0 && E_shared <= 16, "E_shared must be in [0, 16]");
   REQUIRE(bytes != nullptr, "bytes is NULL");
   *bytes = align256(std::max(moe::ffn_backward_workspace_bytes(T, d_model, E, E_shared, k, d_ff),
-                             moe::route_backward_workspace_bytes(T, E)));
+                             moe::route_backward_workspace_bytes(T, d_model, E)));
   return MOE_OK;
 }
 
@@ -336,7 +336,8 @@ int moe_expert_ffn_backward(int64_t T, int64_t d_model, int32_t E, int32_t E_sha
                             const void* w3, const void* w2, const void* ws1, const void* ws3,
                             const void* ws2, const void* dy_perm, void* dx_perm, void* dx_shared,
                             float* dw1, float* dw3, float* dw2, float* dws1, float* dws3,
-                            float* dws2, void* ws, size_t ws_bytes, void* stream) {
+                            float* dws2, const void* ab, void* ws, size_t ws_bytes,
+                            void* stream) {
   if (int r = check_common(T, E, k)) return r;
   if (int r = check_dim("d_model", d_model)) return r;
   if (int r = check_dim("d_ff", d_ff)) return r;
@@ -373,7 +374,7 @@ int moe_expert_ffn_backward(int64_t T, int64_t d_model, int32_t E, int32_t E_sha
   return launched(moe::launch_expert_ffn_backward(T, d_model, E, E_shared, k, d_ff, x_perm,
                                                   offsets, x, w1, w3, w2, ws1, ws3, ws2, dy_perm,
                                                   dx_perm, dx_shared, dw1, dw3, dw2, dws1, dws3,
-                                                  dws2, ws, static_cast<hipStream_t>(stream)),
+                                                  dws2, ab, ws, static_cast<hipStream_t>(stream)),
                   "moe_expert_ffn_backward");
 }
 
@@ -401,7 +402,7 @@ int moe_route_backward(int64_t T, int64_t d_model, int32_t E, int32_t E_shared, 
   REQUIRE_PTR(dw_gate);
   REQUIRE_PTR(ws);
   if (E_shared > 0) REQUIRE_PTR(dx_shared);
-  const size_t need = moe::route_backward_workspace_bytes(T, E);
+  const size_t need = moe::route_backward_workspace_bytes(T, d_model, E);
   if (ws_bytes < need)
     return fail(MOE_EWORKSPACE, "moe_route_backward needs %zu workspace bytes, got %zu", need,
                 ws_bytes);
@@ -539,6 +540,44 @@ int moe_expert_ffn(int64_t T, int64_t d_model, int32_t E, int32_t E_shared, int3
                                          x_perm, offsets, x, w1, w3, w2, ws1, ws3, ws2, y_perm,
                                          y_shared, ws, static_cast<hipStream_t>(stream)),
                   "moe_expert_ffn");
+}
+
+int moe_expert_ffn_train(int64_t T, int64_t d_model, int32_t E, int32_t E_shared, int32_t k,
+                         int64_t d_ff, int32_t dtype, const void* x_perm, const int32_t* offsets,
+                         const void* x, const void* w1, const void* w3, const void* w2,
+                         const void* ws1, const void* ws3, const void* ws2, void* y_perm,
+                         void* y_shared, void* ab, void* ws, size_t ws_bytes, void* stream) {
+  if (int r = check_common(T, E, k)) return r;
+  REQUIRE(dtype == MOE_BF16, "moe_expert_ffn_train runs in bf16 (dtype MOE_BF16)");
+  if (int r = check_dim("d_model", d_model)) return r;
+  if (int r = check_dim("d_ff", d_ff)) return r;
+  REQUIRE(E_shared >= 0 && E_shared <= 16, "E_shared must be in [0, 16]");
+  REQUIRE(T * k + static_cast<int64_t>(E_shared) * T < (int64_t(1) << 31),
+          "T*k + E_shared*T must be < 2^31");
+  REQUIRE_PTR(x_perm);
+  REQUIRE_PTR(offsets);
+  REQUIRE_PTR(w1);
+  REQUIRE_PTR(w3);
+  REQUIRE_PTR(w2);
+  REQUIRE_PTR(y_perm);
+  REQUIRE_PTR(ab);
+  REQUIRE_PTR(ws);
+  if (E_shared > 0) {
+    REQUIRE_PTR(x);
+    REQUIRE_PTR(ws1);
+    REQUIRE_PTR(ws3);
+    REQUIRE_PTR(ws2);
+    REQUIRE_PTR(y_shared);
+  }
+  const size_t need = moe::ffn_workspace_bytes(T, E, E_shared, k, d_ff, 2);
+  if (ws_bytes < need)
+    return fail(MOE_EWORKSPACE, "moe_expert_ffn_train needs %zu workspace bytes, got %zu", need,
+                ws_bytes);
+  (void)hipGetLastError();
+  return launched(moe::launch_expert_ffn_train(T, d_model, E, E_shared, k, d_ff, x_perm, offsets,
+                                               x, w1, w3, w2, ws1, ws3, ws2, y_perm, y_shared, ab,
+                                               ws, static_cast<hipStream_t>(stream)),
+                  "moe_expert_ffn_train");
 }
 
 int moe_combine(int64_t T, int64_t d_model, int32_t E_shared, int32_t k, int32_t dtype,

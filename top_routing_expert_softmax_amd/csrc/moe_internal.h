@@ -78,6 +78,14 @@ hipError_t launch_expert_ffn(int64_t T, int64_t d, int E, int E_shared, int k,
                              const void* ws1, const void* ws3, const void* ws2,
                              void* y_perm, void* y_shared, void* ws,
                              hipStream_t s);
+// The bf16 forward on the large tiles that also stores the pre-activations
+// A = X W1^T and B = X W3^T of every H row to ab [rows, 2F].
+hipError_t launch_expert_ffn_train(int64_t T, int64_t d, int E, int E_shared, int k, int64_t F,
+                                   const void* x_perm, const int32_t* offsets, const void* x,
+                                   const void* w1, const void* w3, const void* w2,
+                                   const void* ws1, const void* ws3, const void* ws2,
+                                   void* y_perm, void* y_shared, void* ab, void* ws,
+                                   hipStream_t s);
 
 // One phase (1: H = SiLU(X W1^T) * (X W3^T), 2: Y = H W2^T) of the
 // weight-streaming FFN over the segments with 1 .. kStreamMaxRows rows.
@@ -100,8 +108,8 @@ hipError_t launch_expert_ffn_backward(int64_t T, int64_t d, int E, int E_shared,
                                       const void* w2, const void* ws1, const void* ws3,
                                       const void* ws2, const void* dy_perm, void* dx_perm,
                                       void* dx_shared, float* dw1, float* dw3, float* dw2,
-                                      float* dws1, float* dws3, float* dws2, void* ws,
-                                      hipStream_t s);
+                                      float* dws1, float* dws3, float* dws2, const void* ab,
+                                      void* ws, hipStream_t s);
 hipError_t launch_seg_info(const int32_t* offsets, int* poff, int* hstart, int* nrows, int E,
                            int Es, int64_t T, int k, hipStream_t s);
 hipError_t launch_transpose_batched(const void* src, void* dst, int G, int R, int C, int64_t ld,
@@ -109,15 +117,15 @@ hipError_t launch_transpose_batched(const void* src, void* dst, int G, int R, in
 hipError_t launch_transpose_seg(const void* src, const void* src_shared, void* dst,
                                 const int* poff, const int* hstart, const int* nrows, int C,
                                 int64_t ld, int E, int Es, int64_t T, int k, hipStream_t s);
-hipError_t launch_swiglu_bwd(void* g13, void* dh, const int32_t* offsets, int E, int64_t Tk,
-                             int64_t rows_total, int64_t F, hipStream_t s);
+hipError_t launch_swiglu_bwd(const void* ab, void* g13, void* dh, const int32_t* offsets, int E,
+                             int64_t Tk, int64_t rows_total, int64_t F, hipStream_t s);
 
 // Combine and router backward (bwd.hip).
 hipError_t launch_combine_backward(int64_t T, int64_t d, int E_shared, int k, const void* dy,
                                    const void* y_perm, const int32_t* row_of_pair,
                                    const float* topk_w, void* dy_perm, float* dtopk_w,
                                    hipStream_t s);
-size_t route_backward_workspace_bytes(int64_t T, int E);
+size_t route_backward_workspace_bytes(int64_t T, int64_t d, int E);
 hipError_t launch_route_backward(int64_t T, int64_t d, int E, int E_shared, int k, const void* x,
                                  const void* w_gate, const float* logits,
                                  const int32_t* topk_idx, const float* topk_w,
