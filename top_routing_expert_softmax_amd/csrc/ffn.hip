@@ -80,6 +80,18 @@ struct FfnArgs {
 };
 
 // ---------------------------------------------------------------- tiling --
+//
+// A tile is (segment, first A row, rows, first H row).  Its x field also
+// carries the tile's row group: the large-tile kernel runs the row tiles of
+// one group against every column tile before the next group, so the blocks
+// an XCD holds at once share weight and activation tiles in its L2.  Groups
+// never cross a segment (an expert's weights are streamed once per group)
+// and hold at most kTileGroup row tiles: x = segment | size << 16 |
+// (index in the group) << 20.
+constexpr int kTileGroup = 8;
+__device__ __forceinline__ int tile_seg(int x) { return x & 0xFFFF; }
+__device__ __forceinline__ int tile_gsize(int x) { return (x >> 16) & 15; }
+__device__ __forceinline__ int tile_goff(int x) { return (x >> 20) & 15; }
 
 __global__ __launch_bounds__(kWave) void tile_table_kernel(const int32_t* __restrict__ offsets,
                                                           int4* __restrict__ tiles,
@@ -113,9 +125,19 @@ __global__ __launch_bounds__(kWave) void tile_table_kernel(const int32_t* __rest
 #pragma unroll
   for (int q = 0; q < 5; ++q) {
     const int s = lane * 5 + q;
+    // the segment's tiles form ng groups of at most kTileGroup, sizes as
+    // even as possible (the first rem groups one larger)
+    const int ng = (cnt[q] + kTileGroup - 1) / kTileGroup;
+    const int gs = ng > 0 ? cnt[q] / ng : 0, rem = ng > 0 ? cnt[q] % ng : 0;
+    int g_first = 0, g_size = gs + (rem > 0 ? 1 : 0), g_idx = 0;
     for (int i = 0; i < cnt[q]; ++i) {
+      if (i == g_first + g_size) {
+        g_first = i;
+        ++g_idx;
+        g_size = gs + (g_idx < rem ? 1 : 0);
+      }
       int4 t;
-      t.x = s;
+      t.x = s | (g_size << 16) | ((i - g_first) << 20);
       if (s < E) {
         const int r0 = offsets[s] + i * BM;
         t.y = r0;
@@ -145,7 +167,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(FfnArgs a) {
 
   if (static_cast<int>(blockIdx.x) >= *a.ntiles) return;
   const int4 tl = a.tiles[blockIdx.x];
-  const int seg = tl.x, arow0 = tl.y, mrows = tl.z, hrow0 = tl.w;
+  const int seg = tile_seg(tl.x), arow0 = tl.y, mrows = tl.z, hrow0 = tl.w;
   const bool routed = seg < a.E;
   const int e = routed ? seg : seg - a.E;
   // segments of at most kStreamMaxRows rows belong to the streaming kernels
@@ -303,8 +325,10 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(FfnArgs a) {
 //
 // Block order: a 1-D grid; each XCD (blocks are dealt to the 8 XCDs round
 // robin) takes a contiguous chunk of the live tiles, and inside a chunk
-// tiles run in groups of kGM row tiles x all column tiles, so concurrently
-// resident blocks of one XCD share A and B tiles in that XCD's L2.
+// tiles run by row group (at most kTileGroup row tiles of one segment) x all
+// column tiles, column by column, so concurrently resident blocks of one XCD
+// share A and B tiles in that XCD's L2, and an expert's weight tiles are
+// streamed once for all its row tiles rather than once per group it spans.
 #ifndef MOE_GEMM_BM
 #define MOE_GEMM_BM 256
 #endif
@@ -314,7 +338,6 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(FfnArgs a) {
 constexpr int kBM2 = MOE_GEMM_BM;   // rows per tile, large segments
 constexpr int kWM = MOE_GEMM_WM;    // wavefronts along M
 constexpr int kBN2 = 256;
-constexpr int kGM = 8;
 constexpr int kXcds = 8;
 
 template <int BKT, int BMT>
@@ -477,15 +500,17 @@ void gemm_big_kernel(FfnArgs a, int NT, int ncu) {
   const int parts = split_unit ? S : 1;         // whole tiles take all of K
   const int kb = part * nk_all / parts;
   const int nk = (part + 1) * nk_all / parts - kb;
-  const int group = pid / (kGM * NT);
-  const int first_m = group * kGM;
-  const int gm = min(kGM, MT - first_m);
-  const int in_group = pid - group * kGM * NT;
+  // pid / NT lies in pid's row group, since a group spans every column
+  const int mt0 = pid / NT;
+  const int gx = a.tiles[mt0].x;
+  const int first_m = mt0 - tile_goff(gx);
+  const int gm = tile_gsize(gx);
+  const int in_group = pid - first_m * NT;
   const int mt = first_m + in_group % gm;
   const int nt = in_group / gm;
 
   const int4 tl = a.tiles[mt];
-  const int seg = tl.x, arow0 = tl.y, mrows = tl.z, hrow0 = tl.w;
+  const int seg = tile_seg(tl.x), arow0 = tl.y, mrows = tl.z, hrow0 = tl.w;
   const bool routed = seg < a.E;
   const int e = routed ? seg : seg - a.E;
 
@@ -724,7 +749,7 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(FfnArgs a) {
   __shared__ float Bs[64][BKf + 1];
   if (static_cast<int>(blockIdx.x) >= *a.ntiles) return;
   const int4 tl = a.tiles[blockIdx.x];
-  const int seg = tl.x, arow0 = tl.y, mrows = tl.z, hrow0 = tl.w;
+  const int seg = tile_seg(tl.x), arow0 = tl.y, mrows = tl.z, hrow0 = tl.w;
   const bool routed = seg < a.E;
   const int e = routed ? seg : seg - a.E;
   const int tid = threadIdx.x;
