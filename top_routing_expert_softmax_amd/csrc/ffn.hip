@@ -77,6 +77,8 @@ struct FfnArgs {
   unsigned* sk_count;    // arrivals per split tile: [2][kMaxCUs], phase 1 then 2
   int T, d, E, Es, k, F;
   void* ab;              // PHASE 4: the pre-activations (A, B) as [rows, 2F]
+  int ksplit;            // PHASE 5: B rows k < ksplit come from w2 / ws2, the
+                         // rest from w3 / ws3 (row k - ksplit)
 };
 
 // ---------------------------------------------------------------- tiling --
@@ -365,19 +367,43 @@ __device__ __forceinline__ void lds_dma16(const void* gptr, uint32_t* lds_row_ba
 // loads and run the wave's MFMAs on them.  MIA (0..MI) is the number of
 // the wave's MI 32-row blocks that hold segment rows; the others take no
 // MFMA work.  Every wave of the block runs the same loads and barriers.
-template <int BKT, int BMT, int NST, int NIA, int NIB, int MI, int NB, int MIA>
+// B tile rows of an MN-contiguous operand: BKT rows (k) of kBN2 columns.
+constexpr int kBRowMN = kBN2 * 2;                       // bytes per LDS row
+
+// Two LDS transpose reads (4 x 16 bit each) make one 8-value MFMA operand.
+// In each group of 16 lanes, lane 4p+m receives in slot q element m of the
+// 8 bytes that lane 4q+p addresses; so with lane 4q+p pointing at row
+// k0+q, column n0+4p of an MN-contiguous tile, lane i gets column n0+i,
+// rows k0..k0+3.
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef short i16x8_t __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ bf16x8_t lds_read_tr_pair(const char* p, int second) {
+  typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
+  const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+  const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + second));
+  const i16x8_t v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8_t, v);
+}
+
+// BMN: the B operand is MN-contiguous (rows of k in global memory and in
+// LDS); slice k0 of B then starts k0 rows further on, and b_jump more
+// elements from b_kjump on (a second matrix continues the K range).
+template <int BKT, int BMT, int NST, int NIA, int NIB, int MI, int NB, int MIA, bool BMN>
 __device__ __forceinline__ void gemm_mainloop(
     f32x16_t (&acc)[MI][NB], const uint16_t* const (&asrc)[NIA],
     const uint16_t* const (&bsrc)[NIB], char* lds_bytes, int a_dst, int b_dst,
-    const int (&a_off)[MI], const int (&b_off)[NB], int lane, int nk) {
+    const int (&a_off)[MI], const int (&b_off)[NB], int lane, int nk, int64_t b_kstride,
+    int b_kjump, int64_t b_jump) {
   using G = SliceGeom<BKT, BMT>;
+#define MOE_BK(k0) (BMN ? static_cast<int64_t>(k0) * b_kstride + ((k0) >= b_kjump ? b_jump : 0) \
+                        : static_cast<int64_t>(k0))
 #define MOE_ISSUE_SLICE(slot, k0)                                                          \
   _Pragma("unroll") for (int i = 0; i < NIA; ++i)                                          \
     lds_dma16(asrc[i] + (k0), reinterpret_cast<uint32_t*>(                                \
                   lds_bytes + (slot) * G::STAGE + a_dst + i * G::RPI * G::ROW));          \
   _Pragma("unroll") for (int i = 0; i < NIB; ++i)                                          \
-    lds_dma16(bsrc[i] + (k0), reinterpret_cast<uint32_t*>(                                \
-                  lds_bytes + (slot) * G::STAGE + b_dst + i * G::RPI * G::ROW));
+    lds_dma16(bsrc[i] + MOE_BK(k0), reinterpret_cast<uint32_t*>(                          \
+                  lds_bytes + (slot) * G::STAGE + b_dst + i * 1024));
   // fragment rows are 32-aligned bases + lane%32, so the swizzle key of
   // all of this lane's fragment rows is ((lane % 32) / RPL) % CH
   const int key = ((lane & 31) / G::RPL) % G::CH;
@@ -396,6 +422,21 @@ __device__ __forceinline__ void gemm_mainloop(
     }
     __syncthreads();            // every wave's part of slice kt is in LDS, and
                                 // slot (kt-1) % NST is no longer read
+    // An MN-contiguous B is read with LDS transpose reads, which the
+    // compiler does not tell apart from the LDS-DMA writes in flight: it
+    // would wait for the next slice's loads before the first of them.  So
+    // the whole slice's B fragments are read here, before that DMA issue.
+    bf16x8_t fbs[BMN ? BKT / 16 : 1][NB];
+    if constexpr (BMN) {
+      if (MIA > 0) {
+        const char* sb = lds_bytes + slot * G::STAGE;
+#pragma unroll
+        for (int ks = 0; ks < BKT / 16; ++ks)
+#pragma unroll
+          for (int ni = 0; ni < NB; ++ni)
+            fbs[ks][ni] = lds_read_tr_pair(sb + b_off[ni] + ks * 16 * kBRowMN, 4 * kBRowMN);
+      }
+    }
 #if MOE_GEMM_UNCOND
     {
       // always issue (one block of code for the scheduler): past the last
@@ -421,7 +462,12 @@ __device__ __forceinline__ void gemm_mainloop(
 #pragma unroll
       for (int mi = 0; mi < MIA; ++mi) fa[mi] = *reinterpret_cast<const bf16x8_t*>(sb + a_off[mi] + pc);
 #pragma unroll
-      for (int ni = 0; ni < NB; ++ni) fb[ni] = *reinterpret_cast<const bf16x8_t*>(sb + b_off[ni] + pc);
+      for (int ni = 0; ni < NB; ++ni) {
+        if constexpr (BMN)
+          fb[ni] = fbs[ks][ni];
+        else
+          fb[ni] = *reinterpret_cast<const bf16x8_t*>(sb + b_off[ni] + pc);
+      }
 #pragma unroll
       for (int mi = 0; mi < MIA; ++mi)
 #pragma unroll
@@ -437,6 +483,7 @@ __device__ __forceinline__ void gemm_mainloop(
   wait_vmcnt<0>();              // the extra loads of the last iterations
 #endif
 #undef MOE_ISSUE_SLICE
+#undef MOE_BK
 }
 
 template <int PHASE, int BKT, int NST, int WAVES, int BMT, int WMW>
@@ -468,7 +515,10 @@ void gemm_big_kernel(FfnArgs a, int NT, int ncu) {
   // PHASE 3 is phase 1 with the gate and up products stored apart (the
   // recompute of the backward pass); PHASE 4 stores both H and the two
   // products (a forward that keeps what its backward needs)
-  constexpr bool P1 = PHASE != 2;
+  // PHASE 5 is the phase-2 form with an MN-contiguous B (the backward's
+  // dH = dO W2 and dX = [dA dB] [W1; W3] on the weights as stored)
+  constexpr bool P1 = PHASE == 1 || PHASE == 3 || PHASE == 4;
+  constexpr bool BMN = PHASE == 5;
   const int K = P1 ? a.d : a.F;
   const int nk_all = K / BKT;
   const int r = L % ncu;
@@ -539,21 +589,54 @@ void gemm_big_kernel(FfnArgs a, int NT, int ncu) {
     const int ra = r < mrows ? r : mrows - 1;
     asrc[i] = A + static_cast<int64_t>(ra) * K + kb * BKT + lchunk * 8;
   }
+  int64_t b_kstride = 1, b_jump = 0;
+  int b_kjump = 1 << 30;
+  if constexpr (BMN) {
+    // B tile: BKT rows of kBN2 columns, row k of B = row k of w2 (k <
+    // ksplit) or row k - ksplit of w3, each matrix ksplit x N per expert.
+    // An instruction covers two rows (32 chunks of 16 bytes each); lane l
+    // takes row r = wave * BKT/WAVES + 2i + l/32 and the logical chunk that
+    // sits at physical chunk l%32, chunks XOR-ed with 4 (r%4), so the
+    // transpose reads of four consecutive rows hit 64 distinct banks.
+    static_assert(NIB * 2 == BKT / WAVES, "MN-contiguous B rows per wave");
+    const int kabs = kb * BKT;
+    const bool second = kabs >= a.ksplit;
+    const uint16_t* W2s = static_cast<const uint16_t*>(routed ? a.w2 : a.ws2);
+    const uint16_t* W3s = static_cast<const uint16_t*>(routed ? a.w3 : a.ws3);
+    const int64_t wst = static_cast<int64_t>(a.ksplit) * N;
+    const uint16_t* W = (second ? W3s : W2s) + e * wst;
+    const int kbase = second ? kabs - a.ksplit : kabs;
 #pragma unroll
-  for (int i = 0; i < NIB; ++i) {
-    const int r = wave * BROWS + i * G::RPI + lane / G::CH;
-    const int lchunk = (lane % G::CH) ^ ((r / G::RPL) % G::CH);
-    int col;
-    const uint16_t* W;
-    if (P1) {
-      col = n0 + (r & 127);
-      W = static_cast<const uint16_t*>(r < 128 ? (routed ? a.w1 : a.ws1) : (routed ? a.w3 : a.ws3));
-    } else {
-      col = n0 + r;
-      W = static_cast<const uint16_t*>(routed ? a.w2 : a.ws2);
+    for (int i = 0; i < NIB; ++i) {
+      const int r = wave * (BKT / WAVES) + 2 * i + lane / 32;
+      const int lchunk = (lane % 32) ^ (4 * (r % 4));
+      int col = n0 + lchunk * 8;
+      col = col < N ? col : N - 8;
+      bsrc[i] = W + static_cast<int64_t>(kbase + r) * N + col;
     }
-    col = col < N ? col : N - 1;
-    bsrc[i] = W + e * wstride + static_cast<int64_t>(col) * K + kb * BKT + lchunk * 8;
+    b_kstride = N;
+    if (!second) {
+      b_kjump = a.ksplit - kabs;
+      b_jump = (reinterpret_cast<intptr_t>(W3s) - reinterpret_cast<intptr_t>(W2s)) / 2 -
+               static_cast<int64_t>(a.ksplit) * N;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < NIB; ++i) {
+      const int r = wave * BROWS + i * G::RPI + lane / G::CH;
+      const int lchunk = (lane % G::CH) ^ ((r / G::RPL) % G::CH);
+      int col;
+      const uint16_t* W;
+      if (P1) {
+        col = n0 + (r & 127);
+        W = static_cast<const uint16_t*>(r < 128 ? (routed ? a.w1 : a.ws1) : (routed ? a.w3 : a.ws3));
+      } else {
+        col = n0 + r;
+        W = static_cast<const uint16_t*>(routed ? a.w2 : a.ws2);
+      }
+      col = col < N ? col : N - 1;
+      bsrc[i] = W + e * wstride + static_cast<int64_t>(col) * K + kb * BKT + lchunk * 8;
+    }
   }
   char* lds_bytes = reinterpret_cast<char*>(lds);
   const int a_dst = wave * AROWS * G::ROW;
@@ -574,10 +657,19 @@ void gemm_big_kernel(FfnArgs a, int NT, int ncu) {
   for (int mi = 0; mi < MI; ++mi) a_off[mi] = (wm * WR + mi * 32 + (lane & 31)) * G::ROW;
 #pragma unroll
   for (int ni = 0; ni < NB; ++ni) {
-    const int r = P1
-        ? ((ni / (NB / 2)) * 128 + wn * (128 / WN) + (ni % (NB / 2)) * 32 + (lane & 31))
-        : (wn * (kBN2 / WN) + ni * 32 + (lane & 31));
-    b_off[ni] = BMT * G::ROW + r * G::ROW;
+    if constexpr (BMN) {
+      // transpose-read pointers: lane 16g + 4q + p addresses row
+      // 8 (g/2) + q, column nb + 16 (g%2) + 4p of the slice
+      const int g = lane / 16, q = (lane % 16) / 4, pp = lane % 4;
+      const int ncol = wn * (kBN2 / WN) + ni * 32 + 16 * (g % 2) + 4 * pp;
+      const int krow = 8 * (g / 2) + q;
+      b_off[ni] = BMT * G::ROW + krow * kBRowMN + (((ncol / 8) ^ (4 * q)) * 16) + (ncol % 8) * 2;
+    } else {
+      const int r = P1
+          ? ((ni / (NB / 2)) * 128 + wn * (128 / WN) + (ni % (NB / 2)) * 32 + (lane & 31))
+          : (wn * (kBN2 / WN) + ni * 32 + (lane & 31));
+      b_off[ni] = BMT * G::ROW + r * G::ROW;
+    }
   }
 
   // 32-row blocks of this wave's WR rows that hold segment rows: a tail
@@ -586,8 +678,9 @@ void gemm_big_kernel(FfnArgs a, int NT, int ncu) {
   const int mia = __builtin_amdgcn_readfirstlane(
       rows_w <= 0 ? 0 : (rows_w >= WR ? MI : (rows_w + 31) / 32));
 #define MOE_MAINLOOP(X)                                                                    \
-  gemm_mainloop<BKT, BMT, NST, NIA, NIB, MI, NB, (X)>(acc, asrc, bsrc, lds_bytes, a_dst,   \
-                                                      b_dst, a_off, b_off, lane, nk)
+  gemm_mainloop<BKT, BMT, NST, NIA, NIB, MI, NB, (X), BMN>(                                 \
+      acc, asrc, bsrc, lds_bytes, a_dst, b_dst, a_off, b_off, lane, nk, b_kstride, b_kjump,  \
+      b_jump)
   switch (mia) {
     case 4: if constexpr (MI >= 4) MOE_MAINLOOP(MI >= 4 ? 4 : 0); break;
     case 3: if constexpr (MI >= 3) MOE_MAINLOOP(MI >= 3 ? 3 : 0); break;
@@ -620,7 +713,7 @@ void gemm_big_kernel(FfnArgs a, int NT, int ncu) {
     __threadfence();
     __syncthreads();
     int* flag = reinterpret_cast<int*>(lds_bytes);
-    unsigned* count = &a.sk_count[(PHASE == 2 ? kMaxCUs : 0) + tile_sk];
+    unsigned* count = &a.sk_count[(P1 ? 0 : kMaxCUs) + tile_sk];
     if (tid == 0) {
       const bool last = atomicAdd(count, 1u) == static_cast<unsigned>(S - 1);
       // the last part leaves the counter at zero for the next launch
@@ -914,8 +1007,8 @@ void gemm_wgrad_kernel(WgradArgs a) {
   for (int ni = 0; ni < NB; ++ni)
     b_off[ni] = BMT * G::ROW + (wn * (kBN2 / WN) + ni * 32 + (lane & 31)) * G::ROW;
   if (nk > 0)
-    gemm_mainloop<BKT, BMT, NST, NIA, NIB, MI, NB, MI>(acc, asrc, bsrc, lds_bytes, a_dst, b_dst,
-                                                       a_off, b_off, lane, nk);
+    gemm_mainloop<BKT, BMT, NST, NIA, NIB, MI, NB, MI, false>(acc, asrc, bsrc, lds_bytes, a_dst, b_dst,
+                                                       a_off, b_off, lane, nk, 1, 1 << 30, 0);
   // (a segment with no rows stores zeros)
 #pragma unroll
   for (int ni = 0; ni < NB; ++ni) {
@@ -1086,11 +1179,10 @@ hipError_t launch_expert_ffn(int64_t T, int64_t d, int E, int E_shared, int k, i
 namespace {
 
 // Workspace of the backward, after the forward's tile table and split-K
-// region: segment info, transposed weights (W2^T per expert, [W1; W3]^T),
-// the recomputed (A, B) -> (dA, dB) buffer, dH -> H, and the K-major
-// copies of X, dO, H and (dA, dB) for the weight gradients.
+// region: segment info, the (A, B) -> (dA, dB) buffer, dH -> H, and the
+// K-major copies of X, dO, H and (dA, dB) for the weight gradients.
 struct BwdLayout {
-  size_t seg, w2t, w13t, g13, dh, xt, dot, ht, dabt, total;
+  size_t seg, g13, dh, xt, dot, ht, dabt, total;
   int64_t rows, ld;       // H-indexed rows; K-major row length (padded)
 };
 
@@ -1103,8 +1195,6 @@ BwdLayout bwd_layout(int64_t T, int64_t d, int E, int Es, int k, int64_t F) {
   const int G = E + Es;
   auto take = [&](size_t bytes) { const size_t p = at; at += align256(bytes); return p; };
   L.seg = take(3 * sizeof(int) * (G + 1));
-  L.w2t = take(static_cast<size_t>(G) * F * d * 2);
-  L.w13t = take(static_cast<size_t>(G) * d * 2 * F * 2);
   L.g13 = take(static_cast<size_t>(L.rows) * 2 * F * 2);
   L.dh = take(static_cast<size_t>(L.rows) * F * 2);
   L.xt = take(static_cast<size_t>(d) * L.ld * 2);
@@ -1143,11 +1233,8 @@ hipError_t launch_expert_ffn_backward(int64_t T, int64_t d, int E, int E_shared,
   int* poff = reinterpret_cast<int*>(base + L.seg);
   int* hstart = poff + (G + 1);
   int* nrows = hstart + (G + 1);
-  uint16_t* w2t = reinterpret_cast<uint16_t*>(base + L.w2t);
-  uint16_t* w13t = reinterpret_cast<uint16_t*>(base + L.w13t);
   void* g13 = base + L.g13;
   void* dh = base + L.dh;
-  const int64_t wsz = F * d;                     // elements of one expert matrix
   const int Fi = static_cast<int>(F), di = static_cast<int>(d);
 
   hipError_t err = hipSuccess;
@@ -1156,15 +1243,6 @@ hipError_t launch_expert_ffn_backward(int64_t T, int64_t d, int E, int E_shared,
   hipLaunchKernelGGL(tile_table_kernel, dim3(1), dim3(kWave), 0, s, offsets, tiles, ntiles, E,
                      E_shared, static_cast<int>(T), k, kBM2, sk_count);
   ok(launch_seg_info(offsets, poff, hstart, nrows, E, E_shared, T, k, s));
-  // transposed weights: W2^T [G][F][d]; [W1; W3]^T [G][d][2F]
-  ok(launch_transpose_batched(w2, w2t, E, di, Fi, d, 0, s));
-  ok(launch_transpose_batched(w1, w13t, E, Fi, di, 2 * F, 0, s));
-  ok(launch_transpose_batched(w3, w13t, E, Fi, di, 2 * F, Fi, s));
-  if (E_shared > 0) {
-    ok(launch_transpose_batched(ws2, w2t + E * wsz, E_shared, di, Fi, d, 0, s));
-    ok(launch_transpose_batched(ws1, w13t + 2 * E * wsz, E_shared, Fi, di, 2 * F, 0, s));
-    ok(launch_transpose_batched(ws3, w13t + 2 * E * wsz, E_shared, Fi, di, 2 * F, Fi, s));
-  }
   int ncu = 0;
   if (!ok(device_cus(&ncu))) return err;
   const int64_t mt = max_tiles(T, E, E_shared, k, kBM2);
@@ -1176,19 +1254,21 @@ hipError_t launch_expert_ffn_backward(int64_t T, int64_t d, int E, int E_shared,
                ntiles, sk_partial, sk_count, static_cast<int>(T), di, E, E_shared, k, Fi};
     ok(launch_gemm_big<3>(a3, nt_of(F, kBN2 / 2), mt, ncu, s));
   }
-  // 2. dH = dO W2: the phase-2 form with K = d and N = F (W2^T rows)
-  FfnArgs ah{nullptr, nullptr, offsets, nullptr, nullptr, w2t, nullptr, nullptr,
-             w2t + E * wsz, const_cast<void*>(dy_perm), dh,
-             static_cast<uint16_t*>(dh) + T * k * F, tiles, ntiles, sk_partial, sk_count,
-             static_cast<int>(T), Fi, E, E_shared, k, di};
-  ok(launch_gemm_big<2>(ah, nt_of(F, kBN2), mt, ncu, s));
+  // 2. dH = dO W2: the phase-2 form with K = d and N = F, reading the
+  //    rows of W2 [d, F] as stored (PHASE 5)
+  FfnArgs ah{nullptr, nullptr, offsets, nullptr, w2, w2, nullptr, ws2, ws2,
+             const_cast<void*>(dy_perm), dh, static_cast<uint16_t*>(dh) + T * k * F, tiles,
+             ntiles, sk_partial, sk_count, static_cast<int>(T), Fi, E, E_shared, k, di,
+             nullptr, di};
+  ok(launch_gemm_big<5>(ah, nt_of(F, kBN2), mt, ncu, s));
   // 3. (A, B), dH -> (dA, dB) in g13, H in place of dH
   ok(launch_swiglu_bwd(ab != nullptr ? ab : g13, g13, dh, offsets, E, T * k, L.rows, F, s));
-  // 4. dX = [dA dB] [W1; W3]: the phase-2 form with K = 2F and N = d
-  FfnArgs ax{nullptr, nullptr, offsets, nullptr, nullptr, w13t, nullptr, nullptr,
-             w13t + 2 * E * wsz, g13, dx_perm, dx_shared, tiles, ntiles, sk_partial, sk_count,
-             static_cast<int>(T), di, E, E_shared, k, 2 * Fi};
-  ok(launch_gemm_big<2>(ax, nt_of(d, kBN2), mt, ncu, s));
+  // 4. dX = [dA dB] [W1; W3]: the phase-2 form with K = 2F and N = d, B
+  //    rows from W1 [F, d] then W3 [F, d] as stored (PHASE 5)
+  FfnArgs ax{nullptr, nullptr, offsets, nullptr, w3, w1, nullptr, ws3, ws1, g13, dx_perm,
+             dx_shared, tiles, ntiles, sk_partial, sk_count, static_cast<int>(T), di, E,
+             E_shared, k, 2 * Fi, nullptr, Fi};
+  ok(launch_gemm_big<5>(ax, nt_of(d, kBN2), mt, ncu, s));
   // 5. K-major copies for the weight gradients
   uint16_t* xt = reinterpret_cast<uint16_t*>(base + L.xt);
   uint16_t* dot = reinterpret_cast<uint16_t*>(base + L.dot);

@@ -1,7 +1,6 @@
 // Helpers of the expert-FFN backward pass (bf16): segment offsets, the
-// transposes that put every GEMM of the backward in the "both operands
-// K-contiguous" form of the forward kernel, and the elementwise SwiGLU
-// step.
+// K-major copies of the activations for the weight-gradient GEMMs, and the
+// elementwise SwiGLU step.
 //
 // For one expert with rows X (the gathered tokens), A = X W1^T, B = X W3^T,
 // H = SiLU(A) (*) B, O = H W2^T, and output gradient dO:
@@ -107,39 +106,6 @@ __device__ __forceinline__ void tile_read_pair(const TileT& t, int tid, u32x4_t&
   o1 = u32x4_t{b[0], b[1], b[2], b[3]};
 }
 
-// dst[g][c][col0 + r] = src[g][r][c] for a batch of G matrices src [R][C]
-// (dst rows hold ld elements): the weights' transposes.  R, C, ld and col0
-// are multiples of 64.
-__global__ __launch_bounds__(256) void transpose_batched_kernel(const uint16_t* __restrict__ src,
-                                                                uint16_t* __restrict__ dst,
-                                                                int R, int C, int64_t ld,
-                                                                int col0) {
-  __shared__ TileT tile;
-  const int g = blockIdx.z;
-  const int r0 = blockIdx.y * kTile, c0 = blockIdx.x * kTile;
-  const uint16_t* S = src + static_cast<int64_t>(g) * R * C;
-  uint16_t* D = dst + static_cast<int64_t>(g) * C * ld;
-  const int tid = threadIdx.x;
-  u32x4_t v[2];
-#pragma unroll
-  for (int it = 0; it < 2; ++it) {
-    const int idx = tid + 256 * it, r = idx >> 3, cc = idx & 7;
-    v[it] = *reinterpret_cast<const u32x4_t*>(S + static_cast<int64_t>(r0 + r) * C + c0 + cc * 8);
-  }
-#pragma unroll
-  for (int it = 0; it < 2; ++it) {
-    const int idx = tid + 256 * it;
-    tile_store_chunk(tile, idx >> 3, idx & 7, v[it]);
-  }
-  __syncthreads();
-  u32x4_t o0, o1;
-  tile_read_pair(tile, tid, o0, o1);
-  const int rb = tid & 7, c = c0 + 2 * (tid >> 3);
-  uint16_t* out = D + static_cast<int64_t>(c) * ld + col0 + r0 + rb * 8;
-  *reinterpret_cast<u32x4_t*>(out) = o0;
-  *reinterpret_cast<u32x4_t*>(out + ld) = o1;
-}
-
 // K-major copy of H-indexed activations: dst[c][poff[s] + j] = row
 // hstart[s] + j of the source (column c), for j < nrows[s], and 0 up to the
 // next multiple of 64.  Routed rows come from src; shared rows from
@@ -213,17 +179,6 @@ hipError_t launch_seg_info(const int32_t* offsets, int* poff, int* hstart, int* 
                            int Es, int64_t T, int k, hipStream_t s) {
   hipLaunchKernelGGL(seg_info_kernel, dim3(1), dim3(kWave), 0, s, offsets, poff, hstart, nrows,
                      E, Es, static_cast<int>(T), k);
-  return hipGetLastError();
-}
-
-hipError_t launch_transpose_batched(const void* src, void* dst, int G, int R, int C, int64_t ld,
-                                    int col0, hipStream_t s) {
-  if (G == 0) return hipSuccess;
-  const dim3 grid(static_cast<unsigned>((C + kTile - 1) / kTile),
-                  static_cast<unsigned>((R + kTile - 1) / kTile), static_cast<unsigned>(G));
-  hipLaunchKernelGGL(transpose_batched_kernel, grid, dim3(256), 0, s,
-                     static_cast<const uint16_t*>(src), static_cast<uint16_t*>(dst), R, C, ld,
-                     col0);
   return hipGetLastError();
 }
 

@@ -112,8 +112,6 @@ hipError_t launch_expert_ffn_backward(int64_t T, int64_t d, int E, int E_shared,
                                       void* ws, hipStream_t s);
 hipError_t launch_seg_info(const int32_t* offsets, int* poff, int* hstart, int* nrows, int E,
                            int Es, int64_t T, int k, hipStream_t s);
-hipError_t launch_transpose_batched(const void* src, void* dst, int G, int R, int C, int64_t ld,
-                                    int col0, hipStream_t s);
 hipError_t launch_transpose_seg(const void* src, const void* src_shared, void* dst,
                                 const int* poff, const int* hstart, const int* nrows, int C,
                                 int64_t ld, int E, int Es, int64_t T, int k, hipStream_t s);
