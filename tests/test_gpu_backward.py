@@ -141,6 +141,18 @@ def test_training_forward_keeps_preactivations(shape):
             assert torch.equal(g1[3][m], g0[3][m]), f"shared weight gradient {m} differs"
 
 
+@pytest.mark.parametrize("name,shape,save_ab", [
+    # heavily skewed router: three experts with no rows, 114 of 192 pairs dropped
+    ("skewed_train", dict(T=96, d_model=128, E=16, E_shared=0, k=2, d_ff=192, CF=1.0), True),
+    # decode-sized, two shared experts, no capacity limit
+    ("dsmoe16b_prefill", dict(T=40, d_model=192, E=16, E_shared=2, k=4, d_ff=128, CF=None), True),
+    # top-1: the selected softmax is 1, so only the balance and z terms reach g
+    ("mixtral_prefill", dict(T=200, d_model=256, E=8, k=1, d_ff=320, CF=1.0), False),
+])
+def test_backward_edge_shapes(name, shape, save_ab):
+    _backward_case(get_config(name, **shape), alpha=0.05, beta=0.01, save_ab=save_ab)
+
+
 def test_backward_mid_size():
     cfg = get_config("mixtral_prefill", T=1024, d_model=1024, E=8, k=2, d_ff=2048, CF=1.25)
     _backward_case(cfg, alpha=0.01, beta=0.001)
