@@ -149,3 +149,61 @@ def test_full_size_config(name):
     ref = H.oracle_y(inp, r, disp, tokens)
     mx, mr = H.check_y(cfg, g["y"][tokens], ref)
     H.log(f"{name}: R={R} drop={stats['drop_rate']:.4f} max_err={mx:.2e} mean_rel={mr:.2e}")
+
+
+@pytest.mark.parametrize("d_model,d_ff", [(512, 384), (2048, 1024), (1024, 2048)])
+def test_expert_ffn_segments_with_short_remainders(d_model, d_ff):
+    """moe_expert_ffn on expert segments of 257, 288, 289, 272, 256, 528 and
+    0 rows and a 280-row shared expert: each segment ends in a short row tile
+    (1, 32, 33, 16 and 24 rows) or exactly on a 256-row boundary, and an empty
+    segment takes no tile.  (2048, 1024) splits phase 1 in K, (1024, 2048)
+    phase 2, with short tiles among the split ones.  Every row against the
+    oracle's SwiGLU expert; moe_expert_ffn_train gives the same bits and its
+    A, B match the oracle."""
+    import top_routing_expert_softmax_amd as M
+    from oracle import moe_oracle as O
+    counts = [257, 288, 289, 272, 256, 528, 0]
+    T, k = 280, 7
+    cfg = get_config("dsmoe16b_prefill", T=T, d_model=d_model, E=len(counts), E_shared=1, k=k,
+                     d_ff=d_ff, CF=None)
+    H.log(f"short remainders: {cfg}")
+    inp = H.LayerInputs(cfg)
+    dd = inp.dev
+    R = sum(counts)
+    src = np.arange(R) % T                       # x_perm row r copies token r mod T
+    xp = torch.zeros((T * k, d_model), dtype=torch.bfloat16, device="cuda")
+    xp[:R] = inp.x_dev[torch.from_numpy(src).cuda()]
+    offs = torch.tensor(np.concatenate([[0], np.cumsum(counts)]), dtype=torch.int32,
+                        device="cuda")
+    E, F = len(counts), d_ff
+    ws = torch.empty(M.moe_workspace_size(T, d_model, E, 1, k, F, torch.bfloat16),
+                     dtype=torch.uint8, device="cuda")
+    yp = torch.empty((T * k, d_model), dtype=torch.bfloat16, device="cuda")
+    ysh = torch.empty((1, T, d_model), dtype=torch.bfloat16, device="cuda")
+    M.moe_expert_ffn(T, k, xp, offs, inp.x_dev, dd["w1"], dd["w3"], dd["w2"], dd["ws1"],
+                     dd["ws3"], dd["ws2"], yp, ysh, ws)
+    yp2, ysh2 = torch.empty_like(yp), torch.empty_like(ysh)
+    ab = torch.empty((T * k + T, 2 * F), dtype=torch.bfloat16, device="cuda")
+    M.moe_expert_ffn_train(T, k, xp, offs, inp.x_dev, dd["w1"], dd["w3"], dd["w2"], dd["ws1"],
+                           dd["ws3"], dd["ws2"], yp2, ysh2, ab, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(yp[:R], yp2[:R]) and torch.equal(ysh, ysh2)
+    x64 = inp.x.astype(np.float64)
+    got_y, ref_y, got_ab, ref_ab = [], [], [], []
+    o = np.concatenate([[0], np.cumsum(counts)])
+    for e in range(E):
+        w1, w3, w2 = inp.load_routed(e)
+        xr = x64[src[o[e]:o[e + 1]]]
+        got_y.append(yp[o[e]:o[e + 1]].float().cpu().numpy())
+        ref_y.append(O.swiglu_expert(xr, w1, w3, w2))
+        got_ab.append(ab[o[e]:o[e + 1]].float().cpu().numpy())
+        ref_ab.append(np.concatenate([xr @ w1.T, xr @ w3.T], axis=1))
+    s1, s3, s2 = (a.astype(np.float64) for a in inp.load_shared(0))
+    got_y.append(ysh[0].float().cpu().numpy())
+    ref_y.append(O.swiglu_expert(x64, s1, s3, s2))
+    got_ab.append(ab[T * k:].float().cpu().numpy())
+    ref_ab.append(np.concatenate([x64 @ s1.T, x64 @ s3.T], axis=1))
+    mx, mr = H.check_y(cfg, np.concatenate(got_y), np.concatenate(ref_y))
+    H.log(f"  y: max_err={mx:.2e} mean_rel={mr:.2e}")
+    mx, mr = H.check_y(cfg, np.concatenate(got_ab), np.concatenate(ref_ab))
+    H.log(f"  A, B: max_err={mx:.2e} mean_rel={mr:.2e}")
