@@ -386,9 +386,12 @@ def main():
     # counters were taken with the softmax router (the routing decides the rows)
     roof["traffic"] = (MEASURED_TRAFFIC.get((cfg.name, src_hash))
                        if args.router == "softmax" and fp8 is None else None)
-    roof["kernel"] = ("moe_expert_ffn (grouped GEMM phase 1 + phase 2 + tile table)"
-                      if fp8 is None else
-                      "moe_expert_ffn_fp8 (weight streaming of E4M3 codes, phase 1 + phase 2)")
+    if fp8 is not None:
+        roof["kernel"] = "moe_expert_ffn_fp8 (weight streaming of E4M3 codes, phase 1 + phase 2)"
+    elif roof["bound"] == "hbm":
+        roof["kernel"] = "moe_expert_ffn (weight streaming of bf16 weights, phase 1 + phase 2)"
+    else:
+        roof["kernel"] = "moe_expert_ffn (grouped GEMM phase 1 + phase 2 + tile table)"
     if bwd is not None:
         roof["kernel"] = ("moe_expert_ffn_backward (dH, dX, weight gradients, transposes; "
                           "pre-activations kept by the forward)")
