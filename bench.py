@@ -37,8 +37,8 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 # they were taken with (softmax router).  A changed
 # kernel reports null until it is measured again.
 MEASURED_TRAFFIC = {
-    ("mixtral_prefill", "97831a2f636f9ca7"): 9.4121e9,
-    ("dsv3_decode", "97831a2f636f9ca7"): 1.9664e10,
+    ("mixtral_prefill", "2823e2a75294dd98"): 9.4726e9,
+    ("dsv3_decode", "2823e2a75294dd98"): 1.9663e10,
 }
 
 

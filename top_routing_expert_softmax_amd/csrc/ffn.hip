@@ -44,20 +44,6 @@ constexpr int kMaxSplit = 4;
 constexpr int kMinSplitSlices = 16;
 constexpr int kMaxCUs = 256;
 
-// K-slice depth and LDS ring length of the large-tile bf16 kernel.
-#ifndef MOE_GEMM_BK
-#define MOE_GEMM_BK 64
-#endif
-#ifndef MOE_GEMM_NST
-#define MOE_GEMM_NST 2
-#endif
-#ifndef MOE_GEMM_UNCOND
-#define MOE_GEMM_UNCOND 1
-#endif
-#ifndef MOE_GEMM_PRIO
-#define MOE_GEMM_PRIO 1
-#endif
-
 struct FfnArgs {
   const void* x_perm;
   const void* x;
@@ -331,14 +317,8 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(FfnArgs a) {
 // column tiles, column by column, so concurrently resident blocks of one XCD
 // share A and B tiles in that XCD's L2, and an expert's weight tiles are
 // streamed once for all its row tiles rather than once per group it spans.
-#ifndef MOE_GEMM_BM
-#define MOE_GEMM_BM 256
-#endif
-#ifndef MOE_GEMM_WM
-#define MOE_GEMM_WM 2
-#endif
-constexpr int kBM2 = MOE_GEMM_BM;   // rows per tile, large segments
-constexpr int kWM = MOE_GEMM_WM;    // wavefronts along M
+constexpr int kBM2 = 256;           // rows per tile, large segments
+constexpr int kWM = 2;              // wavefronts along M
 constexpr int kBN2 = 256;
 constexpr int kXcds = 8;
 
@@ -437,24 +417,15 @@ __device__ __forceinline__ void gemm_mainloop(
             fbs[ks][ni] = lds_read_tr_pair(sb + b_off[ni] + ks * 16 * kBRowMN, 4 * kBRowMN);
       }
     }
-#if MOE_GEMM_UNCOND
     {
       // always issue (one block of code for the scheduler): past the last
       // slice, reload the last slice into the free slot
       const int s_next = kt + NST - 1;
       MOE_ISSUE_SLICE(s_next % NST, min(s_next, nk - 1) * BKT);
     }
-#else
-    if (kt + NST - 1 < nk) {
-      const int s_next = kt + NST - 1;
-      MOE_ISSUE_SLICE(s_next % NST, s_next * BKT);
-    }
-#endif
     if (MIA == 0) continue;
     const char* sb = lds_bytes + slot * G::STAGE;
-#if MOE_GEMM_PRIO
-    __builtin_amdgcn_s_setprio(1);
-#endif
+    __builtin_amdgcn_s_setprio(1);       // the MFMA issue ahead of other waves' loads
 #pragma unroll
     for (int ks = 0; ks < BKT / 16; ++ks) {
       const int pc = ((2 * ks + khalf) ^ key) * 16;
@@ -475,13 +446,9 @@ __device__ __forceinline__ void gemm_mainloop(
           acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[mi], fb[ni], acc[mi][ni], 0, 0, 0);
       __builtin_amdgcn_iglp_opt(0);
     }
-#if MOE_GEMM_PRIO
     __builtin_amdgcn_s_setprio(0);
-#endif
   }
-#if MOE_GEMM_UNCOND
   wait_vmcnt<0>();              // the extra loads of the last iterations
-#endif
 #undef MOE_ISSUE_SLICE
 #undef MOE_BK
 }
@@ -803,14 +770,11 @@ void gemm_big_kernel(FfnArgs a, int NT, int ncu) {
   }
 }
 
-// The configuration the library launches.
-constexpr int kBKsel = MOE_GEMM_BK;
-constexpr int kNSTsel = MOE_GEMM_NST;
-
-#ifndef MOE_GEMM_WAVES
-#define MOE_GEMM_WAVES 8
-#endif
-constexpr int kWavesSel = MOE_GEMM_WAVES;
+// The configuration the library launches: K slices of 64, a ring of two
+// slices in LDS, eight wavefronts.
+constexpr int kBKsel = 64;
+constexpr int kNSTsel = 2;
+constexpr int kWavesSel = 8;
 
 template <int PHASE>
 hipError_t launch_gemm_big(const FfnArgs& a, int nt, int64_t mt, int ncu, hipStream_t s) {

@@ -38,32 +38,9 @@ namespace {
 
 constexpr int kSWaves = 4;               // waves per block (K quarters)
 constexpr int kSNB = 2;                  // 16-row weight fragments per K step (bf16)
-#ifndef MOE_STREAM_NB8
-#define MOE_STREAM_NB8 4
-#endif
-#ifndef MOE_STREAM_U8
-#define MOE_STREAM_U8 2
-#endif
-constexpr int kSNB8 = MOE_STREAM_NB8;    // fragments per K step (FP8): half gate, half up
-
-#ifndef MOE_STREAM_NT
-#define MOE_STREAM_NT 0
-#endif
-#ifndef MOE_STREAM_U
-#define MOE_STREAM_U 4
-#endif
-#ifndef MOE_STREAM_PIPE
-#define MOE_STREAM_PIPE 1
-#endif
-
-template <typename V>
-__device__ __forceinline__ V wload(const V* p) {
-#if MOE_STREAM_NT
-  return __builtin_nontemporal_load(p);
-#else
-  return *p;
-#endif
-}
+constexpr int kSNB8 = 4;                 // fragments per K step (FP8): half gate, half up
+constexpr int kSU = 4;                   // 32-wide K steps per load batch (bf16, 16 tokens)
+constexpr int kSU8 = 2;                  // 64-wide K steps per load batch (FP8, 16 tokens)
 
 struct StreamArgs {
   const void* x_perm;
@@ -168,7 +145,7 @@ __device__ __forceinline__ void stream_finish(const StreamArgs& a, f32x4_t (&acc
 template <int PHASE, int TG>
 __device__ __forceinline__ void stream_block(const StreamArgs& a, int seg, int rows, int arow0,
                                              int hrow0, float* red) {
-  constexpr int U = TG == 1 ? MOE_STREAM_U : (TG == 2 ? (MOE_STREAM_U + 1) / 2 : 1);
+  constexpr int U = TG == 1 ? kSU : (TG == 2 ? (kSU + 1) / 2 : 1);
   const bool routed = seg < a.E;
   const int e = routed ? seg : seg - a.E;
   const int lane = threadIdx.x & (kWave - 1);
@@ -218,7 +195,7 @@ __device__ __forceinline__ void stream_block(const StreamArgs& a, int seg, int r
   _Pragma("unroll") for (int u = 0; u < U; ++u) {                                         \
     const int kk = ((S0) + u) * 32 + kq;                                                  \
     _Pragma("unroll") for (int b = 0; b < kSNB; ++b)                                      \
-      FB[u][b] = wload(reinterpret_cast<const bf16x8_t*>(wrow[b] + kk));                  \
+      FB[u][b] = *reinterpret_cast<const bf16x8_t*>(wrow[b] + kk);                        \
     _Pragma("unroll") for (int tg = 0; tg < TG; ++tg)                                     \
       FA[u][tg] = *reinterpret_cast<const bf16x8_t*>(arow[tg] + kk);                      \
   }
@@ -227,7 +204,6 @@ __device__ __forceinline__ void stream_block(const StreamArgs& a, int seg, int r
     _Pragma("unroll") for (int tg = 0; tg < TG; ++tg)                                     \
       _Pragma("unroll") for (int b = 0; b < kSNB; ++b)                                    \
         acc[tg][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(FA[u][tg], FB[u][b], acc[tg][b], 0, 0, 0);
-#if MOE_STREAM_PIPE
   if (s + 2 * U <= s1) {
     // two batches in flight: load batch i+1, then use batch i
     bf16x8_t fa0[U][TG], fb0[U][kSNB], fa1[U][TG], fb1[U][kSNB];
@@ -241,7 +217,6 @@ __device__ __forceinline__ void stream_block(const StreamArgs& a, int seg, int r
     }
     MOE_SMFMA(fa0, fb0);
   }
-#endif
   for (; s + U <= s1; s += U) {
     bf16x8_t fa[U][TG], fb[U][kSNB];
     MOE_SLOAD(fa, fb, s);
@@ -254,7 +229,7 @@ __device__ __forceinline__ void stream_block(const StreamArgs& a, int seg, int r
     bf16x8_t fb[kSNB], fa[TG];
 #pragma unroll
     for (int b = 0; b < kSNB; ++b)
-      fb[b] = wload(reinterpret_cast<const bf16x8_t*>(wrow[b] + kk));
+      fb[b] = *reinterpret_cast<const bf16x8_t*>(wrow[b] + kk);
 #pragma unroll
     for (int tg = 0; tg < TG; ++tg) fa[tg] = *reinterpret_cast<const bf16x8_t*>(arow[tg] + kk);
 #pragma unroll
@@ -272,7 +247,7 @@ template <int PHASE, int TG>
 __device__ __forceinline__ void stream_block_fp8(const StreamArgs& a, int seg, int rows,
                                                  int arow0, int hrow0, float* red) {
   constexpr int NB = kSNB8;
-  constexpr int U = TG == 1 ? MOE_STREAM_U8 : 1;     // 64-wide K steps per batch
+  constexpr int U = TG == 1 ? kSU8 : 1;              // 64-wide K steps per batch
   const bool routed = seg < a.E;
   const int e = routed ? seg : seg - a.E;
   const int lane = threadIdx.x & (kWave - 1);

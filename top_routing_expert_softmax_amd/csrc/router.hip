@@ -39,9 +39,7 @@ namespace {
 constexpr int kTW = 8;          // tokens per block
 constexpr int kMaxWavesR = 8;   // waves per block at most
 constexpr int kMaxSplits = 64;  // d-splits at most (decode)
-#ifndef MOE_ROUTER_SPLIT_BLOCKS
-#define MOE_ROUTER_SPLIT_BLOCKS 256  // blocks the d-split aims for
-#endif
+constexpr int kRouterSplitBlocks = 256;   // blocks the d-split aims for
 
 }  // namespace
 
@@ -382,7 +380,7 @@ RouterPlan plan_router(int64_t T, int64_t d, int E) {
   // the chip (each split keeps at least one chunk per ds lane)
   p.S = 1;
   if (p.nblocks < 128) {
-    p.S = (MOE_ROUTER_SPLIT_BLOCKS + p.nblocks - 1) / p.nblocks;
+    p.S = (kRouterSplitBlocks + p.nblocks - 1) / p.nblocks;
     p.S = std::min(p.S, kMaxSplits);
     p.S = std::min(p.S, std::max(1, p.nchunk / p.DS));
   }
