@@ -6,9 +6,9 @@
 // token computes softmax and log-sum-exp in fp32 (each lane holds up to four
 // logits), and fp64 per-lane accumulators collect sum_t p_ti and sum_t lse^2.
 // The block folds its four waves in a fixed order into one partial row.
-// Pass 2: one block adds the partial rows and forms f, P, L_balance, z and
-// the drop rate in fp64, always in the same order (the result is
-// deterministic).
+// Pass 2: one block adds the partial rows (spread over all its threads
+// whatever E is) and forms f, P, L_balance, z and the drop rate in fp64,
+// always in the same order (the result is deterministic).
 #include <math.h>
 
 #include "moe_device.h"
@@ -75,49 +75,62 @@ __global__ __launch_bounds__(kWavesS * kWave) void stats_partial_kernel(
   }
 }
 
-// 1024 threads: thread (j, e) with j = tid / 256 sums partial rows
-// b = j, j+4, j+8, ... of expert e into eight fixed accumulators; the four
-// j-sums and the accumulators are combined in a fixed order.
+// 1024 threads: with EP = E rounded up to a power of two (at most 256) and
+// G = 1024 / EP groups, thread (g, e) = (tid / EP, tid % EP) sums the
+// partial rows b = g, g + G, g + 2G, ... of expert e into eight fixed
+// accumulators (its loads all issued before the adds), and the G group
+// sums are folded in a fixed tree, so the result does not depend on
+// scheduling.
 __global__ __launch_bounds__(1024) void stats_final_kernel(
     const double* __restrict__ part_P, const double* __restrict__ part_z,
     const int32_t* __restrict__ counts, float* __restrict__ f, float* __restrict__ P,
-    double* __restrict__ scalars, int nblk, int nT, int E, int k, int cap) {
-  __shared__ double sj[4][256];
-  __shared__ double zj[4];
+    double* __restrict__ scalars, int nblk, int nT, int E, int k, int cap, int EP) {
+  __shared__ double sj[1024];
+  __shared__ double zj[1024];
   __shared__ double fp[256];
   __shared__ double dr[256];
-  const int e = threadIdx.x & 255;
-  const int j = threadIdx.x >> 8;
+  const int G = 1024 / EP;
+  const int e = threadIdx.x % EP;
+  const int g = threadIdx.x / EP;
   {
     double acc8[8] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
     double z8[8] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
-    for (int b0 = j; b0 < nblk; b0 += 32) {
+    for (int b0 = g; b0 < nblk; b0 += 8 * G) {
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
-        const int b = b0 + 4 * q;
+        const int b = b0 + q * G;
         if (b < nblk) {
           if (e < E) acc8[q] += part_P[static_cast<int64_t>(b) * E + e];
           if (e == 0) z8[q] += part_z[b];
         }
       }
     }
-    sj[j][e] = ((acc8[0] + acc8[1]) + (acc8[2] + acc8[3])) + ((acc8[4] + acc8[5]) + (acc8[6] + acc8[7]));
-    if (e == 0) zj[j] = ((z8[0] + z8[1]) + (z8[2] + z8[3])) + ((z8[4] + z8[5]) + (z8[6] + z8[7]));
+    sj[threadIdx.x] = ((acc8[0] + acc8[1]) + (acc8[2] + acc8[3])) +
+                      ((acc8[4] + acc8[5]) + (acc8[6] + acc8[7]));
+    zj[threadIdx.x] = ((z8[0] + z8[1]) + (z8[2] + z8[3])) + ((z8[4] + z8[5]) + (z8[6] + z8[7]));
   }
   __syncthreads();
-  if (j == 0) {
-    double fP = 0.0, drop = 0.0;
-    if (e < E) {
-      const double sumP = (sj[0][e] + sj[1][e]) + (sj[2][e] + sj[3][e]);
-      const double Pe = sumP / nT;
-      const double fe = static_cast<double>(counts[e]) / nT;
-      f[e] = static_cast<float>(fe);
-      P[e] = static_cast<float>(Pe);
-      fP = fe * Pe;
-      drop = static_cast<double>(max(0, counts[e] - cap));
+  // fold the groups: element (g, e) += (g + h, e) for h = G/2, G/4, ..., 1
+  for (int h = G / 2; h > 0; h >>= 1) {
+    if (g < h) {
+      sj[threadIdx.x] += sj[threadIdx.x + h * EP];
+      zj[threadIdx.x] += zj[threadIdx.x + h * EP];
     }
-    fp[e] = fP;
-    dr[e] = drop;
+    __syncthreads();
+  }
+  if (threadIdx.x < 256) {
+    double fP = 0.0, drop = 0.0;
+    const int ee = threadIdx.x;
+    if (ee < E) {
+      const double Pe = sj[ee] / nT;
+      const double fe = static_cast<double>(counts[ee]) / nT;
+      f[ee] = static_cast<float>(fe);
+      P[ee] = static_cast<float>(Pe);
+      fP = fe * Pe;
+      drop = static_cast<double>(max(0, counts[ee] - cap));
+    }
+    fp[ee] = fP;
+    dr[ee] = drop;
   }
   __syncthreads();
   for (int off = 128; off > 0; off >>= 1) {
@@ -128,9 +141,8 @@ __global__ __launch_bounds__(1024) void stats_final_kernel(
     __syncthreads();
   }
   if (threadIdx.x == 0) {
-    const double z = (zj[0] + zj[1]) + (zj[2] + zj[3]);
     scalars[0] = static_cast<double>(E) * fp[0];
-    scalars[1] = z / nT;
+    scalars[1] = zj[0] / nT;
     scalars[2] = dr[0] / (static_cast<double>(nT) * k);
   }
 }
@@ -157,8 +169,10 @@ hipError_t launch_aux_stats(int64_t T, int E, int k, int64_t cap, const float* l
   double* part_z = part_P + static_cast<size_t>(kStatsBlocks) * E;
   hipLaunchKernelGGL(stats_partial_kernel, dim3(nblk), dim3(kWavesS * kWave), 0, s, logits,
                      part_P, part_z, static_cast<int>(T), E, tpb);
+  int EP = 1;
+  while (EP < E) EP <<= 1;
   hipLaunchKernelGGL(stats_final_kernel, dim3(1), dim3(1024), 0, s, part_P, part_z, counts, f,
-                     P, scalars, nblk, static_cast<int>(T), E, k, static_cast<int>(cap));
+                     P, scalars, nblk, static_cast<int>(T), E, k, static_cast<int>(cap), EP);
   return hipGetLastError();
 }
 
