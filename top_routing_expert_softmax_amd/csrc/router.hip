@@ -109,6 +109,28 @@ __device__ __forceinline__ void load_w(const T* row, int e0, int E, bool vec, fl
   for (int e = 0; e < EPL; ++e) w[e] = (e0 + e < E) ? load1(row + e0 + e) : 0.f;
 }
 
+// One reduce-scatter round per call over the lane bit `off` (then the next
+// one, with half the values): the lane with the bit set keeps the upper H
+// of its 2H values, the other the lower H, and each adds its partner's copy
+// of the half it keeps.  base: index of v[0] among the original values.
+// Stops early once off reaches the wave width.
+template <int H>
+__device__ __forceinline__ void scatter_rounds(float* v, int lane, int& off, int& base) {
+  if constexpr (H >= 1) {
+    if (off >= kWave) return;
+    const bool hi = (lane & off) != 0;
+#pragma unroll
+    for (int j = 0; j < H; ++j) {
+      const float send = hi ? v[j] : v[j + H];
+      const float keep = hi ? v[j + H] : v[j];
+      v[j] = keep + __shfl_xor(send, off, kWave);
+    }
+    if (hi) base += H;
+    off <<= 1;
+    scatter_rounds<H / 2>(v, lane, off, base);
+  }
+}
+
 __device__ __forceinline__ float from_order_key(uint32_t key) {
   const uint32_t u = (key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key;
   return __uint_as_float(u);
@@ -275,20 +297,33 @@ __global__ __launch_bounds__(kMaxWavesR * kWave) void router_kernel(
       }
     }
   }
-  // Sum over the ds lanes that share es (lane bits above log2(ES)).
-  for (int off = ES; off < kWave; off <<= 1) {
+  // Sum over the ds lanes that share es (lane bits above log2(ES)) by
+  // reduce-scatter: each round hands half of the lane's remaining sums to
+  // its partner and adds the partner's copy of the other half, so the
+  // lanes end up holding distinct, fully summed (token, expert) values.
+  constexpr int V = kTW * EPL;
+  float v[V];
 #pragma unroll
-    for (int t = 0; t < kTW; ++t)
+  for (int t = 0; t < kTW; ++t)
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[t][e] += __shfl_xor(acc[t][e], off, kWave);
-  }
+    for (int e = 0; e < EPL; ++e) v[t * EPL + e] = acc[t][e];
+  int off = ES, base = 0;
+  scatter_rounds<V / 2>(v, lane, off, base);
+  int rounds = 0;                                 // rounds that halved
+  while ((ES << rounds) < off) ++rounds;
+  const int R = V >> rounds;                      // sums this lane holds
+  // more ds lanes than values: the remaining rounds add whole sums
+  for (; off < kWave; off <<= 1) v[0] += __shfl_xor(v[0], off, kWave);
   float* red = smem;                              // [nwaves][kTW][E_pad]
   float* lg = smem + nwaves * kTW * E_pad;        // [kTW][E_pad]
-  if (ds == 0) {
+  if ((ds >> rounds) == 0) {                      // one writer per value
 #pragma unroll
-    for (int t = 0; t < kTW; ++t)
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) red[(wave * kTW + t) * E_pad + e0 + e] = acc[t][e];
+    for (int j = 0; j < V; ++j) {
+      if (j < R) {
+        const int q = base + j, t = q / EPL, e = q % EPL;
+        red[(wave * kTW + t) * E_pad + e0 + e] = v[j];
+      }
+    }
   }
   __syncthreads();
   float* dst = SPLIT ? partial + static_cast<int64_t>(blockIdx.y) * nT * E : logits;
