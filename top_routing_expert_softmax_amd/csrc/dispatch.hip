@@ -87,9 +87,20 @@ __global__ __launch_bounds__(1024) void scan_kernel(int32_t* __restrict__ blk,
   __shared__ int wave_tot[16];
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
-  const int nwaves = blockDim.x / kWave;
-  for (int e = wave; e < E; e += nwaves) {
-    const int v = (lane < nblk) ? blk[e * kMaxDispatchBlocks + lane] : 0;
+  constexpr int kWavesScan = 16;                 // 1024 threads
+  constexpr int kPerWave = 256 / kWavesScan;     // experts per wave, E <= 256
+  // every load of the wave first, then the scans
+  int vals[kPerWave];
+#pragma unroll
+  for (int q = 0; q < kPerWave; ++q) {
+    const int e = wave + q * kWavesScan;
+    vals[q] = (e < E && lane < nblk) ? blk[e * kMaxDispatchBlocks + lane] : 0;
+  }
+#pragma unroll
+  for (int q = 0; q < kPerWave; ++q) {
+    const int e = wave + q * kWavesScan;
+    if (e >= E) break;
+    const int v = vals[q];
     int incl = v;
 #pragma unroll
     for (int off = 1; off < kWave; off <<= 1) {
