@@ -11,7 +11,9 @@
 //      and how many of the keys equal to K* are taken;
 //   2. every thread owns a contiguous run of tokens; block scans place the
 //      keys above K* and the first (lowest-token) keys equal to K* into LDS;
-//   3. a bitonic sort on (key, -token) orders the cap picks, larger first.
+//   3. a bitonic sort on (key, -token) orders the cap picks, larger first
+//      (keys in registers and wave shuffles for strides below 64 when the
+//      padded count fits the block).
 // Keys compare exactly (the logits are fp32), so the choice is exact.
 //
 // Dispatch: expert e owns rows e*cap .. e*cap+cap-1 of x_perm; row_of_te and
@@ -103,14 +105,33 @@ __global__ __launch_bounds__(kEcThreads) void ec_select_kernel(
       if (match) atomicAdd(&hist[(k >> shift) & 255u], 1);
     }
     __syncthreads();
-    if (tid == 0) {
-      int cum = 0, digit = 0;
-      for (int b = 255; b >= 0; --b) {
-        if (cum + hist[b] >= need) { digit = b; break; }
-        cum += hist[b];
+    if (tid < kWave) {
+      // the digit is the largest bin b whose count together with the bins
+      // above it reaches `need`; lane l holds bins 255 - 4l .. 252 - 4l
+      const int lane = tid;
+      int h[4], sum = 0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        h[q] = hist[255 - 4 * lane - q];
+        sum += h[q];
       }
-      s_sel[0] = prefix | (static_cast<uint32_t>(digit) << shift);
-      s_sel[1] = static_cast<uint32_t>(need - cum);
+      int incl = sum;
+#pragma unroll
+      for (int off = 1; off < kWave; off <<= 1) {
+        const int n = __shfl_up(incl, off, kWave);
+        if (lane >= off) incl += n;
+      }
+      int cum = incl - sum, digit = -1, above = 0;   // cum: keys in the bins above
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (digit < 0 && cum + h[q] >= need) { digit = 255 - 4 * lane - q; above = cum; }
+        cum += h[q];
+      }
+      const uint64_t found = __ballot(digit >= 0);
+      if (lane == __ffsll(static_cast<unsigned long long>(found)) - 1) {
+        s_sel[0] = prefix | (static_cast<uint32_t>(digit) << shift);
+        s_sel[1] = static_cast<uint32_t>(need - above);
+      }
     }
     __syncthreads();
     prefix = s_sel[0];
@@ -147,20 +168,49 @@ __global__ __launch_bounds__(kEcThreads) void ec_select_kernel(
   }
   __syncthreads();
 
-  // 3. bitonic sort, larger composite key first
-  for (int size = 2; size <= npow2; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int i = tid; i < npow2; i += kEcThreads) {
-        const int j = i ^ stride;
-        if (j > i) {
-          const uint64_t a = picks[i], b = picks[j];
-          const bool desc = (i & size) == 0;
-          if (desc ? (a < b) : (a > b)) { picks[i] = b; picks[j] = a; }
+  // 3. bitonic sort, larger composite key first.  Up to one key per
+  // thread: the key stays in a register, partners closer than a wavefront
+  // are reached by shuffles and only the wider strides go through LDS.
+  if (npow2 <= kEcThreads) {
+    uint64_t key = tid < npow2 ? picks[tid] : 0ull;
+    for (int size = 2; size <= npow2; size <<= 1) {
+      for (int stride = size >> 1; stride > 0; stride >>= 1) {
+        uint64_t other;
+        if (stride >= kWave) {
+          __syncthreads();                       // every read of the last round is done
+          if (tid < npow2) picks[tid] = key;
+          __syncthreads();
+          other = tid < npow2 ? picks[tid ^ stride] : 0ull;
+        } else {
+          const uint32_t lo = __shfl_xor(static_cast<uint32_t>(key), stride, kWave);
+          const uint32_t hi = __shfl_xor(static_cast<uint32_t>(key >> 32), stride, kWave);
+          other = (static_cast<uint64_t>(hi) << 32) | lo;
         }
+        // the lower index of a pair keeps the larger key in a descending
+        // run, the smaller in an ascending one
+        const bool desc = (tid & size) == 0;
+        const bool lower = (tid & stride) == 0;
+        key = (desc == lower) ? (key > other ? key : other) : (key < other ? key : other);
       }
-      __syncthreads();
+    }
+    __syncthreads();
+    if (tid < npow2) picks[tid] = key;
+  } else {
+    for (int size = 2; size <= npow2; size <<= 1) {
+      for (int stride = size >> 1; stride > 0; stride >>= 1) {
+        for (int i = tid; i < npow2; i += kEcThreads) {
+          const int j = i ^ stride;
+          if (j > i) {
+            const uint64_t a = picks[i], b = picks[j];
+            const bool desc = (i & size) == 0;
+            if (desc ? (a < b) : (a > b)) { picks[i] = b; picks[j] = a; }
+          }
+        }
+        __syncthreads();
+      }
     }
   }
+  __syncthreads();
   for (int j = tid; j < cap; j += kEcThreads) {
     const int t = static_cast<int>(0xFFFFFFFFu - static_cast<uint32_t>(picks[j]));
     const float g = logits[static_cast<int64_t>(t) * E + e];
