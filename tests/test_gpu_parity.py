@@ -57,6 +57,12 @@ SMALL_CASES = {
     # pipeline and its remainder; a shared expert with 48 rows (3 groups)
     "bf16_decode_stream": ("dsv3_decode", dict(T=48, d_model=2048, E=64, E_shared=1, k=4,
                                                d_ff=1024)),
+    # T * k < 64 E with T > 64: segments of at most 64 rows stream their
+    # weights, larger ones (two experts of 200 and 183 rows and the 200-row
+    # shared expert) take the 128-row tiles beside them; twelve experts are
+    # empty
+    "bf16_decode_mixed_tiles": ("skewed_train", dict(T=200, d_model=256, E=16, E_shared=1, k=2,
+                                                     d_ff=256, CF=None, zipf_tau=1.0)),
     # fewer 256 x 256 tiles than compute units and K >= 2048: both phases
     # split K in two and sum the partial tiles
     "bf16_split_k2": ("mixtral_prefill", dict(T=640, d_model=2048, E=4, k=2, d_ff=2048,
