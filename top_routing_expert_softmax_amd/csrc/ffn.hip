@@ -1225,24 +1225,23 @@ hipError_t launch_expert_ffn_backward(int64_t T, int64_t d, int E, int E_shared,
              ntiles, sk_partial, sk_count, static_cast<int>(T), Fi, E, E_shared, k, di,
              nullptr, di};
   ok(launch_gemm_big<5>(ah, nt_of(F, kBN2), mt, ncu, s));
-  // 3. (A, B), dH -> (dA, dB) in g13, H in place of dH
-  ok(launch_swiglu_bwd(ab != nullptr ? ab : g13, g13, dh, offsets, E, T * k, L.rows, F, s));
+  // 3. (A, B), dH -> (dA, dB) row-major in g13, and the K-major copies
+  //    dA^T, dB^T, H^T the weight gradients read
+  uint16_t* xt = reinterpret_cast<uint16_t*>(base + L.xt);
+  uint16_t* dot = reinterpret_cast<uint16_t*>(base + L.dot);
+  uint16_t* ht = reinterpret_cast<uint16_t*>(base + L.ht);
+  uint16_t* dabt = reinterpret_cast<uint16_t*>(base + L.dabt);
+  ok(launch_swiglu_bwd_t(ab != nullptr ? ab : g13, g13, dh, dabt, ht, poff, hstart, nrows, E,
+                         E_shared, T, F, L.ld, s));
   // 4. dX = [dA dB] [W1; W3]: the phase-2 form with K = 2F and N = d, B
   //    rows from W1 [F, d] then W3 [F, d] as stored (PHASE 5)
   FfnArgs ax{nullptr, nullptr, offsets, nullptr, w3, w1, nullptr, ws3, ws1, g13, dx_perm,
              dx_shared, tiles, ntiles, sk_partial, sk_count, static_cast<int>(T), di, E,
              E_shared, k, 2 * Fi, nullptr, Fi};
   ok(launch_gemm_big<5>(ax, nt_of(d, kBN2), mt, ncu, s));
-  // 5. K-major copies for the weight gradients
-  uint16_t* xt = reinterpret_cast<uint16_t*>(base + L.xt);
-  uint16_t* dot = reinterpret_cast<uint16_t*>(base + L.dot);
-  uint16_t* ht = reinterpret_cast<uint16_t*>(base + L.ht);
-  uint16_t* dabt = reinterpret_cast<uint16_t*>(base + L.dabt);
+  // 5. K-major copies of X and dO for the weight gradients
   ok(launch_transpose_seg(x_perm, x, xt, poff, hstart, nrows, di, L.ld, E, E_shared, T, k, s));
   ok(launch_transpose_seg(dy_perm, nullptr, dot, poff, hstart, nrows, di, L.ld, E, E_shared, T,
-                          k, s));
-  ok(launch_transpose_seg(dh, nullptr, ht, poff, hstart, nrows, Fi, L.ld, E, E_shared, T, k, s));
-  ok(launch_transpose_seg(g13, nullptr, dabt, poff, hstart, nrows, 2 * Fi, L.ld, E, E_shared, T,
                           k, s));
   // 6. dW1 = dA^T X, dW3 = dB^T X  ([F, d]),  dW2 = dO^T H  ([d, F])
   WgradArgs g1{dabt, xt, L.ld, poff, dw1, dws1, Fi, di, E, 0};

@@ -1,6 +1,6 @@
 // Helpers of the expert-FFN backward pass (bf16): segment offsets, the
 // K-major copies of the activations for the weight-gradient GEMMs, and the
-// elementwise SwiGLU step.
+// SwiGLU step (which writes its outputs' K-major copies itself).
 //
 // For one expert with rows X (the gathered tokens), A = X W1^T, B = X W3^T,
 // H = SiLU(A) (*) B, O = H W2^T, and output gradient dO:
@@ -150,27 +150,78 @@ __global__ __launch_bounds__(256) void transpose_seg_kernel(
   *reinterpret_cast<u32x4_t*>(out + ld) = o1;
 }
 
-// Per valid H-indexed row (one block per row): (A, B) from ab [2F] and dH
-// from dh [F] give (dA, dB) in g13 [2F] and H = SiLU(A) (*) B in place of
-// dH.  ab may be g13 itself (each element is read before it is written, by
-// the same thread).
-__global__ __launch_bounds__(256) void swiglu_bwd_kernel(const uint16_t* ab, uint16_t* g13,
-                                                         uint16_t* __restrict__ dh,
-                                                         const int32_t* __restrict__ offsets,
-                                                         int E, int64_t Tk, int F) {
-  const int64_t row = blockIdx.x;
-  if (row < Tk && row >= offsets[E]) return;     // routed rows past R are unused
-  const uint16_t* I = ab + row * 2 * F;
-  uint16_t* G = g13 + row * 2 * F;
-  uint16_t* D = dh + row * F;
-  for (int f = threadIdx.x; f < F; f += blockDim.x) {
-    const float a = bf16_to_f32(I[f]), b = bf16_to_f32(I[F + f]), d = bf16_to_f32(D[f]);
-    const float sg = 1.0f / (1.0f + __expf(-a));
-    const float s = a * sg;
-    G[f] = f32_to_bf16(d * b * sg * (1.0f + a * (1.0f - sg)));
-    G[F + f] = f32_to_bf16(d * s);
-    D[f] = f32_to_bf16(s * b);
+// The SwiGLU step fused with the K-major copies its outputs feed: per 64 x
+// 64 tile of segment s (rows j0.., columns c0.. of F), from A, B (ab [2F])
+// and dH (dh [F]) it forms dA, dB and H = SiLU(A) (*) B, writes dA and dB
+// row-major into g13 (the dX GEMM reads them so) and dA^T, dB^T, H^T
+// K-major into dabt [2F][ld] and ht [F][ld] at column poff[s] + j (the
+// weight gradients read them so).  Rows past the segment load as zero and
+// so give the zero padding up to the next multiple of 64.  H is not kept
+// row-major: only its K-major copy is read later.  ab may be g13 itself
+// (every element is read before it is written, by the same thread).
+__global__ __launch_bounds__(256) void swiglu_bwd_t_kernel(
+    const uint16_t* ab, uint16_t* g13, const uint16_t* __restrict__ dh,
+    uint16_t* __restrict__ dabt, uint16_t* __restrict__ ht, const int* __restrict__ poff,
+    const int* __restrict__ hstart, const int* __restrict__ nrows, int F, int64_t ld) {
+  __shared__ TileT tiles[3];                    // dA, dB, H
+  const int s = blockIdx.z;
+  const int n = nrows[s];
+  const int npad = poff[s + 1] - poff[s];
+  const int j0 = blockIdx.y * kTile, c0 = blockIdx.x * kTile;
+  if (j0 >= npad) return;
+  const int h = hstart[s];
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int it = 0; it < 2; ++it) {
+    const int idx = tid + 256 * it, r = idx >> 3, cc = idx & 7, j = j0 + r;
+    u32x4_t qa{0u, 0u, 0u, 0u}, qb = qa, qd = qa;
+    const int64_t row = static_cast<int64_t>(h) + j;
+    if (j < n) {
+      qa = *reinterpret_cast<const u32x4_t*>(ab + row * 2 * F + c0 + cc * 8);
+      qb = *reinterpret_cast<const u32x4_t*>(ab + row * 2 * F + F + c0 + cc * 8);
+      qd = *reinterpret_cast<const u32x4_t*>(dh + row * F + c0 + cc * 8);
+    }
+    u32x4_t oa, ob, oh;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      uint32_t pa = 0u, pb = 0u, ph = 0u;
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const float a = half ? bf16hi(qa[w]) : bf16lo(qa[w]);
+        const float b = half ? bf16hi(qb[w]) : bf16lo(qb[w]);
+        const float d = half ? bf16hi(qd[w]) : bf16lo(qd[w]);
+        const float sg = 1.0f / (1.0f + __expf(-a));
+        const float si = a * sg;
+        const uint32_t ga = f32_to_bf16(d * b * sg * (1.0f + a * (1.0f - sg)));
+        const uint32_t gb = f32_to_bf16(d * si);
+        const uint32_t hh = f32_to_bf16(si * b);
+        pa |= ga << (16 * half);
+        pb |= gb << (16 * half);
+        ph |= hh << (16 * half);
+      }
+      oa[w] = pa; ob[w] = pb; oh[w] = ph;
+    }
+    if (j < n) {
+      *reinterpret_cast<u32x4_t*>(g13 + row * 2 * F + c0 + cc * 8) = oa;
+      *reinterpret_cast<u32x4_t*>(g13 + row * 2 * F + F + c0 + cc * 8) = ob;
+    }
+    tile_store_chunk(tiles[0], r, cc, oa);
+    tile_store_chunk(tiles[1], r, cc, ob);
+    tile_store_chunk(tiles[2], r, cc, oh);
   }
+  __syncthreads();
+  const int rb = tid & 7, c = c0 + 2 * (tid >> 3);
+  const int64_t col = poff[s] + j0 + rb * 8;
+  u32x4_t o0, o1;
+  tile_read_pair(tiles[0], tid, o0, o1);
+  *reinterpret_cast<u32x4_t*>(dabt + static_cast<int64_t>(c) * ld + col) = o0;
+  *reinterpret_cast<u32x4_t*>(dabt + static_cast<int64_t>(c + 1) * ld + col) = o1;
+  tile_read_pair(tiles[1], tid, o0, o1);
+  *reinterpret_cast<u32x4_t*>(dabt + static_cast<int64_t>(F + c) * ld + col) = o0;
+  *reinterpret_cast<u32x4_t*>(dabt + static_cast<int64_t>(F + c + 1) * ld + col) = o1;
+  tile_read_pair(tiles[2], tid, o0, o1);
+  *reinterpret_cast<u32x4_t*>(ht + static_cast<int64_t>(c) * ld + col) = o0;
+  *reinterpret_cast<u32x4_t*>(ht + static_cast<int64_t>(c + 1) * ld + col) = o1;
 }
 
 }  // namespace
@@ -196,11 +247,16 @@ hipError_t launch_transpose_seg(const void* src, const void* src_shared, void* d
   return hipGetLastError();
 }
 
-hipError_t launch_swiglu_bwd(const void* ab, void* g13, void* dh, const int32_t* offsets, int E,
-                             int64_t Tk, int64_t rows_total, int64_t F, hipStream_t s) {
-  hipLaunchKernelGGL(swiglu_bwd_kernel, dim3(static_cast<unsigned>(rows_total)), dim3(256), 0, s,
+hipError_t launch_swiglu_bwd_t(const void* ab, void* g13, const void* dh, void* dabt, void* ht,
+                               const int* poff, const int* hstart, const int* nrows, int E,
+                               int Es, int64_t T, int64_t F, int64_t ld, hipStream_t s) {
+  const dim3 grid(static_cast<unsigned>(F / kTile),
+                  static_cast<unsigned>((T + kTile - 1) / kTile + 1),
+                  static_cast<unsigned>(E + Es));
+  hipLaunchKernelGGL(swiglu_bwd_t_kernel, grid, dim3(256), 0, s,
                      static_cast<const uint16_t*>(ab), static_cast<uint16_t*>(g13),
-                     static_cast<uint16_t*>(dh), offsets, E, Tk, static_cast<int>(F));
+                     static_cast<const uint16_t*>(dh), static_cast<uint16_t*>(dabt),
+                     static_cast<uint16_t*>(ht), poff, hstart, nrows, static_cast<int>(F), ld);
   return hipGetLastError();
 }
 

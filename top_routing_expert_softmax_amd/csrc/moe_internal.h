@@ -115,8 +115,9 @@ hipError_t launch_seg_info(const int32_t* offsets, int* poff, int* hstart, int* 
 hipError_t launch_transpose_seg(const void* src, const void* src_shared, void* dst,
                                 const int* poff, const int* hstart, const int* nrows, int C,
                                 int64_t ld, int E, int Es, int64_t T, int k, hipStream_t s);
-hipError_t launch_swiglu_bwd(const void* ab, void* g13, void* dh, const int32_t* offsets, int E,
-                             int64_t Tk, int64_t rows_total, int64_t F, hipStream_t s);
+hipError_t launch_swiglu_bwd_t(const void* ab, void* g13, const void* dh, void* dabt, void* ht,
+                               const int* poff, const int* hstart, const int* nrows, int E,
+                               int Es, int64_t T, int64_t F, int64_t ld, hipStream_t s);
 
 // Combine and router backward (bwd.hip).
 hipError_t launch_combine_backward(int64_t T, int64_t d, int E_shared, int k, const void* dy,
