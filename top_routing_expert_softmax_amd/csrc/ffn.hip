@@ -25,6 +25,8 @@
 // the correctness path.
 #include <math.h>
 
+#include <atomic>
+
 #include "moe_device.h"
 #include "moe_internal.h"
 
@@ -776,6 +778,22 @@ constexpr int kBKsel = 64;
 constexpr int kNSTsel = 2;
 constexpr int kWavesSel = 8;
 
+// The dynamic LDS above the default limit is a per-device setting of a
+// kernel: set it once for each (kernel, device) the process launches on.
+template <auto Kern>
+hipError_t allow_dynamic_lds(int bytes) {
+  static std::atomic<uint64_t> done{0};        // one bit per device id < 64
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  const uint64_t bit = dev < 64 ? (uint64_t{1} << dev) : 0;
+  if (bit != 0 && (done.load(std::memory_order_acquire) & bit) != 0) return hipSuccess;
+  err = hipFuncSetAttribute(reinterpret_cast<const void*>(Kern),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (err == hipSuccess && bit != 0) done.fetch_or(bit, std::memory_order_acq_rel);
+  return err;
+}
+
 template <int PHASE>
 hipError_t launch_gemm_big(const FfnArgs& a, int nt, int64_t mt, int ncu, hipStream_t s) {
   // whole-tile blocks (at most every tile, in XCD-sized steps) plus one
@@ -784,10 +802,8 @@ hipError_t launch_gemm_big(const FfnArgs& a, int nt, int64_t mt, int ncu, hipStr
   const unsigned g = static_cast<unsigned>(kXcds * ((lmax + kXcds - 1) / kXcds) + ncu);
   constexpr size_t lds = static_cast<size_t>(kNSTsel) * SliceGeom<kBKsel, kBM2>::STAGE;
   static_assert(lds <= 160 * 1024, "LDS ring exceeds the 160 KB of a CU");
-  auto kern = &gemm_big_kernel<PHASE, kBKsel, kNSTsel, kWavesSel, kBM2, kWM>;
-  static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
-      static_cast<int>(lds));
+  constexpr auto kern = &gemm_big_kernel<PHASE, kBKsel, kNSTsel, kWavesSel, kBM2, kWM>;
+  const hipError_t attr = allow_dynamic_lds<kern>(static_cast<int>(lds));
   if (attr != hipSuccess) return attr;
   hipLaunchKernelGGL(kern, dim3(g), dim3(kWavesSel * kWave), lds, s, a, nt, ncu);
   return hipGetLastError();
@@ -993,10 +1009,8 @@ hipError_t launch_wgrad(const WgradArgs& a0, int nseg, hipStream_t s) {
   a.NT = (a.N + kBN2 - 1) / kBN2;
   const int MT = (a.M + 255) / 256;
   constexpr size_t lds = static_cast<size_t>(kNSTsel) * SliceGeom<kBKsel, 256>::STAGE;
-  auto kern = &gemm_wgrad_kernel<kBKsel, kNSTsel, kWavesSel>;
-  static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
-      static_cast<int>(lds));
+  constexpr auto kern = &gemm_wgrad_kernel<kBKsel, kNSTsel, kWavesSel>;
+  const hipError_t attr = allow_dynamic_lds<kern>(static_cast<int>(lds));
   if (attr != hipSuccess) return attr;
   hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(MT * a.NT), static_cast<unsigned>(nseg)),
                      dim3(kWavesSel * kWave), lds, s, a);
