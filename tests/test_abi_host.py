@@ -195,12 +195,13 @@ def test_training_forward_and_backward_arguments_are_checked(M):
     assert train(ws=1024) == -4
     assert train(d=100) == -1                                # not a multiple of 64
 
-    def bwd(dtype=M.MOE_BF16, ws=1 << 36, dw1=fake):
+    def bwd(dtype=M.MOE_BF16, ws=1 << 36, dw1=fake, ab=nil):
         return L.moe_expert_ffn_backward(4096, 4096, 8, 0, 2, 14336, dtype, fake, fake, fake,
                                          fake, fake, fake, nil, nil, nil, fake, fake, nil, dw1,
-                                         fake, fake, nil, nil, nil, nil, fake, ws, nil)
+                                         fake, fake, nil, nil, nil, ab, fake, ws, nil)
     assert bwd(dtype=M.MOE_F32) == -1
     assert bwd(dw1=nil) == -1
+    assert bwd(ab=ctypes.c_void_p(4096 + 8)) == -1 and "ab" in L.moe_last_error().decode()
     assert bwd(ws=1024) == -4 and "workspace" in L.moe_last_error().decode()
     n = ctypes.c_size_t()
     assert L.moe_backward_workspace_size(4096, 4096, 8, 0, 2, 14336, M.MOE_BF16,

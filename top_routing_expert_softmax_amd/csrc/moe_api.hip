@@ -356,6 +356,7 @@ int moe_expert_ffn_backward(int64_t T, int64_t d_model, int32_t E, int32_t E_sha
   REQUIRE_PTR(dw3);
   REQUIRE_PTR(dw2);
   REQUIRE_PTR(ws);
+  REQUIRE(ab == nullptr || aligned16(ab), "ab is not 16-byte aligned");
   if (E_shared > 0) {
     REQUIRE_PTR(x);
     REQUIRE_PTR(ws1);
