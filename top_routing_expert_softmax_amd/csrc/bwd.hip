@@ -174,7 +174,17 @@ __global__ __launch_bounds__(256) void dx_kernel(
     for (int u = 0; u < 8; ++u) {
       const uint16_t* wrow = w_gate + static_cast<int64_t>(c * 8 + u) * E;
       float s = 0.f;
-      for (int e = 0; e < E; ++e) s = fmaf(sdg[wv][e], bf16_to_f32(wrow[e]), s);
+      if (E % 8 == 0) {
+        // the row in 16-byte pieces (rows are 16-byte aligned), same order
+        for (int q = 0; q < E / 8; ++q) {
+          float w[8];
+          unpack8(reinterpret_cast<const u32x4_t*>(wrow)[q], w);
+#pragma unroll
+          for (int v2 = 0; v2 < 8; ++v2) s = fmaf(sdg[wv][q * 8 + v2], w[v2], s);
+        }
+      } else {
+        for (int e = 0; e < E; ++e) s = fmaf(sdg[wv][e], bf16_to_f32(wrow[e]), s);
+      }
       a[u] += s;
     }
     dx[static_cast<int64_t>(t) * chunks + c] = pack8(a);
@@ -228,7 +238,15 @@ __global__ __launch_bounds__(256) void dwgate_sum_kernel(const float* __restrict
   const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (idx >= n) return;
   float s = 0.f;
-  for (int q = 0; q < S; ++q) s += part[q * n + idx];
+  int q = 0;
+  for (; q + 8 <= S; q += 8) {
+    float v[8];                                  // the loads first, the adds in order
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = part[(q + u) * n + idx];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) s += v[u];
+  }
+  for (; q < S; ++q) s += part[q * n + idx];
   dwg[idx] = s;
 }
 
