@@ -37,8 +37,8 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 # they were taken with (softmax router).  A changed
 # kernel reports null until it is measured again.
 MEASURED_TRAFFIC = {
-    ("mixtral_prefill", "2823e2a75294dd98"): 9.4726e9,
-    ("dsv3_decode", "2823e2a75294dd98"): 1.9663e10,
+    ("mixtral_prefill", "df0078bdbd1090b5"): 9.4461e9,
+    ("dsv3_decode", "df0078bdbd1090b5"): 1.9663e10,
 }
 
 
