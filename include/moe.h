@@ -327,7 +327,7 @@ int moe_aux_stats(int64_t T, int32_t E, int32_t k, double CF,
                   void* stream);
 
 /*
- * Backward pass of the layer (bf16; SURVEY row N2).  With an output
+ * Backward pass of the layer (bf16).  With an output
  * gradient dy and the loss L = sum(dy * y) + alpha * L_balance + beta * z
  * (the statistics of moe_aux_stats):
  *   combine ("CMU 11-868 Lecture 17" 2.2; "MoE routing math" 2.2):

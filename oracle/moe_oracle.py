@@ -16,7 +16,7 @@ Sources, cited by page title and section:
         (semidirectx.com notes)
   [INF] "MoE inference optimisation, deep dive" (jerryiiii.gitbook.io notes)
 
-Readings where the pages are silent or disagree (each is listed in the design doc):
+Readings where the pages are silent or disagree:
   * top-k order: larger first; equal values go to the lower expert index.
   * capacity: ceil(CF * T * k / E) evaluated exactly on the given CF value,
     clamped to T; CF None or <= 0 means no limit (cap = T).
