@@ -51,6 +51,11 @@ EC_CASES = {
     "dsmoe_shape": ("dsmoe16b_prefill", dict(T=8192, d_model=2048, E=64, E_shared=0, k=1), 1.25),
     # ragged: T not a multiple of E, cap not a power of two
     "ragged": ("mixtral_prefill", dict(T=1001, d_model=192, E=7, k=1), 1.5),
+    # 4096 picks per expert: more than the block has threads, so the pick
+    # sort runs in LDS
+    "largest_cap": ("mixtral_prefill", dict(T=8192, d_model=128, E=2, k=1), 1.0),
+    # 25 picks per expert (32 padded): the sort needs wave shuffles only
+    "small_cap": ("mixtral_prefill", dict(T=200, d_model=128, E=8, k=1), 1.0),
 }
 
 
