@@ -57,6 +57,9 @@ SMALL_CASES = {
     # pipeline and its remainder; a shared expert with 48 rows (3 groups)
     "bf16_decode_stream": ("dsv3_decode", dict(T=48, d_model=2048, E=64, E_shared=1, k=4,
                                                d_ff=1024)),
+    # the largest k the boundary takes (64 of 128 experts per token) and a
+    # shared expert
+    "bf16_k64": ("dsv3_decode", dict(T=33, d_model=128, E=128, E_shared=1, k=64, d_ff=128)),
     # T * k < 64 E with T > 64: segments of at most 64 rows stream their
     # weights, larger ones (two experts of 200 and 183 rows and the 200-row
     # shared expert) take the 128-row tiles beside them; twelve experts are
