@@ -65,6 +65,9 @@ V3_CASES = {
                        8, 3, 1.0),
     # small E, every group kept
     "all_groups": ("mixtral_prefill", dict(T=300, d_model=256, E=16, k=4), 4, 4, 1.5),
+    # the DeepSeek-V3 gate at a prefill size: the matrix-core router with
+    # 256 experts (three waves per block) and the gate in its epilogue
+    "prefill_E256": ("dsv3_decode", dict(T=1100, d_model=1024), 8, 4, 2.5),
 }
 
 

@@ -55,15 +55,4 @@ __device__ __forceinline__ uint32_t f32_order_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int off = kWave / 2; off > 0; off >>= 1) {
-    uint32_t lo = __shfl_xor(static_cast<uint32_t>(v), off, kWave);
-    uint32_t hi = __shfl_xor(static_cast<uint32_t>(v >> 32), off, kWave);
-    uint64_t o = (static_cast<uint64_t>(hi) << 32) | lo;
-    v = o > v ? o : v;
-  }
-  return v;
-}
-
 }  // namespace moe

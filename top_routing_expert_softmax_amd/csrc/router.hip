@@ -14,9 +14,16 @@
 // blocks that write partial logits to the workspace; a select kernel adds
 // the S partials in a fixed order and runs the same top-k.
 //
-// Top-k: one wavefront per token, each lane holding up to four logits; k
-// rounds of a wave-wide max over (order key of the logit, -index) pick the
-// experts, larger logit first and ties to the lower index; the weights are
+// Many tokens in bf16 with E a multiple of 8: the matrix-core kernel
+// router_mfma_kernel below (its comment has the details) computes the same
+// logits with MFMA, also exactly on the dyadic grid, and runs the same
+// epilogue.
+//
+// Top-k: one wavefront per token (four tokens per wavefront when E <= 64),
+// each lane holding up to four logits; k rounds of a wave-wide max of the
+// logits' order keys (DPP within rows of 16 lanes, then the row maxima)
+// pick the experts, larger logit first, and a ballot of the lanes holding
+// that key gives the lowest index among ties; the weights are
 // exp(g_j - g_max) / sum over the selected j.
 //
 // DeepSeek-V3 gate ("CMU 11-868 Lecture 17", section 5.3; the bias of
@@ -136,29 +143,49 @@ __device__ __forceinline__ float from_order_key(uint32_t key) {
   return __uint_as_float(u);
 }
 
+// Largest 32-bit value over the wavefront, returned to every lane: DPP
+// moves within each row of 16 lanes (quad swaps, then rotations by 4 and
+// 8), then the four row maxima through scalar registers.  Every lane must
+// be active.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0xB1, 0xF, 0xF, false)));
+  v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x4E, 0xF, 0xF, false)));
+  v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x124, 0xF, 0xF, false)));
+  v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x128, 0xF, 0xF, false)));
+  const uint32_t r0 = __builtin_amdgcn_readlane(v, 0), r1 = __builtin_amdgcn_readlane(v, 16);
+  const uint32_t r2 = __builtin_amdgcn_readlane(v, 32), r3 = __builtin_amdgcn_readlane(v, 48);
+  return max(max(r0, r1), max(r2, r3));
+}
+
+// Among entries r < 4 of every lane whose key equals best (wave-uniform),
+// the lowest expert index lane + 64 r.  best must be held by some entry.
+__device__ __forceinline__ int lowest_holder(const uint32_t (&key)[4], uint32_t best) {
+  const uint64_t m0 = __ballot(key[0] == best), m1 = __ballot(key[1] == best);
+  const uint64_t m2 = __ballot(key[2] == best), m3 = __ballot(key[3] == best);
+  return m0 ? __builtin_ctzll(m0)
+            : m1 ? 64 + __builtin_ctzll(m1) : m2 ? 128 + __builtin_ctzll(m2) : 192 + __builtin_ctzll(m3);
+}
+
 // Top-k of one token held by one wavefront: lane holds logits of experts
 // lane + 64 r (r < 4) in v[r].  Writes k ids and renormalised weights.
+// Each of the k rounds takes the largest order key left (key 0 marks
+// experts past E and those already taken: every finite logit has a larger
+// key), then the lowest expert index holding it.
 __device__ __forceinline__ void topk_select(const float (&v)[4], int E, int k, int lane,
                                             int32_t* __restrict__ idx_row,
                                             float* __restrict__ w_row) {
-  uint32_t taken = 0;
+  uint32_t key[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) key[r] = lane + kWave * r < E ? f32_order_key(v[r]) : 0u;
   float gmax = 0.f, wsum = 0.f, my_w = 0.f;
   int my_e = 0;
   for (int j = 0; j < k; ++j) {
-    uint64_t best = 0;
+    const uint32_t best = wave_max_u32(max(max(key[0], key[1]), max(key[2], key[3])));
+    const int e_sel = lowest_holder(key, best);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int e = lane + kWave * r;
-      if (e < E && !((taken >> r) & 1u)) {
-        const uint64_t key = (static_cast<uint64_t>(f32_order_key(v[r])) << 32) |
-                             static_cast<uint64_t>(0xFFFFFFFFu - static_cast<uint32_t>(e));
-        best = key > best ? key : best;
-      }
-    }
-    best = wave_max_u64(best);
-    const int e_sel = static_cast<int>(0xFFFFFFFFu - static_cast<uint32_t>(best));
-    const float g_sel = from_order_key(static_cast<uint32_t>(best >> 32));
-    if ((e_sel & (kWave - 1)) == lane) taken |= 1u << (e_sel / kWave);
+    for (int r = 0; r < 4; ++r)
+      if (e_sel == lane + kWave * r) key[r] = 0u;
+    const float g_sel = from_order_key(best);
     if (j == 0) gmax = g_sel;
     const float ex = expf(g_sel - gmax);
     wsum += ex;
@@ -167,6 +194,48 @@ __device__ __forceinline__ void topk_select(const float (&v)[4], int E, int k, i
   if (lane < k) {
     idx_row[lane] = my_e;
     w_row[lane] = my_w / wsum;
+  }
+}
+
+// Top-k of four tokens at once when E <= 64: lane holds the logit of
+// expert lane of token r in v[r] (tokens r >= ntok do not exist and are not
+// written).  The same rounds as topk_select, run for the four tokens side
+// by side so that their cross-lane reductions overlap; the results are
+// bit for bit those of topk_select.  Rows idx_rows + r * k, w_rows + r * k.
+__device__ __forceinline__ void topk_select4(const float (&v)[4], int E, int k, int lane,
+                                             int ntok, int32_t* __restrict__ idx_rows,
+                                             float* __restrict__ w_rows) {
+  uint32_t key[4];
+  float gmax[4], wsum[4], my_w[4];
+  int my_e[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    key[r] = lane < E && r < ntok ? f32_order_key(v[r]) : 0u;
+    gmax[r] = 0.f; wsum[r] = 0.f; my_w[r] = 0.f; my_e[r] = 0;
+  }
+  for (int j = 0; j < k; ++j) {
+    uint32_t best[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) best[r] = wave_max_u32(key[r]);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int e_sel = __builtin_ctzll(__ballot(key[r] == best[r]));
+      if (e_sel == lane) key[r] = 0u;
+      const float g_sel = from_order_key(best[r]);
+      if (j == 0) gmax[r] = g_sel;
+      const float ex = expf(g_sel - gmax[r]);
+      wsum[r] += ex;
+      if (lane == j) { my_w[r] = ex; my_e[r] = e_sel; }
+    }
+  }
+  if (lane < k) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      if (r < ntok) {
+        idx_rows[r * k + lane] = my_e[r];
+        w_rows[r * k + lane] = my_w[r] / wsum[r];
+      }
+    }
   }
 }
 
@@ -203,37 +272,34 @@ __device__ __forceinline__ void v3_select(const float* g_row, float* scratch, co
     }
     gkey = f32_order_key(t1 + t2);
   }
-  // keep topk_groups groups: rounds of a wave max over (score, -group)
+  // keep topk_groups groups: rounds of a wave max over the group scores
+  // (key 0: not a group, or kept already), ties to the lower group
   uint64_t kept = 0;
   for (int j = 0; j < gp.topk_groups; ++j) {
-    uint64_t key = 0;
-    if (lane < gp.n_groups && !((kept >> lane) & 1ull))
-      key = (static_cast<uint64_t>(gkey) << 32) | static_cast<uint64_t>(0xFFFFFFFFu - lane);
-    key = wave_max_u64(key);
-    kept |= 1ull << (0xFFFFFFFFu - static_cast<uint32_t>(key));
+    const uint32_t key = lane < gp.n_groups && !((kept >> lane) & 1ull) ? gkey : 0u;
+    const uint32_t best = wave_max_u32(key);
+    kept |= 1ull << __builtin_ctzll(__ballot(key == best));
   }
-  // k experts of the kept groups by biased score
-  uint32_t taken = 0;
+  // k experts of the kept groups by biased score, ties to the lower expert
+  uint32_t key[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int e = lane + kWave * r;
+    key[r] = e < E && ((kept >> (e / G)) & 1ull) ? f32_order_key(bsc[r]) : 0u;
+  }
   float wsum = 0.f, my_s = 0.f;
   int my_e = 0;
   for (int j = 0; j < k; ++j) {
-    uint64_t best = 0;
-    float best_s = 0.f;
+    const uint32_t best = wave_max_u32(max(max(key[0], key[1]), max(key[2], key[3])));
+    const int e_sel = lowest_holder(key, best);
+    // the lane that holds the winner hands its affinity to every lane
+    const int r_sel = e_sel / kWave;
+    const float s_own = r_sel == 0 ? s[0] : r_sel == 1 ? s[1] : r_sel == 2 ? s[2] : s[3];
+    const float s_sel = __uint_as_float(
+        __builtin_amdgcn_readlane(__float_as_uint(s_own), e_sel & (kWave - 1)));
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int e = lane + kWave * r;
-      if (e < E && ((kept >> (e / G)) & 1ull) && !((taken >> r) & 1u)) {
-        const uint64_t key = (static_cast<uint64_t>(f32_order_key(bsc[r])) << 32) |
-                             static_cast<uint64_t>(0xFFFFFFFFu - static_cast<uint32_t>(e));
-        if (key > best) { best = key; best_s = s[r]; }
-      }
-    }
-    const uint64_t wbest = wave_max_u64(best);
-    const int e_sel = static_cast<int>(0xFFFFFFFFu - static_cast<uint32_t>(wbest));
-    // the lane that holds the winner broadcasts its affinity
-    const int owner = e_sel & (kWave - 1);
-    const float s_sel = __shfl(best_s, owner, kWave);
-    if (owner == lane) taken |= 1u << (e_sel / kWave);
+    for (int r = 0; r < 4; ++r)
+      if (e_sel == lane + kWave * r) key[r] = 0u;
     wsum += s_sel;
     if (lane == j) { my_s = s_sel; my_e = e_sel; }
   }
@@ -395,6 +461,200 @@ __global__ __launch_bounds__(256) void router_select_kernel(
   }
 }
 
+// Matrix-core router (bf16, E a multiple of 8, many tokens): a block owns
+// 16 * MT tokens and its nw waves split d into ranges of 32-wide k-steps.
+// Each wave runs v_mfma_f32_16x16x32_bf16 with x as the A operand (lane l:
+// token l % 16 of a 16-token tile, k = 8 (l / 16) .. +7, one 16-byte load)
+// and W_gate as the B operand (lane l: expert 16 g + l % 16 of column group
+// g, the same k).  W_gate is stored [d, E] with the experts contiguous, so
+// the wave copies U k-steps of its rows into its own LDS slice and reads
+// the B fragments back with LDS transpose reads.  Accumulator element v of
+// lane l is token 4 (l / 16) + v of the tile.  bf16 products are exact in
+// fp32, so on the dyadic input grid every MFMA sum is exact too and the
+// logits equal the fp32 FMA kernel's bit for bit.  The waves' partial
+// logits meet in LDS and are added in wave order; then the same top-k
+// epilogue runs.  Token rows past T read row T-1 and are never stored;
+// staged columns past E only feed accumulator columns that are dropped.
+
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef short i16x8_t __attribute__((ext_vector_type(8)));
+
+// Two LDS transpose reads (4 x 16 bit each) give one 8-value B fragment.
+// In each group of 16 lanes, lane 4p+m receives in slot j element m of the
+// 8 bytes that lane 4j+p addresses.  With lane 4j+p of group q pointing at
+// staged row 8q+j, column c0+4p, and the second read four rows further on,
+// lane i of group q holds column c0+i of rows 8q .. 8q+7.
+__device__ __forceinline__ bf16x8_t read_b_frag(const char* p, int four_rows) {
+  typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
+  const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+  const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + four_rows));
+  return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// Orders this wave's LDS accesses: the writes and reads before it are done
+// before those after it (a wave's LDS operations run in issue order).
+__device__ __forceinline__ void wave_lds_order() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+template <int EP, int U>
+struct MfmaRouterGeom {
+  static constexpr int G = EP / 16;                  // 16-expert column groups
+  static constexpr int ROWB = EP * 2 + 16;           // bytes per staged W_gate row
+  static constexpr int SLICE = 32 * U * ROWB;        // one wave's staging bytes
+  static constexpr int CPR = EP / 8;                 // 16-byte chunks per staged row
+  static constexpr int NWC = 32 * U * CPR / kWave;   // chunk slots per lane
+};
+
+template <int EP, int MT, int U, int P>
+__global__ __launch_bounds__(kMaxWavesR * kWave) void router_mfma_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ wg, float* __restrict__ logits,
+    int32_t* __restrict__ topk_idx, float* __restrict__ topk_w, int nT, int d, int E, int k,
+    GateParams gp) {
+  using Geo = MfmaRouterGeom<EP, U>;
+  constexpr int G = Geo::G, ROWB = Geo::ROWB, CPR = Geo::CPR, NWC = Geo::NWC;
+  constexpr int TB = 16 * MT;
+  extern __shared__ __align__(16) char smem_m[];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int nw = blockDim.x / kWave;
+  const int t0 = blockIdx.x * TB;
+  const int cpe = E / 8;                       // 16-byte chunks per W_gate row
+  const int nsteps = d / 32;
+  const int spw = (nsteps + nw - 1) / nw;
+  const int s_begin = wave * spw;
+  const int s_end = min(nsteps, s_begin + spw);
+  char* slice = smem_m + wave * Geo::SLICE;
+
+  const uint16_t* xrow[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+    xrow[mt] = x + static_cast<int64_t>(min(t0 + 16 * mt + (lane & 15), nT - 1)) * d +
+               8 * (lane >> 4);
+  // transpose-read address of this lane in a staged k-step (column group 0)
+  const int rd = (8 * (lane >> 4) + ((lane & 15) >> 2)) * ROWB + 8 * (lane & 3);
+
+  f32x4_t acc[MT][G];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int g = 0; g < G; ++g) acc[mt][g] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  // P k-steps per batch are loaded at once (sub-batch by sub-batch, so the
+  // first can be staged while the rest are in flight), then staged and
+  // multiplied U steps at a time.  Every load is unconditional and in
+  // bounds: steps past the wave's range read the last step or row of d,
+  // chunks past E re-read the row's last chunk; what they bring is staged
+  // but never multiplied (steps) or only reaches dropped columns (chunks).
+  constexpr int NB = P / U;
+  for (int s = s_begin; s < s_end; s += P) {
+    const int cnt = min(P, s_end - s);         // k-steps in this batch
+    u32x4_t xa[MT][P];
+    u32x4_t wa[NB][NWC];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+#pragma unroll
+      for (int u = b * U; u < b * U + U; ++u)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+          xa[mt][u] = *reinterpret_cast<const u32x4_t*>(xrow[mt] + min(s + u, nsteps - 1) * 32);
+      // chunk slot c = lane + 64 i: staged row c / CPR, 16-byte column c % CPR
+#pragma unroll
+      for (int i = 0; i < NWC; ++i) {
+        const int c = lane + kWave * i, r = c / CPR, cc = min(c % CPR, cpe - 1);
+        const int row = min((s + b * U) * 32 + r, d - 1);
+        wa[b][i] = *reinterpret_cast<const u32x4_t*>(wg + static_cast<int64_t>(row) * E + cc * 8);
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      wave_lds_order();                        // the previous sub-batch's reads are done
+#pragma unroll
+      for (int i = 0; i < NWC; ++i) {
+        const int c = lane + kWave * i;
+        *reinterpret_cast<u32x4_t*>(slice + (c / CPR) * ROWB + (c % CPR) * 16) = wa[b][i];
+      }
+      wave_lds_order();
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        // steps past the range multiply a zero A operand (the staged rows
+        // there are finite W_gate rows, so they add exact zeros)
+        const u32x4_t a = b * U + u < cnt ? xa[0][b * U + u] : u32x4_t{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          const bf16x8_t bf = read_b_frag(slice + u * 32 * ROWB + rd + 32 * g, 4 * ROWB);
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) {
+            const u32x4_t am = mt == 0 ? a : (b * U + u < cnt ? xa[mt][b * U + u]
+                                                               : u32x4_t{0u, 0u, 0u, 0u});
+            acc[mt][g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                __builtin_bit_cast(bf16x8_t, am), bf, acc[mt][g], 0, 0, 0);
+          }
+        }
+      }
+    }
+  }
+
+  // partial logits of every wave, red[w][t][e] (over the staging slices)
+  __syncthreads();
+  float* red = reinterpret_cast<float*>(smem_m);
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+        red[(wave * TB + 16 * mt + 4 * (lane >> 4) + v) * EP + 16 * g + (lane & 15)] =
+            acc[mt][g][v];
+  __syncthreads();
+  // sum in wave order into red[0] (each element read and written by one
+  // thread), store the logits
+  for (int q = threadIdx.x; q < TB * EP; q += blockDim.x) {
+    float sum = red[q];
+    for (int w = 1; w < nw; ++w) sum += red[w * TB * EP + q];
+    red[q] = sum;
+    const int t = q / EP, e = q % EP;
+    if (t0 + t < nT && e < E) logits[static_cast<int64_t>(t0 + t) * E + e] = sum;
+  }
+  if (gp.v3 == 2) return;
+  __syncthreads();
+  if (gp.v3 == 0 && E <= kWave) {
+    // four tokens per wavefront
+    for (int tt = 4 * wave; tt < TB; tt += 4 * nw) {
+      const int ntok = min(4, nT - (t0 + tt));
+      if (ntok <= 0) break;
+      float v[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) v[r] = lane < E ? red[(tt + r) * EP + lane] : 0.f;
+      topk_select4(v, E, k, lane, ntok, topk_idx + static_cast<int64_t>(t0 + tt) * k,
+                   topk_w + static_cast<int64_t>(t0 + tt) * k);
+    }
+    return;
+  }
+  for (int tt = wave; tt < TB; tt += nw) {
+    const int t = t0 + tt;
+    if (t >= nT) break;
+    const float* row = red + tt * EP;
+    if (gp.v3 == 1) {
+      // E floats of scratch per wave past the summed rows (nw >= 2 leaves
+      // (nw - 1) * TB * EP free floats there)
+      v3_select(row, red + TB * EP + wave * EP, gp, E, k, lane,
+                topk_idx + static_cast<int64_t>(t) * k, topk_w + static_cast<int64_t>(t) * k);
+      continue;
+    }
+    float v[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int e = lane + kWave * r;
+      v[r] = (e < E) ? row[e] : 0.f;
+    }
+    topk_select(v, E, k, lane, topk_idx + static_cast<int64_t>(t) * k,
+                topk_w + static_cast<int64_t>(t) * k);
+  }
+}
+
 struct RouterPlan {
   int E_pad, ES, EPL, DS;
   int nblocks, nchunk;
@@ -468,6 +728,74 @@ hipError_t dispatch_epl(int64_t T_, int64_t d, int E, int k, const void* x, cons
   }
 }
 
+// Matrix-core router plan: EP = E rounded up to a power of two (at least
+// 16), 32 tokens per block once that still gives 256 blocks, U k-steps
+// staged per batch (fewer for wide E, so a wave's slice stays small), and
+// enough waves (d-ranges) per block to put about 2048 waves on the chip,
+// within 64 KB of LDS.
+struct MfmaRouterPlan {
+  int EP, MT, U, nw, nblocks;
+  size_t lds;
+};
+
+bool mfma_router_applies(int64_t T, int64_t d, int E, bool bf16) {
+  return bf16 && E % 8 == 0 && plan_router(T, d, E).S == 1;
+}
+
+MfmaRouterPlan plan_mfma_router(int64_t T, int64_t d, int E) {
+  MfmaRouterPlan p;
+  p.EP = 16;
+  while (p.EP < E) p.EP <<= 1;
+  p.MT = (T + 31) / 32 >= 256 ? 2 : 1;
+  p.U = p.EP <= 32 ? 4 : (p.EP == 64 ? 2 : 1);
+  const int TB = 16 * p.MT;
+  p.nblocks = static_cast<int>((T + TB - 1) / TB);
+  const size_t slice = static_cast<size_t>(32) * p.U * (p.EP * 2 + 16);
+  const size_t per_wave = std::max(slice, static_cast<size_t>(TB) * p.EP * 4);
+  int nw = (2048 + p.nblocks - 1) / p.nblocks;
+  nw = std::min(nw, kMaxWavesR);
+  nw = std::min(nw, static_cast<int>(d / 32));
+  nw = std::min(nw, static_cast<int>(65536 / per_wave));
+  p.nw = std::max(nw, 2);
+  p.lds = per_wave * p.nw;
+  return p;
+}
+
+template <int EP, int MT>
+hipError_t launch_mfma_mt(const MfmaRouterPlan& p, int64_t T, int64_t d, int E, int k,
+                          const void* x, const void* wg, float* logits, int32_t* idx, float* w,
+                          const GateParams& gp, hipStream_t s) {
+  constexpr int U = EP <= 32 ? 4 : (EP == 64 ? 2 : 1);
+  // k-steps loaded per batch: what about 200 VGPRs hold next to the
+  // accumulators
+  constexpr int P = EP == 16 ? 16 : EP == 32 ? 8 : EP == 64 ? 6 : EP == 128 ? 3 : (MT == 1 ? 2 : 1);
+  hipLaunchKernelGGL((router_mfma_kernel<EP, MT, U, P>), dim3(p.nblocks), dim3(p.nw * kWave),
+                     p.lds, s, static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(wg),
+                     logits, idx, w, static_cast<int>(T), static_cast<int>(d), E, k, gp);
+  return hipGetLastError();
+}
+
+template <int EP>
+hipError_t launch_mfma_ep(const MfmaRouterPlan& p, int64_t T, int64_t d, int E, int k,
+                          const void* x, const void* wg, float* logits, int32_t* idx, float* w,
+                          const GateParams& gp, hipStream_t s) {
+  if (p.MT == 2) return launch_mfma_mt<EP, 2>(p, T, d, E, k, x, wg, logits, idx, w, gp, s);
+  return launch_mfma_mt<EP, 1>(p, T, d, E, k, x, wg, logits, idx, w, gp, s);
+}
+
+hipError_t launch_mfma_router(int64_t T, int64_t d, int E, int k, const void* x, const void* wg,
+                              float* logits, int32_t* idx, float* w, const GateParams& gp,
+                              hipStream_t s) {
+  const MfmaRouterPlan p = plan_mfma_router(T, d, E);
+  switch (p.EP) {
+    case 16: return launch_mfma_ep<16>(p, T, d, E, k, x, wg, logits, idx, w, gp, s);
+    case 32: return launch_mfma_ep<32>(p, T, d, E, k, x, wg, logits, idx, w, gp, s);
+    case 64: return launch_mfma_ep<64>(p, T, d, E, k, x, wg, logits, idx, w, gp, s);
+    case 128: return launch_mfma_ep<128>(p, T, d, E, k, x, wg, logits, idx, w, gp, s);
+    default: return launch_mfma_ep<256>(p, T, d, E, k, x, wg, logits, idx, w, gp, s);
+  }
+}
+
 // Balance-bias step ("CMU 11-868 Lecture 17", section 3.4): thread e
 // compares counts[e] * E with T * k (the mean load, exactly).
 __global__ __launch_bounds__(256) void update_bias_kernel(const int32_t* __restrict__ counts,
@@ -491,6 +819,8 @@ hipError_t launch_route(int64_t T, int64_t d, int E, int k, bool bf16, const voi
                         const void* w_gate, float* logits, int32_t* topk_idx, float* topk_w,
                         void* ws, const GateParams& gp, hipStream_t s) {
   float* partial = static_cast<float*>(ws);
+  if (mfma_router_applies(T, d, E, bf16))
+    return launch_mfma_router(T, d, E, k, x, w_gate, logits, topk_idx, topk_w, gp, s);
   if (bf16)
     return dispatch_epl<uint16_t>(T, d, E, k, x, w_gate, logits, topk_idx, topk_w, partial, gp,
                                   s);
