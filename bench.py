@@ -37,8 +37,8 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 # they were taken with (softmax router).  A changed
 # kernel reports null until it is measured again.
 MEASURED_TRAFFIC = {
-    ("mixtral_prefill", "df0078bdbd1090b5"): 9.4461e9,
-    ("dsv3_decode", "df0078bdbd1090b5"): 1.9663e10,
+    ("mixtral_prefill", "01914064b5b39fa4"): 9.4449e9,
+    ("dsv3_decode", "01914064b5b39fa4"): 1.9662e10,
 }
 
 

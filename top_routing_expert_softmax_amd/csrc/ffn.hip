@@ -94,13 +94,22 @@ __global__ __launch_bounds__(kWave) void tile_table_kernel(const int32_t* __rest
   if (sk_count != nullptr)
     for (int i = lane; i < 2 * kMaxCUs; i += kWave) sk_count[i] = 0u;
   const int nseg = E + Es;
+  // the lane's segment bounds, loaded together (indices clamped to E, so
+  // every load is in bounds and none waits behind a branch)
+  int o0[5], o1[5];
+#pragma unroll
+  for (int q = 0; q < 5; ++q) {
+    const int s = lane * 5 + q;
+    o0[q] = offsets[min(s, E)];
+    o1[q] = offsets[min(s + 1, E)];
+  }
   int cnt[5];
   int tot = 0;
 #pragma unroll
   for (int q = 0; q < 5; ++q) {
     const int s = lane * 5 + q;
     int rows = 0;
-    if (s < E) rows = offsets[s + 1] - offsets[s];
+    if (s < E) rows = o1[q] - o0[q];
     else if (s < nseg) rows = T;
     cnt[q] = (rows + BM - 1) / BM;
     tot += cnt[q];
@@ -129,9 +138,9 @@ __global__ __launch_bounds__(kWave) void tile_table_kernel(const int32_t* __rest
       int4 t;
       t.x = s | (g_size << 16) | ((i - g_first) << 20);
       if (s < E) {
-        const int r0 = offsets[s] + i * BM;
+        const int r0 = o0[q] + i * BM;
         t.y = r0;
-        t.z = min(BM, offsets[s + 1] - r0);
+        t.z = min(BM, o1[q] - r0);
         t.w = r0;
       } else {
         const int m0 = i * BM;

@@ -143,20 +143,6 @@ __device__ __forceinline__ float from_order_key(uint32_t key) {
   return __uint_as_float(u);
 }
 
-// Largest 32-bit value over the wavefront, returned to every lane: DPP
-// moves within each row of 16 lanes (quad swaps, then rotations by 4 and
-// 8), then the four row maxima through scalar registers.  Every lane must
-// be active.
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-  v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0xB1, 0xF, 0xF, false)));
-  v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x4E, 0xF, 0xF, false)));
-  v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x124, 0xF, 0xF, false)));
-  v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x128, 0xF, 0xF, false)));
-  const uint32_t r0 = __builtin_amdgcn_readlane(v, 0), r1 = __builtin_amdgcn_readlane(v, 16);
-  const uint32_t r2 = __builtin_amdgcn_readlane(v, 32), r3 = __builtin_amdgcn_readlane(v, 48);
-  return max(max(r0, r1), max(r2, r3));
-}
-
 // Among entries r < 4 of every lane whose key equals best (wave-uniform),
 // the lowest expert index lane + 64 r.  best must be held by some entry.
 __device__ __forceinline__ int lowest_holder(const uint32_t (&key)[4], uint32_t best) {

@@ -2,9 +2,11 @@
 // 3.2 (f_i, P_i, L_balance) and 4.3 (drop rate), "MoE deep dive" section 3.2
 // (z-loss), all unscaled.
 //
-// Pass 1: each block takes a contiguous token range; one wavefront per
-// token computes softmax and log-sum-exp in fp32 (each lane holds up to four
-// logits), and fp64 per-lane accumulators collect sum_t p_ti and sum_t lse^2.
+// Pass 1: each block takes a contiguous token range; a wavefront computes
+// softmax and log-sum-exp in fp32 for one token (each lane holding up to
+// four logits) or, when E <= 64, for four tokens at once (one per logit
+// slot), and fp64 per-lane accumulators collect sum_t p_ti and
+// sum_t lse^2.
 // The block folds its four waves in a fixed order into one partial row.
 // Pass 2: one block adds the partial rows (spread over all its threads
 // whatever E is) and forms f, P, L_balance, z and the drop rate in fp64,
@@ -19,6 +21,10 @@ namespace {
 
 constexpr int kWavesS = 4;
 
+// Softmax and log-sum-exp of the tokens a lane's four logit slots hold:
+// with E <= 64 slot r is token t + r (expert lane), otherwise the four
+// slots are experts lane + 64 r of token t.  The wave reductions are DPP
+// ones (fixed order); the four tokens' reductions run side by side.
 __global__ __launch_bounds__(kWavesS * kWave) void stats_partial_kernel(
     const float* __restrict__ logits, double* __restrict__ part_P,
     double* __restrict__ part_z, int nT, int E, int tokens_per_block) {
@@ -30,31 +36,54 @@ __global__ __launch_bounds__(kWavesS * kWave) void stats_partial_kernel(
   double accz = 0.0;
   const int tb0 = blockIdx.x * tokens_per_block;
   const int tb1 = min(nT, tb0 + tokens_per_block);
-  for (int t = tb0 + wave; t < tb1; t += kWavesS) {
-    const float* row = logits + static_cast<int64_t>(t) * E;
-    float g[4];
-    float m = -INFINITY;
+  if (E <= kWave) {
+    for (int t = tb0 + 4 * wave; t < tb1; t += 4 * kWavesS) {
+      float g[4], m[4], ex[4], s[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int e = lane + kWave * r;
-      g[r] = (e < E) ? row[e] : -INFINITY;
-      m = fmaxf(m, g[r]);
+      for (int r = 0; r < 4; ++r)
+        g[r] = lane < E && t + r < tb1 ? logits[static_cast<int64_t>(t + r) * E + lane] : -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) m[r] = wave_max_dpp(g[r]);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) ex[r] = lane < E && t + r < tb1 ? expf(g[r] - m[r]) : 0.f;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) s[r] = wave_sum_dpp(ex[r]);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        if (t + r < tb1) {
+          accP[0] += static_cast<double>(ex[r] * (1.0f / s[r]));
+          const double lse = static_cast<double>(m[r]) + log(static_cast<double>(s[r]));
+          accz += lse * lse;   // same value on every lane; lane 0's copy is used
+        }
+      }
     }
-    m = wave_max(m);
-    float ex[4];
-    float s = 0.f;
+  } else {
+    for (int t = tb0 + wave; t < tb1; t += kWavesS) {
+      const float* row = logits + static_cast<int64_t>(t) * E;
+      float g[4];
+      float m = -INFINITY;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int e = lane + kWave * r;
-      ex[r] = (e < E) ? expf(g[r] - m) : 0.f;
-      s += ex[r];
+      for (int r = 0; r < 4; ++r) {
+        const int e = lane + kWave * r;
+        g[r] = (e < E) ? row[e] : -INFINITY;
+        m = fmaxf(m, g[r]);
+      }
+      m = wave_max_dpp(m);
+      float ex[4];
+      float s = 0.f;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int e = lane + kWave * r;
+        ex[r] = (e < E) ? expf(g[r] - m) : 0.f;
+        s += ex[r];
+      }
+      s = wave_sum_dpp(s);
+      const float inv = 1.0f / s;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) accP[r] += static_cast<double>(ex[r] * inv);
+      const double lse = static_cast<double>(m) + log(static_cast<double>(s));
+      accz += lse * lse;
     }
-    s = wave_sum(s);
-    const float inv = 1.0f / s;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) accP[r] += static_cast<double>(ex[r] * inv);
-    const double lse = static_cast<double>(m) + log(static_cast<double>(s));
-    accz += lse * lse;   // same value on every lane; lane 0's copy is used
   }
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
@@ -95,13 +124,22 @@ __global__ __launch_bounds__(1024) void stats_final_kernel(
   {
     double acc8[8] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
     double z8[8] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
+    // every load in bounds and unconditional, so the eight are in flight
+    // together; rows past nblk and experts past E add nothing
+    const int ec = min(e, E - 1);
     for (int b0 = g; b0 < nblk; b0 += 8 * G) {
+      double vP[8], vz[8];
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
-        const int b = b0 + q * G;
-        if (b < nblk) {
-          if (e < E) acc8[q] += part_P[static_cast<int64_t>(b) * E + e];
-          if (e == 0) z8[q] += part_z[b];
+        const int b = min(b0 + q * G, nblk - 1);
+        vP[q] = part_P[static_cast<int64_t>(b) * E + ec];
+        vz[q] = part_z[b];
+      }
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        if (b0 + q * G < nblk) {
+          if (e < E) acc8[q] += vP[q];
+          if (e == 0) z8[q] += vz[q];
         }
       }
     }
