@@ -14,10 +14,11 @@
 // blocks that write partial logits to the workspace; a select kernel adds
 // the S partials in a fixed order and runs the same top-k.
 //
-// Many tokens in bf16 with E a multiple of 8: the matrix-core kernel
-// router_mfma_kernel below (its comment has the details) computes the same
-// logits with MFMA, also exactly on the dyadic grid, and runs the same
-// epilogue.
+// bf16 with E a multiple of 8: the matrix-core kernel router_mfma_kernel
+// below (its comment has the details) computes the same logits with MFMA,
+// also exactly on the dyadic grid, and runs the same epilogue; with few
+// tokens it splits d over blocks in the same way and hands its partial
+// logits to the same select kernel.
 //
 // Top-k: one wavefront per token (four tokens per wavefront when E <= 64),
 // each lane holding up to four logits; k rounds of a wave-wide max of the
@@ -411,8 +412,8 @@ __global__ __launch_bounds__(kMaxWavesR * kWave) void router_kernel(
 
 // Decode: logits = sum over the S d-splits, then top-k.  One block of 256
 // threads per token, thread e < E adds partial[s][t][e] into eight
-// accumulators (s mod 8) that are combined in a fixed order; wavefront 0
-// then selects from the LDS copy of the row.
+// accumulators (s mod 8, splits in order) that are combined in a fixed
+// order; wavefront 0 then selects from the LDS copy of the row.
 __global__ __launch_bounds__(256) void router_select_kernel(
     const float* __restrict__ partial, float* __restrict__ logits,
     int32_t* __restrict__ topk_idx, float* __restrict__ topk_w, int nT, int E, int k, int S,
@@ -422,12 +423,18 @@ __global__ __launch_bounds__(256) void router_select_kernel(
   const int t = blockIdx.x;
   const int e = threadIdx.x;
   float s8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  if (e < E) {
-    for (int s0 = 0; s0 < S; s0 += 8) {
+  // split s goes to accumulator s mod 8, splits in order; the loads of 32
+  // splits go out together: unconditional, at indices clamped into the
+  // buffer (splits past S and experts past E add nothing)
+  const int ec = min(e, E - 1);
+  for (int s0 = 0; s0 < S; s0 += 32) {
+    float v[32];
 #pragma unroll
-      for (int q = 0; q < 8; ++q)
-        if (s0 + q < S) s8[q] += partial[(static_cast<int64_t>(s0 + q) * nT + t) * E + e];
-    }
+    for (int q = 0; q < 32; ++q)
+      v[q] = partial[(static_cast<int64_t>(min(s0 + q, S - 1)) * nT + t) * E + ec];
+#pragma unroll
+    for (int q = 0; q < 32; ++q)
+      if (e < E && s0 + q < S) s8[q % 8] += v[q];
   }
   const float g = ((s8[0] + s8[1]) + (s8[2] + s8[3])) + ((s8[4] + s8[5]) + (s8[6] + s8[7]));
   if (e < E) logits[static_cast<int64_t>(t) * E + e] = g;
@@ -494,11 +501,14 @@ struct MfmaRouterGeom {
   static constexpr int NWC = 32 * U * CPR / kWave;   // chunk slots per lane
 };
 
-template <int EP, int MT, int U, int P>
+// SPLIT = true (few tokens): block (x, y) takes the k-steps
+// [y * steps_per_split, +steps_per_split) of d and writes its partial logits
+// to partial[y][t][e]; router_select_kernel adds the splits and selects.
+template <int EP, int MT, int U, int P, bool SPLIT>
 __global__ __launch_bounds__(kMaxWavesR * kWave) void router_mfma_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wg, float* __restrict__ logits,
-    int32_t* __restrict__ topk_idx, float* __restrict__ topk_w, int nT, int d, int E, int k,
-    GateParams gp) {
+    int32_t* __restrict__ topk_idx, float* __restrict__ topk_w, float* __restrict__ partial,
+    int nT, int d, int E, int k, int steps_per_split, GateParams gp) {
   using Geo = MfmaRouterGeom<EP, U>;
   constexpr int G = Geo::G, ROWB = Geo::ROWB, CPR = Geo::CPR, NWC = Geo::NWC;
   constexpr int TB = 16 * MT;
@@ -509,9 +519,11 @@ __global__ __launch_bounds__(kMaxWavesR * kWave) void router_mfma_kernel(
   const int t0 = blockIdx.x * TB;
   const int cpe = E / 8;                       // 16-byte chunks per W_gate row
   const int nsteps = d / 32;
-  const int spw = (nsteps + nw - 1) / nw;
-  const int s_begin = wave * spw;
-  const int s_end = min(nsteps, s_begin + spw);
+  const int sp0 = SPLIT ? blockIdx.y * steps_per_split : 0;
+  const int sp1 = SPLIT ? min(nsteps, sp0 + steps_per_split) : nsteps;
+  const int spw = (sp1 - sp0 + nw - 1) / nw;
+  const int s_begin = sp0 + wave * spw;
+  const int s_end = min(sp1, s_begin + spw);
   char* slice = smem_m + wave * Geo::SLICE;
 
   const uint16_t* xrow[MT];
@@ -596,15 +608,16 @@ __global__ __launch_bounds__(kMaxWavesR * kWave) void router_mfma_kernel(
             acc[mt][g][v];
   __syncthreads();
   // sum in wave order into red[0] (each element read and written by one
-  // thread), store the logits
+  // thread), store the logits (or this split's partial logits)
+  float* dst = SPLIT ? partial + static_cast<int64_t>(blockIdx.y) * nT * E : logits;
   for (int q = threadIdx.x; q < TB * EP; q += blockDim.x) {
     float sum = red[q];
     for (int w = 1; w < nw; ++w) sum += red[w * TB * EP + q];
     red[q] = sum;
     const int t = q / EP, e = q % EP;
-    if (t0 + t < nT && e < E) logits[static_cast<int64_t>(t0 + t) * E + e] = sum;
+    if (t0 + t < nT && e < E) dst[static_cast<int64_t>(t0 + t) * E + e] = sum;
   }
-  if (gp.v3 == 2) return;
+  if (SPLIT || gp.v3 == 2) return;
   __syncthreads();
   if (gp.v3 == 0 && E <= kWave) {
     // four tokens per wavefront
@@ -718,29 +731,38 @@ hipError_t dispatch_epl(int64_t T_, int64_t d, int E, int k, const void* x, cons
 // 16), 32 tokens per block once that still gives 256 blocks, U k-steps
 // staged per batch (fewer for wide E, so a wave's slice stays small), and
 // enough waves (d-ranges) per block to put about 2048 waves on the chip,
-// within 64 KB of LDS.
+// within 64 KB of LDS.  With few tokens (max_splits > 1, the split count the
+// workspace holds) d is also split over blocks: S <= max_splits splits of
+// whole k-steps, aiming at 256 blocks.
 struct MfmaRouterPlan {
   int EP, MT, U, nw, nblocks;
+  int S, sps;             // d-splits and k-steps per split (S = 1: no split)
   size_t lds;
 };
 
-bool mfma_router_applies(int64_t T, int64_t d, int E, bool bf16) {
-  return bf16 && E % 8 == 0 && plan_router(T, d, E).S == 1;
-}
+bool mfma_router_applies(int E, bool bf16) { return bf16 && E % 8 == 0; }
 
-MfmaRouterPlan plan_mfma_router(int64_t T, int64_t d, int E) {
+MfmaRouterPlan plan_mfma_router(int64_t T, int64_t d, int E, int max_splits) {
   MfmaRouterPlan p;
   p.EP = 16;
   while (p.EP < E) p.EP <<= 1;
-  p.MT = (T + 31) / 32 >= 256 ? 2 : 1;
+  p.MT = max_splits == 1 && (T + 31) / 32 >= 256 ? 2 : 1;
   p.U = p.EP <= 32 ? 4 : (p.EP == 64 ? 2 : 1);
   const int TB = 16 * p.MT;
   p.nblocks = static_cast<int>((T + TB - 1) / TB);
+  const int nsteps = static_cast<int>(d / 32);
+  p.S = 1;
+  p.sps = nsteps;
+  if (max_splits > 1) {
+    const int want = std::max(1, std::min(max_splits, (256 + p.nblocks - 1) / p.nblocks));
+    p.sps = (nsteps + want - 1) / want;
+    p.S = (nsteps + p.sps - 1) / p.sps;
+  }
   const size_t slice = static_cast<size_t>(32) * p.U * (p.EP * 2 + 16);
   const size_t per_wave = std::max(slice, static_cast<size_t>(TB) * p.EP * 4);
-  int nw = (2048 + p.nblocks - 1) / p.nblocks;
+  int nw = (2048 + p.nblocks * p.S - 1) / (p.nblocks * p.S);
   nw = std::min(nw, kMaxWavesR);
-  nw = std::min(nw, static_cast<int>(d / 32));
+  nw = std::min(nw, p.sps);
   nw = std::min(nw, static_cast<int>(65536 / per_wave));
   p.nw = std::max(nw, 2);
   p.lds = per_wave * p.nw;
@@ -750,35 +772,48 @@ MfmaRouterPlan plan_mfma_router(int64_t T, int64_t d, int E) {
 template <int EP, int MT>
 hipError_t launch_mfma_mt(const MfmaRouterPlan& p, int64_t T, int64_t d, int E, int k,
                           const void* x, const void* wg, float* logits, int32_t* idx, float* w,
-                          const GateParams& gp, hipStream_t s) {
+                          float* partial, const GateParams& gp, hipStream_t s) {
   constexpr int U = EP <= 32 ? 4 : (EP == 64 ? 2 : 1);
   // k-steps loaded per batch: what about 200 VGPRs hold next to the
   // accumulators
   constexpr int P = EP == 16 ? 16 : EP == 32 ? 8 : EP == 64 ? 6 : EP == 128 ? 3 : (MT == 1 ? 2 : 1);
-  hipLaunchKernelGGL((router_mfma_kernel<EP, MT, U, P>), dim3(p.nblocks), dim3(p.nw * kWave),
-                     p.lds, s, static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(wg),
-                     logits, idx, w, static_cast<int>(T), static_cast<int>(d), E, k, gp);
-  return hipGetLastError();
+  const uint16_t* xb = static_cast<const uint16_t*>(x);
+  const uint16_t* wb = static_cast<const uint16_t*>(wg);
+  if (p.S == 1) {
+    hipLaunchKernelGGL((router_mfma_kernel<EP, MT, U, P, false>), dim3(p.nblocks),
+                       dim3(p.nw * kWave), p.lds, s, xb, wb, logits, idx, w, nullptr,
+                       static_cast<int>(T), static_cast<int>(d), E, k, p.sps, gp);
+    return hipGetLastError();
+  }
+  if constexpr (MT == 1) {
+    hipLaunchKernelGGL((router_mfma_kernel<EP, 1, U, P, true>), dim3(p.nblocks, p.S),
+                       dim3(p.nw * kWave), p.lds, s, xb, wb, logits, idx, w, partial,
+                       static_cast<int>(T), static_cast<int>(d), E, k, p.sps, gp);
+    hipLaunchKernelGGL(router_select_kernel, dim3(static_cast<unsigned>(T)), dim3(256), 0, s,
+                       partial, logits, idx, w, static_cast<int>(T), E, k, p.S, gp);
+    return hipGetLastError();
+  }
+  return hipErrorInvalidValue;                   // the plan splits only with MT = 1
 }
 
 template <int EP>
 hipError_t launch_mfma_ep(const MfmaRouterPlan& p, int64_t T, int64_t d, int E, int k,
                           const void* x, const void* wg, float* logits, int32_t* idx, float* w,
-                          const GateParams& gp, hipStream_t s) {
-  if (p.MT == 2) return launch_mfma_mt<EP, 2>(p, T, d, E, k, x, wg, logits, idx, w, gp, s);
-  return launch_mfma_mt<EP, 1>(p, T, d, E, k, x, wg, logits, idx, w, gp, s);
+                          float* partial, const GateParams& gp, hipStream_t s) {
+  if (p.MT == 2) return launch_mfma_mt<EP, 2>(p, T, d, E, k, x, wg, logits, idx, w, partial, gp, s);
+  return launch_mfma_mt<EP, 1>(p, T, d, E, k, x, wg, logits, idx, w, partial, gp, s);
 }
 
 hipError_t launch_mfma_router(int64_t T, int64_t d, int E, int k, const void* x, const void* wg,
-                              float* logits, int32_t* idx, float* w, const GateParams& gp,
-                              hipStream_t s) {
-  const MfmaRouterPlan p = plan_mfma_router(T, d, E);
+                              float* logits, int32_t* idx, float* w, float* partial,
+                              const GateParams& gp, hipStream_t s) {
+  const MfmaRouterPlan p = plan_mfma_router(T, d, E, plan_router(T, d, E).S);
   switch (p.EP) {
-    case 16: return launch_mfma_ep<16>(p, T, d, E, k, x, wg, logits, idx, w, gp, s);
-    case 32: return launch_mfma_ep<32>(p, T, d, E, k, x, wg, logits, idx, w, gp, s);
-    case 64: return launch_mfma_ep<64>(p, T, d, E, k, x, wg, logits, idx, w, gp, s);
-    case 128: return launch_mfma_ep<128>(p, T, d, E, k, x, wg, logits, idx, w, gp, s);
-    default: return launch_mfma_ep<256>(p, T, d, E, k, x, wg, logits, idx, w, gp, s);
+    case 16: return launch_mfma_ep<16>(p, T, d, E, k, x, wg, logits, idx, w, partial, gp, s);
+    case 32: return launch_mfma_ep<32>(p, T, d, E, k, x, wg, logits, idx, w, partial, gp, s);
+    case 64: return launch_mfma_ep<64>(p, T, d, E, k, x, wg, logits, idx, w, partial, gp, s);
+    case 128: return launch_mfma_ep<128>(p, T, d, E, k, x, wg, logits, idx, w, partial, gp, s);
+    default: return launch_mfma_ep<256>(p, T, d, E, k, x, wg, logits, idx, w, partial, gp, s);
   }
 }
 
@@ -805,8 +840,8 @@ hipError_t launch_route(int64_t T, int64_t d, int E, int k, bool bf16, const voi
                         const void* w_gate, float* logits, int32_t* topk_idx, float* topk_w,
                         void* ws, const GateParams& gp, hipStream_t s) {
   float* partial = static_cast<float*>(ws);
-  if (mfma_router_applies(T, d, E, bf16))
-    return launch_mfma_router(T, d, E, k, x, w_gate, logits, topk_idx, topk_w, gp, s);
+  if (mfma_router_applies(E, bf16))
+    return launch_mfma_router(T, d, E, k, x, w_gate, logits, topk_idx, topk_w, partial, gp, s);
   if (bf16)
     return dispatch_epl<uint16_t>(T, d, E, k, x, w_gate, logits, topk_idx, topk_w, partial, gp,
                                   s);
