@@ -34,7 +34,7 @@ class MoEConfig:
     wg_kind: str           # "uniform": n ~ U{-8..8}; "gauss": n = clip(round(N(0, wg_sd^2)), +-255)
     wg_sd: float = 0.0
     zipf_s: float = 0.0    # > 0: x[:,0] = 1 and W_gate[0,:] holds Zipf-ranked offsets
-    zipf_tau: float = 0.0  # temperature of those offsets (chosen once, see DESIGN)
+    zipf_tau: float = 0.0  # temperature of those offsets (oracle/calibrate_zipf.py picks it)
     w_sd: float = 0.02     # expert weights ~ N(0, w_sd^2)
     note: str = field(default="", compare=False)
 
