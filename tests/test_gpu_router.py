@@ -1,6 +1,7 @@
 """GPU parity of moe_route on its own, across both router kernels: the
-matrix-core one (bf16, E a multiple of 8, enough tokens for one block per
-16 or 32 tokens) and the fp32 FMA one (fp32, other E, few tokens).  Logits
+matrix-core one (bf16, E a multiple of 8; with few tokens d is split over
+blocks and a select kernel adds the splits) and the fp32 FMA one (fp32,
+other E).  Logits
 and chosen experts bit-exact against the oracle, weights within 2e-6.
 
 The cases reach every expert padding of the matrix-core kernel (E rounded
@@ -44,6 +45,12 @@ ROUTER_CASES = {
     "mfma_E160": ("dsv3_decode", dict(T=1031, d_model=1024, E=160, k=6)),
     # E = 256 in blocks of 32 tokens: two waves per block
     "mfma_E256_tiles32": ("dsv3_decode", dict(T=8208, d_model=768, E=256, k=8)),
+    # few tokens: the matrix-core kernel with d split over blocks, then the
+    # select kernel; 37 tokens (the last tile holds 5), 50 k-steps in 10
+    # splits of 5, one k-step per wave
+    "mfma_split_E24": ("mixtral_prefill", dict(T=37, d_model=1600, E=24, k=3)),
+    # split path with 256 experts and 20 tokens
+    "mfma_split_E256": ("dsv3_decode", dict(T=20, d_model=1024, E=256, k=8)),
     # E not a multiple of 8 in bf16: the fp32 FMA kernel
     "fma_bf16_E12": ("mixtral_prefill", dict(T=1100, d_model=512, E=12, k=2)),
     # fp32 activations and weights: the fp32 FMA kernel
@@ -64,8 +71,10 @@ def test_route_matches_oracle(label):
     logits = torch.empty((T, E), dtype=torch.float32, device="cuda")
     idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
     w = torch.empty((T, k), dtype=torch.float32, device="cuda")
-    # the large-T path takes no workspace
-    M.moe_route(x_dev, wg_dev, k, logits, idx, w, None)
+    # the split path needs the workspace; the large-T path takes none
+    nbytes = M.moe_workspace_size(T, d, E, 0, k, 64, x_dev.dtype)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda") if T < 1024 else None
+    M.moe_route(x_dev, wg_dev, k, logits, idx, w, ws)
     torch.cuda.synchronize()
     r = O.route(x, wg, k)
     assert np.array_equal(logits.cpu().numpy().astype(np.float64), r["logits"]), "logits differ"
