@@ -56,6 +56,9 @@ EC_CASES = {
     "largest_cap": ("mixtral_prefill", dict(T=8192, d_model=128, E=2, k=1), 1.0),
     # 25 picks per expert (32 padded): the sort needs wave shuffles only
     "small_cap": ("mixtral_prefill", dict(T=200, d_model=128, E=8, k=1), 1.0),
+    # few tokens and a long d: the logits come from the router's d-split
+    # path (partial logits summed by the select kernel, no top-k)
+    "split_router": ("mixtral_prefill", dict(T=40, d_model=2048, E=8, k=1), 1.0),
 }
 
 
