@@ -101,3 +101,40 @@ def test_route_all_ties_take_the_lowest_experts(E):
     assert torch.count_nonzero(logits).item() == 0
     assert np.array_equal(idx.cpu().numpy(), np.tile(np.arange(k), (T, 1)))
     np.testing.assert_allclose(w.cpu().numpy(), 1.0 / k, rtol=1e-6)
+
+
+@pytest.mark.parametrize("T", [2048, 40])
+def test_route_off_the_grid_within_the_fp32_sum_bound(T):
+    """Seeded Gaussian bf16 x and W_gate (not on the dyadic grid), both
+    matrix-core paths (T = 2048 in one pass, T = 40 with d split over
+    blocks).  Every logit is within the bound of a d-term fp32 sum,
+    gamma_d * sum_i |x_ti w_ie| with gamma_d = d u / (1 - d u), u = 2^-24,
+    of the oracle's fp64 value; where the k-th and (k+1)-th largest oracle
+    logits of a token are further apart than twice that bound, the chosen
+    experts are the oracle's."""
+    import top_routing_expert_softmax_amd as M
+    d, E, k = 1024, 64, 6
+    rng = np.random.default_rng(1234 + T)
+    bf = torch.bfloat16
+    x_t = torch.from_numpy(rng.standard_normal((T, d), dtype=np.float32)).to(bf)
+    w_t = torch.from_numpy((rng.standard_normal((d, E), dtype=np.float32) * 0.05)).to(bf)
+    x = x_t.float().numpy().astype(np.float64)
+    wg = w_t.float().numpy().astype(np.float64)
+    logits = torch.empty((T, E), dtype=torch.float32, device="cuda")
+    idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    ws = torch.empty(M.moe_workspace_size(T, d, E, 0, k, 64, bf), dtype=torch.uint8, device="cuda")
+    M.moe_route(x_t.cuda(), w_t.cuda(), k, logits, idx, w, ws)
+    torch.cuda.synchronize()
+    ref = O.router_logits(x, wg)
+    u = 2.0 ** -24
+    gamma = d * u / (1 - d * u)
+    bound = gamma * (np.abs(x) @ np.abs(wg))
+    err = np.abs(logits.cpu().numpy().astype(np.float64) - ref)
+    assert np.all(err <= bound), float(np.max(err / bound))
+    srt = np.sort(ref, axis=1)[:, ::-1]
+    clear = (srt[:, k - 1] - srt[:, k]) > 2 * bound.max(axis=1)
+    assert clear.mean() > 0.5                  # most tokens are decided
+    got = np.sort(idx.cpu().numpy(), axis=1)
+    want = np.sort(O.route(x, wg, k)["idx"], axis=1)
+    assert np.array_equal(got[clear], want[clear]), "chosen experts differ on a clear token"
