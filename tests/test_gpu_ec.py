@@ -59,6 +59,9 @@ EC_CASES = {
     # few tokens and a long d: the logits come from the router's d-split
     # path (partial logits summed by the select kernel, no top-k)
     "split_router": ("mixtral_prefill", dict(T=40, d_model=2048, E=8, k=1), 1.0),
+    # 20000 tokens: more than 16 per thread of the select block, so the
+    # radix passes read the logit column again instead of registers
+    "long_column": ("mixtral_prefill", dict(T=20000, d_model=128, E=8, k=1), 1.0),
 }
 
 

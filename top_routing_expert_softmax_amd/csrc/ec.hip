@@ -80,6 +80,11 @@ __global__ __launch_bounds__(256) void lse_kernel(const float* __restrict__ logi
   if (lane == 0) lse[t] = m + logf(s);
 }
 
+// KPT > 0: thread tid owns tokens [tid * chunk, +chunk) with chunk <= KPT
+// and loads their keys into registers once, all loads in flight together
+// (indices clamped into the column); the radix passes and the compaction
+// read the registers.  KPT = 0: every pass reads the column again.
+template <int KPT>
 __global__ __launch_bounds__(kEcThreads) void ec_select_kernel(
     const float* __restrict__ logits, const float* __restrict__ lse,
     int32_t* __restrict__ ec_token, float* __restrict__ ec_w, int T, int E, int cap, int npow2) {
@@ -90,6 +95,14 @@ __global__ __launch_bounds__(kEcThreads) void ec_select_kernel(
   const int e = blockIdx.x;
   const int tid = threadIdx.x;
   auto key_of = [&](int t) { return f32_order_key(logits[static_cast<int64_t>(t) * E + e]); };
+  const int chunk = (T + kEcThreads - 1) / kEcThreads;
+  const int t0 = min(T, tid * chunk), t1 = min(T, t0 + chunk);
+  constexpr int KR = KPT > 0 ? KPT : 1;
+  uint32_t kr[KR];
+  if constexpr (KPT > 0) {
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) kr[j] = key_of(min(t0 + j, T - 1));
+  }
 
   // 1. radix select of the cap-th largest key
   uint32_t prefix = 0;
@@ -98,11 +111,20 @@ __global__ __launch_bounds__(kEcThreads) void ec_select_kernel(
     const int shift = 24 - 8 * pass;
     for (int i = tid; i < 256; i += kEcThreads) hist[i] = 0;
     __syncthreads();
-    for (int t = tid; t < T; t += kEcThreads) {
-      const uint32_t k = key_of(t);
-      // digits above this one must equal the prefix found so far
-      const bool match = pass == 0 || ((k ^ prefix) >> (shift + 8)) == 0u;
-      if (match) atomicAdd(&hist[(k >> shift) & 255u], 1);
+    if constexpr (KPT > 0) {
+#pragma unroll
+      for (int j = 0; j < KPT; ++j) {
+        const uint32_t k = kr[j];
+        // digits above this one must equal the prefix found so far
+        const bool match = pass == 0 || ((k ^ prefix) >> (shift + 8)) == 0u;
+        if (t0 + j < t1 && match) atomicAdd(&hist[(k >> shift) & 255u], 1);
+      }
+    } else {
+      for (int t = tid; t < T; t += kEcThreads) {
+        const uint32_t k = key_of(t);
+        const bool match = pass == 0 || ((k ^ prefix) >> (shift + 8)) == 0u;
+        if (match) atomicAdd(&hist[(k >> shift) & 255u], 1);
+      }
     }
     __syncthreads();
     if (tid < kWave) {
@@ -142,13 +164,21 @@ __global__ __launch_bounds__(kEcThreads) void ec_select_kernel(
   const int take_eq = need;                      // of the keys equal to K*
 
   // 2. compaction in token order
-  const int chunk = (T + kEcThreads - 1) / kEcThreads;
-  const int t0 = min(T, tid * chunk), t1 = min(T, t0 + chunk);
   int gt = 0, eq = 0;
-  for (int t = t0; t < t1; ++t) {
-    const uint32_t k = key_of(t);
-    gt += k > kstar;
-    eq += k == kstar;
+  if constexpr (KPT > 0) {
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+      if (t0 + j < t1) {
+        gt += kr[j] > kstar;
+        eq += kr[j] == kstar;
+      }
+    }
+  } else {
+    for (int t = t0; t < t1; ++t) {
+      const uint32_t k = key_of(t);
+      gt += k > kstar;
+      eq += k == kstar;
+    }
   }
   int tot;
   const int eq_before = block_exclusive_scan(eq, scan_tmp, &tot);
@@ -157,14 +187,20 @@ __global__ __launch_bounds__(kEcThreads) void ec_select_kernel(
   for (int i = tid; i < npow2; i += kEcThreads) picks[i] = 0ull;   // sorts last
   __syncthreads();
   int pos = pos0, eq_seen = 0;
-  for (int t = t0; t < t1; ++t) {
-    const uint32_t k = key_of(t);
+  auto place = [&](int t, uint32_t k) {
     bool take = k > kstar;
     if (k == kstar) { take = eq_seen < my_eq; ++eq_seen; }
     if (take) {
       picks[pos++] = (static_cast<uint64_t>(k) << 32) |
                      static_cast<uint64_t>(0xFFFFFFFFu - static_cast<uint32_t>(t));
     }
+  };
+  if constexpr (KPT > 0) {
+#pragma unroll
+    for (int j = 0; j < KPT; ++j)
+      if (t0 + j < t1) place(t0 + j, kr[j]);
+  } else {
+    for (int t = t0; t < t1; ++t) place(t, key_of(t));
   }
   __syncthreads();
 
@@ -267,9 +303,19 @@ hipError_t launch_route_ec(int64_t T, int64_t d, int E, int64_t cap, bool bf16, 
                      logits, lse, static_cast<int>(T), E);
   int npow2 = 1;
   while (npow2 < cap) npow2 <<= 1;
-  hipLaunchKernelGGL(ec_select_kernel, dim3(static_cast<unsigned>(E)), dim3(kEcThreads), 0, s,
-                     logits, lse, ec_token, ec_w, static_cast<int>(T), E, static_cast<int>(cap),
-                     npow2);
+  // keys per thread held in registers: 4 or 16 tokens, else none
+  const int64_t chunk = (T + kEcThreads - 1) / kEcThreads;
+  const dim3 grid(static_cast<unsigned>(E)), block(kEcThreads);
+  const int Ti = static_cast<int>(T), capi = static_cast<int>(cap);
+  if (chunk <= 4)
+    hipLaunchKernelGGL(ec_select_kernel<4>, grid, block, 0, s, logits, lse, ec_token, ec_w, Ti, E,
+                       capi, npow2);
+  else if (chunk <= 16)
+    hipLaunchKernelGGL(ec_select_kernel<16>, grid, block, 0, s, logits, lse, ec_token, ec_w, Ti,
+                       E, capi, npow2);
+  else
+    hipLaunchKernelGGL(ec_select_kernel<0>, grid, block, 0, s, logits, lse, ec_token, ec_w, Ti, E,
+                       capi, npow2);
   return hipGetLastError();
 }
 
