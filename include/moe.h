@@ -21,8 +21,16 @@
  * Conventions for every entry point
  *   - All tensor arguments are DEVICE pointers, row-major and contiguous,
  *     16-byte aligned.  The caller owns every buffer; the library never
- *     allocates, frees or keeps a pointer after the call returns, and it has
- *     no mutable global state: calls are re-entrant.
+ *     allocates, frees or keeps a pointer after the call returns.
+ *   - State the library keeps: the last error message, per calling thread
+ *     (thread-local); a per-device record of the large-LDS launch attribute
+ *     it has set on its GEMM kernels (set once, under an atomic); and the
+ *     per-device address of the scratch array of moe_expert_ffn_noalloc.
+ *     Device state lives only in the caller's workspace (and in that
+ *     scratch array): moe_expert_ffn keeps split-K arrival counters and
+ *     partial tiles there, so two calls that run at the same time (two
+ *     streams, or two threads) need a workspace each.  Calls made one after
+ *     another on one stream may share a workspace.
  *   - dtype selects activations AND weights: MOE_F32 (fp32) or MOE_BF16
  *     (bf16 storage).  Accumulation is always fp32.  Router logits,
  *     weights and statistics are fp32 (scalars fp64) for both dtypes.
@@ -85,7 +93,8 @@ int moe_capacity(int64_t T, int32_t E, int32_t k, double CF, int64_t* cap);
 /*
  * Bytes of device workspace that moe_route, moe_permute, moe_expert_ffn
  * and moe_aux_stats need for this shape (one buffer serves all four; calls
- * on one stream may share it).  Host only.
+ * that run one after another on one stream may share it, calls that run
+ * concurrently need one each).  Host only.
  */
 int moe_workspace_size(int64_t T, int64_t d_model, int32_t E, int32_t E_shared,
                        int32_t k, int64_t d_ff, int32_t dtype, size_t* bytes);
@@ -233,6 +242,32 @@ int moe_expert_ffn(int64_t T, int64_t d_model, int32_t E, int32_t E_shared,
                    const void* w3, const void* w2, const void* ws1,
                    const void* ws3, const void* ws2, void* y_perm,
                    void* y_shared, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * moe_expert_ffn without a workspace argument and without allocating, for
+ * callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  The
+ * intermediate H and the tile table live in a fixed 32 MiB device array
+ * that the library holds on every GPU it runs on (one copy per device,
+ * from the device's first call until the process ends).  The call
+ * allocates and frees nothing.
+ *   Arguments and outputs: as for moe_expert_ffn, without ws / ws_bytes.
+ *   Limit: the shape's scratch (tile table + H rows (T*k + E_shared*T) x F
+ *   in dtype, plus 64 MiB of split-K partials on the large-tile path that
+ *   prefill-sized segments take) must fit in 32 MiB, else MOE_EWORKSPACE
+ *   and nothing is launched.  Decode-shaped calls fit: the DeepSeek-V3
+ *   step (T = 64, k = 8, one shared expert, F = 2048) needs 2.4 MB.
+ *   Every call on one GPU shares that GPU's array, which keeps the last
+ *   call's contents: calls that overlap on one GPU (two streams, or two
+ *   threads) race; serialise them.  Results equal moe_expert_ffn's.
+ */
+int moe_expert_ffn_noalloc(int64_t T, int64_t d_model, int32_t E,
+                           int32_t E_shared, int32_t k, int64_t d_ff,
+                           int32_t dtype, const void* x_perm,
+                           const int32_t* offsets, const void* x,
+                           const void* w1, const void* w3, const void* w2,
+                           const void* ws1, const void* ws3, const void* ws2,
+                           void* y_perm, void* y_shared, void* stream);
 
 /*
  * The forward of a training step ("CMU 11-868 Lecture 17" 5.2, the SwiGLU

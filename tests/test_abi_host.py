@@ -208,3 +208,24 @@ def test_training_forward_and_backward_arguments_are_checked(M):
                                          ctypes.byref(n)) == 0
     rows, F = 4096 * 2, 14336
     assert n.value >= rows * 2 * F * 2 + rows * F * 2       # (A, B) -> (dA, dB) and dH -> H
+
+
+def test_noalloc_ffn_rejects_shapes_beyond_its_scratch(M):
+    """moe_expert_ffn_noalloc checks its arguments and the 32 MiB scratch
+    limit on the host, before touching the device: a prefill-sized call
+    (large tiles with their 64 MiB of split-K partials) and a decode call
+    whose intermediate exceeds the scratch are refused with MOE_EWORKSPACE."""
+    L = M.lib()
+    nil = ctypes.c_void_p(0)
+    fake = ctypes.c_void_p(4096)
+
+    def call(T, d, E, Es, k, F, dtype=M.MOE_BF16, y=fake):
+        return L.moe_expert_ffn_noalloc(T, d, E, Es, k, F, dtype, fake, fake, fake, fake, fake,
+                                        fake, fake if Es else nil, fake if Es else nil,
+                                        fake if Es else nil, y, fake if Es else nil, nil)
+    rc = call(4096, 4096, 8, 0, 2, 14336)
+    assert rc == -4 and "scratch" in L.moe_last_error().decode()
+    # decode-shaped (streamed) but H = 64 * 8 rows * 65536 * 2 bytes = 64 MiB
+    assert call(64, 7168, 256, 0, 8, 65536) == -4
+    assert call(64, 7168, 256, 1, 8, 2048, y=nil) == -1     # y_perm NULL
+    assert call(64, 7168, 256, 1, 8, 2048, dtype=5) == -2

@@ -22,7 +22,8 @@ MOE_BF16 = 1
 EXPORTS = ("moe_strerror", "moe_last_error", "moe_capacity", "moe_workspace_size",
            "moe_route", "moe_route_v3", "moe_update_bias", "moe_ec_capacity", "moe_route_ec",
            "moe_permute_ec", "moe_quantize_fp8", "moe_expert_ffn_fp8", "moe_permute",
-           "moe_expert_ffn", "moe_expert_ffn_train", "moe_combine", "moe_aux_stats",
+           "moe_expert_ffn", "moe_expert_ffn_noalloc", "moe_expert_ffn_train", "moe_combine",
+           "moe_aux_stats",
            "moe_backward_workspace_size",
            "moe_combine_backward", "moe_expert_ffn_backward", "moe_route_backward")
 
@@ -91,6 +92,8 @@ def lib():
     L.moe_expert_ffn.restype = ctypes.c_int
     L.moe_expert_ffn.argtypes = [i64, i64, i32, i32, i32, i64, i32, vp, vp, vp, vp, vp, vp,
                                  vp, vp, vp, vp, vp, vp, sz, vp]
+    L.moe_expert_ffn_noalloc.restype = ctypes.c_int
+    L.moe_expert_ffn_noalloc.argtypes = [i64, i64, i32, i32, i32, i64, i32] + [vp] * 12
     L.moe_expert_ffn_train.restype = ctypes.c_int
     L.moe_expert_ffn_train.argtypes = [i64, i64, i32, i32, i32, i64, i32] + [vp] * 13 + \
         [sz, vp]
@@ -238,6 +241,18 @@ def moe_expert_ffn(T, k, x_perm, offsets, x, w1, w3, w2, ws1, ws3, ws2, y_perm, 
         T, d, E, Es, k, F, _dtype_code(x_perm), _ptr(x_perm), _ptr(offsets), _ptr(x),
         _ptr(w1), _ptr(w3), _ptr(w2), _ptr(ws1), _ptr(ws3), _ptr(ws2), _ptr(y_perm),
         _ptr(y_shared), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def moe_expert_ffn_noalloc(T, k, x_perm, offsets, x, w1, w3, w2, ws1, ws3, ws2, y_perm,
+                           y_shared, stream=None):
+    """moe_expert_ffn on the library's fixed device scratch (no workspace,
+    no allocation); shapes whose scratch exceeds it raise MoEError."""
+    E, F, d = w1.shape
+    Es = 0 if ws1 is None else ws1.shape[0]
+    _check("moe_expert_ffn_noalloc", lib().moe_expert_ffn_noalloc(
+        T, d, E, Es, k, F, _dtype_code(x_perm), _ptr(x_perm), _ptr(offsets), _ptr(x),
+        _ptr(w1), _ptr(w3), _ptr(w2), _ptr(ws1), _ptr(ws3), _ptr(ws2), _ptr(y_perm),
+        _ptr(y_shared), _stream(stream)))
 
 
 def moe_expert_ffn_train(T, k, x_perm, offsets, x, w1, w3, w2, ws1, ws3, ws2, y_perm, y_shared,

@@ -1052,6 +1052,30 @@ size_t ffn_workspace_bytes(int64_t T, int E, int E_shared, int k, int64_t d_ff,
 
 namespace {
 
+// Rows per tile of the path launch_expert_ffn takes for this shape: the
+// fp32 tiles, the large bf16 tiles (prefill-sized segments) or the 128-row
+// bf16 tiles beside the weight-streaming kernels (decode-sized calls).
+int ffn_tile_rows(int64_t T, int E, int k, bool bf16) {
+  return !bf16 ? kBMf : (T * k >= 64LL * E ? kBM2 : kBM);
+}
+
+}  // namespace
+
+// The part of the workspace launch_expert_ffn touches: the tile count and
+// table, the split-K partials and arrival counters (large-tile path only),
+// then H.  At most ffn_workspace_bytes.
+size_t ffn_workspace_used_bytes(int64_t T, int E, int E_shared, int k, int64_t d_ff,
+                                int elem_bytes) {
+  const bool bf16 = elem_bytes == 2;
+  const int64_t tiles = max_tiles(T, E, E_shared, k, kBMf);
+  const int64_t hrows = T * k + static_cast<int64_t>(E_shared) * T;
+  const bool big = bf16 && ffn_tile_rows(T, E, k, bf16) == kBM2;
+  return 256 + align256(static_cast<size_t>(tiles) * sizeof(int4)) +
+         (big ? ffn_sk_bytes(2) : 0) + static_cast<size_t>(hrows) * d_ff * elem_bytes;
+}
+
+namespace {
+
 // Compute units of the current device (one large-tile block fits a CU).
 hipError_t device_cus(int* ncu) {
   int dev = 0;
@@ -1109,20 +1133,22 @@ hipError_t launch_expert_ffn(int64_t T, int64_t d, int E, int E_shared, int k, i
                              const void* x, const void* w1, const void* w3, const void* w2,
                              const void* ws1, const void* ws3, const void* ws2, void* y_perm,
                              void* y_shared, void* ws, hipStream_t s) {
+  // Large segments take the large tiles; decode-sized ones (few rows
+  // per expert) the 128-row tiles.  Only the large-tile path has split-K
+  // partials; H follows the tile table directly on the others
+  // (ffn_workspace_used_bytes).
+  const int BM = ffn_tile_rows(T, E, k, bf16);
+  const bool big = bf16 && BM == kBM2;
   char* base = static_cast<char*>(ws);
   int* ntiles = reinterpret_cast<int*>(base);
   int4* tiles = reinterpret_cast<int4*>(base + 256);
   const int64_t tiles_cap = max_tiles(T, E, E_shared, k, kBMf);
   char* sk = base + 256 + align256(static_cast<size_t>(tiles_cap) * sizeof(int4));
-  float* sk_partial = bf16 ? reinterpret_cast<float*>(sk) : nullptr;
+  float* sk_partial = big ? reinterpret_cast<float*>(sk) : nullptr;
   unsigned* sk_count =
-      bf16 ? reinterpret_cast<unsigned*>(sk + static_cast<size_t>(kMaxCUs) * kBM2 * kBN2 * 4)
-           : nullptr;
-  void* H = sk + ffn_sk_bytes(bf16 ? 2 : 4);
-
-  // Large segments take the large tiles; decode-sized ones (few rows
-  // per expert) the 128-row tiles.
-  const int BM = !bf16 ? kBMf : (T * k >= 64LL * E ? kBM2 : kBM);
+      big ? reinterpret_cast<unsigned*>(sk + static_cast<size_t>(kMaxCUs) * kBM2 * kBN2 * 4)
+          : nullptr;
+  void* H = sk + (big ? ffn_sk_bytes(2) : 0);
   // decode-sized calls with T <= kStreamMaxRows only stream (no tiles)
   const bool stream_only = bf16 && BM == kBM && T <= kStreamMaxRows;
   if (!stream_only)
@@ -1132,7 +1158,7 @@ hipError_t launch_expert_ffn(int64_t T, int64_t d, int E, int E_shared, int k, i
             sk_partial, sk_count,
             static_cast<int>(T), static_cast<int>(d), E, E_shared, k, static_cast<int>(F)};
   const unsigned gx = static_cast<unsigned>(max_tiles(T, E, E_shared, k, BM));
-  if (bf16 && BM == kBM2) {
+  if (big) {
     hipError_t err = run_big_ffn<1>(a, s);
     if (err != hipSuccess) return err;
   } else if (bf16) {

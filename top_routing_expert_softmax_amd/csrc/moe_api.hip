@@ -6,6 +6,8 @@
 #include <string.h>
 
 #include <algorithm>
+#include <atomic>
+#include <mutex>
 
 #include "moe.h"
 #include "moe_internal.h"
@@ -118,6 +120,46 @@ size_t workspace_bytes(int64_t T, int64_t d, int32_t E, int32_t Es, int32_t k, i
   b = std::max(b, moe::ec_workspace_bytes(T, d, E));
   b = std::max(b, moe::ffn_workspace_bytes(T, E, Es, k, F, elem));
   return align256(b);
+}
+
+}  // namespace
+
+// Scratch of moe_expert_ffn_noalloc: a device array that every GPU the
+// library runs on holds (its own copy each) until the process ends.  Host
+// code never passes the array's name to a kernel or a copy (on the host it
+// is only a stand-in for the symbol): it looks up each device's address
+// once, with that device current, and uses that pointer.
+constexpr size_t kNoallocScratchBytes = size_t(32) << 20;
+static __device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
+
+namespace {
+
+constexpr int kMaxScratchDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxScratchDevices];
+std::mutex g_scratch_mu;
+
+// The current device's scratch address (looked up on its first use).
+int current_scratch(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(MOE_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxScratchDevices)
+    return fail(MOE_EUNSUPPORTED, "moe_expert_ffn_noalloc supports device ids below %d (got %d)",
+                kMaxScratchDevices, dev);
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess || p == nullptr)
+        return fail(MOE_EHIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev,
+                    hipGetErrorString(e));
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return MOE_OK;
 }
 
 }  // namespace
@@ -541,6 +583,47 @@ int moe_expert_ffn(int64_t T, int64_t d_model, int32_t E, int32_t E_shared, int3
                                          x_perm, offsets, x, w1, w3, w2, ws1, ws3, ws2, y_perm,
                                          y_shared, ws, static_cast<hipStream_t>(stream)),
                   "moe_expert_ffn");
+}
+
+int moe_expert_ffn_noalloc(int64_t T, int64_t d_model, int32_t E, int32_t E_shared, int32_t k,
+                           int64_t d_ff, int32_t dtype, const void* x_perm,
+                           const int32_t* offsets, const void* x, const void* w1, const void* w3,
+                           const void* w2, const void* ws1, const void* ws3, const void* ws2,
+                           void* y_perm, void* y_shared, void* stream) {
+  if (int r = check_common(T, E, k)) return r;
+  if (int r = check_dtype(dtype)) return r;
+  if (int r = check_dim("d_model", d_model)) return r;
+  if (int r = check_dim("d_ff", d_ff)) return r;
+  REQUIRE(E_shared >= 0 && E_shared <= 16, "E_shared must be in [0, 16]");
+  REQUIRE(T * k + static_cast<int64_t>(E_shared) * T < (int64_t(1) << 31),
+          "T*k + E_shared*T must be < 2^31");
+  REQUIRE_PTR(x_perm);
+  REQUIRE_PTR(offsets);
+  REQUIRE_PTR(w1);
+  REQUIRE_PTR(w3);
+  REQUIRE_PTR(w2);
+  REQUIRE_PTR(y_perm);
+  if (E_shared > 0) {
+    REQUIRE_PTR(x);
+    REQUIRE_PTR(ws1);
+    REQUIRE_PTR(ws3);
+    REQUIRE_PTR(ws2);
+    REQUIRE_PTR(y_shared);
+  }
+  const size_t need =
+      moe::ffn_workspace_used_bytes(T, E, E_shared, k, d_ff, dtype == MOE_BF16 ? 2 : 4);
+  if (need > kNoallocScratchBytes)
+    return fail(MOE_EWORKSPACE,
+                "moe_expert_ffn_noalloc needs %zu bytes of scratch for this shape; the library "
+                "holds %zu (use moe_expert_ffn with a workspace)",
+                need, kNoallocScratchBytes);
+  void* ws = nullptr;
+  if (int r = current_scratch(&ws)) return r;
+  (void)hipGetLastError();
+  return launched(moe::launch_expert_ffn(T, d_model, E, E_shared, k, d_ff, dtype == MOE_BF16,
+                                         x_perm, offsets, x, w1, w3, w2, ws1, ws3, ws2, y_perm,
+                                         y_shared, ws, static_cast<hipStream_t>(stream)),
+                  "moe_expert_ffn_noalloc");
 }
 
 int moe_expert_ffn_train(int64_t T, int64_t d_model, int32_t E, int32_t E_shared, int32_t k,

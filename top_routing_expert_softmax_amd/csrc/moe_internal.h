@@ -30,6 +30,8 @@ size_t permute_workspace_bytes(int64_t T, int E);
 size_t stats_workspace_bytes(int64_t T, int E);
 size_t ffn_workspace_bytes(int64_t T, int E, int E_shared, int k, int64_t d_ff,
                            int elem_bytes);
+size_t ffn_workspace_used_bytes(int64_t T, int E, int E_shared, int k, int64_t d_ff,
+                                int elem_bytes);
 
 struct GateParams;   // router.hip: which top-k follows the logits
 
