@@ -43,7 +43,8 @@
  *     fault surfaces at the caller's next synchronisation as a HIP error.
  *   - Limits: 1 <= k <= min(E, 64); E <= 256; 0 <= E_shared <= 16; 1 <= T;
  *     T*k + E_shared*T < 2^31; d_model and d_ff positive multiples of 64
- *     below 2^24.
+ *     below 2^22 (a 256-row operand tile then spans less than 2^31 bytes,
+ *     the reach of the GEMM's 32-bit buffer offsets).
  *   - topk_idx rows must name distinct experts (moe_route writes them so);
  *     ids outside [0, E) are treated as dropped pairs.
  *

@@ -354,6 +354,23 @@ __device__ __forceinline__ void lds_dma16(const void* gptr, uint32_t* lds_row_ba
   __builtin_amdgcn_global_load_lds(gptr, lds_row_base, 16, 0, 0);
 }
 
+// The same 16-byte direct-to-LDS load through a buffer resource: a
+// wave-uniform base in scalar registers plus a 32-bit byte offset per lane
+// (buffer_load_dwordx4 ... lds).  On the grouped GEMM this measured 4-7%
+// faster than the 64-bit-address form.  Offsets stay below 2^31: an
+// operand tile spans at most 256 rows of K < 2^22 bf16 values.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
+                                           0x7FFFFFFF, 0x00020000);
+}
+
+__device__ __forceinline__ void lds_dma16_buf(__amdgpu_buffer_rsrc_t rsrc, uint32_t byte_off,
+                                              void* lds_row_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      rsrc, (__attribute__((address_space(3))) void*)(lds_row_base), 16,
+      byte_off, 0, 0, 0);
+}
+
 // K loop of one wave: stream slices of A and B into the LDS ring with DMA
 // loads and run the wave's MFMAs on them.  MIA (0..MI) is the number of
 // the wave's MI 32-row blocks that hold segment rows; the others take no
@@ -379,22 +396,36 @@ __device__ __forceinline__ bf16x8_t lds_read_tr_pair(const char* p, int second) 
 // BMN: the B operand is MN-contiguous (rows of k in global memory and in
 // LDS); slice k0 of B then starts k0 rows further on, and b_jump more
 // elements from b_kjump on (a second matrix continues the K range).
-template <int BKT, int BMT, int NST, int NIA, int NIB, int MI, int NB, int MIA, bool BMN>
+// BUF: the K-contiguous operands are read through buffer resources (ra,
+// rb) at per-lane byte offsets (aoff, boff) instead of the pointers asrc,
+// bsrc; slice k0 adds 2 k0 bytes.
+struct BufOperands {
+  __amdgpu_buffer_rsrc_t ra, rb;
+};
+
+template <int BKT, int BMT, int NST, int NIA, int NIB, int MI, int NB, int MIA, bool BMN,
+          bool BUF = false>
 __device__ __forceinline__ void gemm_mainloop(
     f32x16_t (&acc)[MI][NB], const uint16_t* const (&asrc)[NIA],
     const uint16_t* const (&bsrc)[NIB], char* lds_bytes, int a_dst, int b_dst,
     const int (&a_off)[MI], const int (&b_off)[NB], int lane, int nk, int64_t b_kstride,
-    int b_kjump, int64_t b_jump) {
+    int b_kjump, int64_t b_jump, const BufOperands& bo = BufOperands{},
+    const uint32_t* aoff = nullptr, const uint32_t* boff = nullptr) {
   using G = SliceGeom<BKT, BMT>;
+  static_assert(!(BUF && BMN), "buffer loads serve the K-contiguous operands");
 #define MOE_BK(k0) (BMN ? static_cast<int64_t>(k0) * b_kstride + ((k0) >= b_kjump ? b_jump : 0) \
                         : static_cast<int64_t>(k0))
 #define MOE_ISSUE_SLICE(slot, k0)                                                          \
-  _Pragma("unroll") for (int i = 0; i < NIA; ++i)                                          \
-    lds_dma16(asrc[i] + (k0), reinterpret_cast<uint32_t*>(                                \
-                  lds_bytes + (slot) * G::STAGE + a_dst + i * G::RPI * G::ROW));          \
-  _Pragma("unroll") for (int i = 0; i < NIB; ++i)                                          \
-    lds_dma16(bsrc[i] + MOE_BK(k0), reinterpret_cast<uint32_t*>(                          \
-                  lds_bytes + (slot) * G::STAGE + b_dst + i * 1024));
+  _Pragma("unroll") for (int i = 0; i < NIA; ++i) {                                        \
+    char* d_ = lds_bytes + (slot) * G::STAGE + a_dst + i * G::RPI * G::ROW;               \
+    if constexpr (BUF) lds_dma16_buf(bo.ra, aoff[i] + 2u * static_cast<uint32_t>(k0), d_); \
+    else lds_dma16(asrc[i] + (k0), reinterpret_cast<uint32_t*>(d_));                      \
+  }                                                                                        \
+  _Pragma("unroll") for (int i = 0; i < NIB; ++i) {                                        \
+    char* d_ = lds_bytes + (slot) * G::STAGE + b_dst + i * 1024;                           \
+    if constexpr (BUF) lds_dma16_buf(bo.rb, boff[i] + 2u * static_cast<uint32_t>(k0), d_); \
+    else lds_dma16(bsrc[i] + MOE_BK(k0), reinterpret_cast<uint32_t*>(d_));                 \
+  }
   // fragment rows are 32-aligned bases + lane%32, so the swizzle key of
   // all of this lane's fragment rows is ((lane % 32) / RPL) % CH
   const int key = ((lane & 31) / G::RPL) % G::CH;
@@ -616,6 +647,24 @@ void gemm_big_kernel(FfnArgs a, int NT, int ncu) {
       bsrc[i] = W + e * wstride + static_cast<int64_t>(col) * K + kb * BKT + lchunk * 8;
     }
   }
+  // The buffer-resource form of the K-contiguous operands: the A tile from
+  // its first row, the B tile from column n0 of the wave's matrix (a wave's
+  // B rows all lie in W1 or all in W3: 128 is a multiple of BROWS).
+  BufOperands bo{};
+  uint32_t aoff[NIA], boff[NIB];
+  if constexpr (!BMN) {
+    bo.ra = buffer_rsrc(A);
+    const bool w3rows = P1 && wave * BROWS >= 128;
+    const uint16_t* Wb = static_cast<const uint16_t*>(
+        P1 ? (w3rows ? (routed ? a.w3 : a.ws3) : (routed ? a.w1 : a.ws1))
+           : (routed ? a.w2 : a.ws2));
+    const uint16_t* Bbase = Wb + e * wstride + static_cast<int64_t>(n0) * K;
+    bo.rb = buffer_rsrc(Bbase);
+#pragma unroll
+    for (int i = 0; i < NIA; ++i) aoff[i] = static_cast<uint32_t>((asrc[i] - A) * 2);
+#pragma unroll
+    for (int i = 0; i < NIB; ++i) boff[i] = static_cast<uint32_t>((bsrc[i] - Bbase) * 2);
+  }
   char* lds_bytes = reinterpret_cast<char*>(lds);
   const int a_dst = wave * AROWS * G::ROW;
   const int b_dst = BMT * G::ROW + wave * BROWS * G::ROW;
@@ -656,9 +705,9 @@ void gemm_big_kernel(FfnArgs a, int NT, int ncu) {
   const int mia = __builtin_amdgcn_readfirstlane(
       rows_w <= 0 ? 0 : (rows_w >= WR ? MI : (rows_w + 31) / 32));
 #define MOE_MAINLOOP(X)                                                                    \
-  gemm_mainloop<BKT, BMT, NST, NIA, NIB, MI, NB, (X), BMN>(                                 \
+  gemm_mainloop<BKT, BMT, NST, NIA, NIB, MI, NB, (X), BMN, !BMN>(                           \
       acc, asrc, bsrc, lds_bytes, a_dst, b_dst, a_off, b_off, lane, nk, b_kstride, b_kjump,  \
-      b_jump)
+      b_jump, bo, aoff, boff)
   switch (mia) {
     case 4: if constexpr (MI >= 4) MOE_MAINLOOP(MI >= 4 ? 4 : 0); break;
     case 3: if constexpr (MI >= 3) MOE_MAINLOOP(MI >= 3 ? 3 : 0); break;

@@ -57,8 +57,8 @@ int check_dtype(int32_t dtype) {
 }
 
 int check_dim(const char* name, int64_t v) {
-  REQUIRE(v >= 64 && v % 64 == 0 && v < (int64_t(1) << 24),
-          "%s must be a positive multiple of 64 below 2^24 (got %lld)", name,
+  REQUIRE(v >= 64 && v % 64 == 0 && v < (int64_t(1) << 22),
+          "%s must be a positive multiple of 64 below 2^22 (got %lld)", name,
           static_cast<long long>(v));
   return MOE_OK;
 }
