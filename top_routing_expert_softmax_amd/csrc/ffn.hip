@@ -319,8 +319,11 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(FfnArgs a) {
 // banks (a 256-byte line holding RPL = 256/ROW rows) and serves a 16-byte
 // read 16 lanes at a time; chunk c of row r sits at physical chunk
 // c ^ ((r / RPL) % CH), so the fragment reads of 16 consecutive rows touch
-// every bank once.  Rows past the segment (A) or past N (B) load a clamped
-// valid row: they only feed outputs that the epilogue does not store.
+// every bank once.  Rows past the segment (A) read as zeros through the
+// bounded buffer resource (no memory access; the 64-bit-address loads of
+// the MN-contiguous form read a clamped valid row instead), and rows past N
+// (B) load a clamped valid row: either way they only feed outputs that the
+// epilogue does not store.
 //
 // Block order: a 1-D grid; each XCD (blocks are dealt to the 8 XCDs round
 // robin) takes a contiguous chunk of the live tiles, and inside a chunk
@@ -359,9 +362,12 @@ __device__ __forceinline__ void lds_dma16(const void* gptr, uint32_t* lds_row_ba
 // (buffer_load_dwordx4 ... lds).  On the grouped GEMM this measured 4-7%
 // faster than the 64-bit-address form.  Offsets stay below 2^31: an
 // operand tile spans at most 256 rows of K < 2^22 bf16 values.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base) {
+// bytes: the resource's extent; loads past it return zeros without a
+// memory access (raw buffer range check).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base,
+                                                            int bytes = 0x7FFFFFFF) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
-                                           0x7FFFFFFF, 0x00020000);
+                                           bytes, 0x00020000);
 }
 
 __device__ __forceinline__ void lds_dma16_buf(__amdgpu_buffer_rsrc_t rsrc, uint32_t byte_off,
@@ -653,7 +659,10 @@ void gemm_big_kernel(FfnArgs a, int NT, int ncu) {
   BufOperands bo{};
   uint32_t aoff[NIA], boff[NIB];
   if constexpr (!BMN) {
-    bo.ra = buffer_rsrc(A);
+    // A rows past the segment fall outside the resource and read as zeros
+    // without touching memory, so a tail tile streams only its own rows
+    // (their products are never stored)
+    bo.ra = buffer_rsrc(A, mrows * K * 2);
     const bool w3rows = P1 && wave * BROWS >= 128;
     const uint16_t* Wb = static_cast<const uint16_t*>(
         P1 ? (w3rows ? (routed ? a.w3 : a.ws3) : (routed ? a.w1 : a.ws1))
@@ -661,7 +670,11 @@ void gemm_big_kernel(FfnArgs a, int NT, int ncu) {
     const uint16_t* Bbase = Wb + e * wstride + static_cast<int64_t>(n0) * K;
     bo.rb = buffer_rsrc(Bbase);
 #pragma unroll
-    for (int i = 0; i < NIA; ++i) aoff[i] = static_cast<uint32_t>((asrc[i] - A) * 2);
+    for (int i = 0; i < NIA; ++i) {
+      const int r = wave * AROWS + i * G::RPI + lane / G::CH;
+      const int lchunk = (lane % G::CH) ^ ((r / G::RPL) % G::CH);
+      aoff[i] = static_cast<uint32_t>((static_cast<int64_t>(r) * K + kb * BKT + lchunk * 8) * 2);
+    }
 #pragma unroll
     for (int i = 0; i < NIB; ++i) boff[i] = static_cast<uint32_t>((bsrc[i] - Bbase) * 2);
   }
