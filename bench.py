@@ -39,8 +39,9 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 # and names that summary ("traffic_from"); a changed kernel reports null
 # until it is profiled again.
 MEASURED_TRAFFIC = {
-    ("mixtral_prefill", "01914064b5b39fa4"): (9.4449e9, "profiles/moe_layer_mixtral_prefill.md"),
-    ("dsv3_decode", "01914064b5b39fa4"): (1.9662e10, "profiles/moe_layer_dsv3_decode.md"),
+    ("skewed_train", "7be7a51ef5d3d080"): (3.6371e10, "profiles/moe_layer_skewed_train.md"),
+    ("dsmoe16b_prefill", "7be7a51ef5d3d080"): (3.2549e9, "profiles/moe_layer_dsmoe16b_prefill.md"),
+    ("mixtral_prefill", "7be7a51ef5d3d080"): (9.7518e9, "profiles/moe_layer_mixtral_prefill.md"),
 }
 
 
@@ -133,6 +134,72 @@ def copy_calibration(nbytes):
     print(json.dumps({"copy_calibration_bytes": nbytes}), flush=True)
 
 
+def dense_gemm(cfg, steps, warmup):
+    """The expert FFN on one dense segment holding the workload's T*k rows
+    (E = 1, no routing, no ragged tails), timed as moe_expert_ffn against
+    torch's bf16 GEMMs (hipBLASLt) on the same two products: the phase-1
+    product X [rows, d] x [W1; W3]^T and the phase-2 product H x W2^T.
+    Context for the grouped GEMM's roofline fraction: the same kernel
+    without ragged segments, and the vendor library on the same shapes."""
+    import torch.nn.functional as Fn
+    d, F = cfg.d_model, cfg.d_ff
+    rows = cfg.T * cfg.k
+    g = torch.Generator(device="cuda")
+    g.manual_seed(cfg.seed)
+    bf = torch.bfloat16
+    x = torch.randn((rows, d), generator=g, device="cuda").to(bf)
+    w1 = (0.02 * torch.randn((1, F, d), generator=g, device="cuda")).to(bf)
+    w3 = (0.02 * torch.randn((1, F, d), generator=g, device="cuda")).to(bf)
+    w2 = (0.02 * torch.randn((1, d, F), generator=g, device="cuda")).to(bf)
+    offsets = torch.tensor([0, rows], dtype=torch.int32, device="cuda")
+    y = torch.empty((rows, d), dtype=bf, device="cuda")
+    ws = torch.empty(M.moe_workspace_size(rows, d, 1, 0, 1, F, bf), dtype=torch.uint8,
+                     device="cuda")
+    stream = torch.cuda.current_stream()
+    w13 = torch.cat([w1[0], w3[0]], dim=0).contiguous()
+    h = torch.empty((rows, F), dtype=bf, device="cuda")
+
+    def ours():
+        M.moe_expert_ffn(rows, 1, x, offsets, x, w1, w3, w2, None, None, None, y, None, ws,
+                         stream)
+
+    def lib_p1():
+        return Fn.linear(x, w13)
+
+    def lib_p2():
+        return Fn.linear(h, w2[0])
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    ab = lib_p1()
+    h.copy_(Fn.silu(ab[:, :F]) * ab[:, F:])
+    del ab
+    t_ours = timed(ours)
+    t1, t2 = timed(lib_p1), timed(lib_p2)
+    f1, f2 = 4.0 * rows * d * F, 2.0 * rows * d * F
+
+    def rate(flop, ms):
+        v = flop / (ms / 1e3) / 1e12
+        return {"ms": round(ms, 4), "tflops": round(v, 1), "frac": round(v / PEAK_BF16_TFLOPS, 4)}
+    out = {"mode": "dense_gemm", "workload_shape": cfg.name, "rows": rows, "d_model": d,
+           "d_ff": F, "dtype": "bf16",
+           "moe_expert_ffn": rate(f1 + f2, t_ours),
+           "torch_linear_hipblaslt": {"phase1": rate(f1, t1), "phase2": rate(f2, t2),
+                                      "both": rate(f1 + f2, t1 + t2)},
+           "peak_tflops": PEAK_BF16_TFLOPS}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -141,7 +208,7 @@ def main():
     # default: the largest single-GPU workload (T = 16384, d = 4096, E = 16,
     # k = 4, F = 10752, CF = 1.0, Zipf-skewed routing with drops)
     ap.add_argument("--workload", default="skewed_train", choices=sorted(CONFIGS))
-    ap.add_argument("--cpu-sample", type=int, default=4096,
+    ap.add_argument("--cpu-sample", type=int, default=12288,
                     help="tokens whose expert outputs the oracle computes")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--weights", default="bf16", choices=["bf16", "fp8"],
@@ -158,6 +225,9 @@ def main():
                          "(moe_route_v3: 8 groups, 4 kept, scale 2.5, seeded bias in "
                          "+-1e-3) or expert choice (moe_route_ec + moe_permute_ec, "
                          "capacity factor 1)")
+    ap.add_argument("--dense-gemm", action="store_true",
+                    help="context only: moe_expert_ffn on one dense segment of the workload's "
+                         "T*k rows against torch's bf16 GEMMs (hipBLASLt) on the same products")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes (reference for "
                          "the FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -174,6 +244,12 @@ def main():
         sys.exit(2)
     M.lib()
     cfg = CONFIGS[args.workload]
+    if args.dense_gemm:
+        if cfg.dtype != "bf16":
+            print("--dense-gemm compares bf16 GEMMs", file=sys.stderr)
+            sys.exit(2)
+        dense_gemm(cfg, args.steps, args.warmup)
+        return
     t = time.time()
     x, wg, dev, host = build_inputs(cfg)
     log(f"inputs for {cfg.name} on the device in {time.time() - t:.1f}s")
