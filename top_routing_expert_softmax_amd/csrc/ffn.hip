@@ -174,7 +174,9 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(FfnArgs a) {
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
-  const int wave = tid / kWave;
+  // wave-uniform by construction; readfirstlane lets the compiler keep it
+  // (and the buffer resources chosen by it) in scalar registers
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int wm = wave >> 1, wn = wave & 1;
 
   // Problem geometry of this phase.
@@ -364,10 +366,17 @@ __device__ __forceinline__ void lds_dma16(const void* gptr, uint32_t* lds_row_ba
 // operand tile spans at most 256 rows of K < 2^22 bf16 values.
 // bytes: the resource's extent; loads past it return zeros without a
 // memory access (raw buffer range check).
+// Callers pass wave-uniform values; reading them from the first lane keeps
+// the descriptor in scalar registers (a descriptor the compiler takes for
+// divergent costs a loop around every load that uses it).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base,
                                                             int bytes = 0x7FFFFFFF) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
-                                           bytes, 0x00020000);
+  const uint64_t v = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
+  void* ub = reinterpret_cast<void*>((static_cast<uint64_t>(hi) << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(ub, static_cast<short>(0),
+                                           __builtin_amdgcn_readfirstlane(bytes), 0x00020000);
 }
 
 __device__ __forceinline__ void lds_dma16_buf(__amdgpu_buffer_rsrc_t rsrc, uint32_t byte_off,
@@ -581,7 +590,9 @@ void gemm_big_kernel(FfnArgs a, int NT, int ncu) {
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
-  const int wave = tid / kWave;
+  // wave-uniform by construction; readfirstlane lets the compiler keep it
+  // (and the buffer resources chosen by it) in scalar registers
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int wm = wave / WN, wn = wave % WN;
 
   const int N = P1 ? a.F : a.d;
@@ -1022,7 +1033,9 @@ void gemm_wgrad_kernel(WgradArgs a) {
                        : a.C_shared + static_cast<int64_t>(seg - a.E) * a.M * a.N;
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
-  const int wave = tid / kWave;
+  // wave-uniform by construction; readfirstlane lets the compiler keep it
+  // (and the buffer resources chosen by it) in scalar registers
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int wm = wave / WN, wn = wave % WN;
 
   const uint16_t* asrc[NIA];
