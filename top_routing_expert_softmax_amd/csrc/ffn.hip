@@ -510,6 +510,38 @@ __device__ __forceinline__ void gemm_mainloop(
 #undef MOE_BK
 }
 
+// ---- epilogue through the LDS.  The block's bf16 output tile (BMT rows x
+// COLS columns) is first written into the idle LDS ring, its 16-byte chunks
+// XOR-swizzled by row (chunk c of row r at c ^ (r % NCH)), so that the two
+// half-waves of a write (rows r and r + 4, 32 columns each) fall in
+// different banks; then consecutive threads copy consecutive chunks of a
+// row to memory, so every store instruction writes whole 16-byte pieces of
+// full rows instead of 2 bytes per lane.
+template <int COLS>
+__device__ __forceinline__ void stage_put(char* lds, int row, int col, float v) {
+  constexpr int NCH = COLS / 8;
+  const int off = row * (COLS * 2) + (((col >> 3) ^ (row & (NCH - 1))) << 4) + ((col & 7) << 1);
+  *reinterpret_cast<uint16_t*>(lds + off) = f32_to_bf16(v);
+}
+
+// dst(row, chunk) gives the destination of 16-byte chunk `chunk` of tile row
+// `row`, or nullptr for a chunk past the matrix's columns.
+template <int BMT, int COLS, int NTHR, class Dst>
+__device__ __forceinline__ void stage_copy_out(const char* lds, int tid, int mrows, Dst dst) {
+  constexpr int NCH = COLS / 8;
+  static_assert((BMT * NCH) % NTHR == 0, "whole chunks per thread");
+#pragma unroll
+  for (int j = 0; j < BMT * NCH / NTHR; ++j) {
+    const int i = j * NTHR + tid;
+    const int row = i / NCH, ch = i % NCH;
+    if (row >= mrows) continue;
+    uint16_t* p = dst(row, ch);
+    if (p == nullptr) continue;
+    *reinterpret_cast<u32x4_t*>(p) = *reinterpret_cast<const u32x4_t*>(
+        lds + row * (COLS * 2) + ((ch ^ (row & (NCH - 1))) << 4));
+  }
+}
+
 template <int PHASE, int BKT, int NST, int WAVES, int BMT, int WMW>
 __global__ __launch_bounds__(WAVES * kWave) __attribute__((amdgpu_waves_per_eu(WAVES / 4, WAVES / 4)))
 void gemm_big_kernel(FfnArgs a, int NT, int ncu) {
@@ -791,66 +823,77 @@ void gemm_big_kernel(FfnArgs a, int NT, int ncu) {
   }
 
   // ---- epilogue (accumulator element v of lane l: row 8*(v/4) + 4*(l/32)
-  // + v%4, column l%32 of its 32 x 32 block)
-  if (PHASE == 3) {
-    // gate to columns 0..F-1, up to F..2F-1 of a [rows, 2F] buffer
-    uint16_t* G = static_cast<uint16_t*>(a.H) + static_cast<int64_t>(hrow0) * 2 * a.F;
-#pragma unroll
-    for (int ni = 0; ni < NB / 2; ++ni) {
-      const int col = n0 + wn * (128 / WN) + ni * 32 + (lane & 31);
-      if (col >= N) continue;
-#pragma unroll
-      for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int row = wm * WR + mi * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-          if (row < mrows) {
-            G[static_cast<int64_t>(row) * 2 * a.F + col] = f32_to_bf16(acc[mi][ni][v]);
-            G[static_cast<int64_t>(row) * 2 * a.F + a.F + col] =
-                f32_to_bf16(acc[mi][ni + NB / 2][v]);
-          }
-        }
-    }
-  } else if (PHASE == 1 || PHASE == 4) {
+  // + v%4, column l%32 of its 32 x 32 block), staged through the LDS ring,
+  // idle once every wave is past its K loop.
+  constexpr int NTHR = WAVES * kWave;
+  static_assert(BMT * 256 * 2 <= NST * G::STAGE, "the staged tile fits the LDS ring");
+  char* stg = lds_bytes;
+  if constexpr (PHASE == 1 || PHASE == 4) {
+    // H = SiLU(gate) * up: 128 columns from n0 of a [rows, F] matrix
     uint16_t* Hout = static_cast<uint16_t*>(a.H) + static_cast<int64_t>(hrow0) * a.F;
-    uint16_t* G = PHASE == 4 ? static_cast<uint16_t*>(a.ab) + static_cast<int64_t>(hrow0) * 2 * a.F
-                             : nullptr;
+    __syncthreads();
 #pragma unroll
-    for (int ni = 0; ni < NB / 2; ++ni) {
-      const int col = n0 + wn * (128 / WN) + ni * 32 + (lane & 31);
-      if (col >= N) continue;
+    for (int ni = 0; ni < NB / 2; ++ni)
 #pragma unroll
       for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int row = wm * WR + mi * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-          if (row < mrows) {
-            const float h = silu_f(acc[mi][ni][v]) * acc[mi][ni + NB / 2][v];
-            Hout[static_cast<int64_t>(row) * a.F + col] = f32_to_bf16(h);
-            if constexpr (PHASE == 4) {
-              G[static_cast<int64_t>(row) * 2 * a.F + col] = f32_to_bf16(acc[mi][ni][v]);
-              G[static_cast<int64_t>(row) * 2 * a.F + a.F + col] =
-                  f32_to_bf16(acc[mi][ni + NB / 2][v]);
-            }
-          }
+          const int col = wn * (128 / WN) + ni * 32 + (lane & 31);
+          stage_put<128>(stg, row, col, silu_f(acc[mi][ni][v]) * acc[mi][ni + NB / 2][v]);
         }
-    }
-  } else {
+    __syncthreads();
+    const int F = a.F;
+    stage_copy_out<BMT, 128, NTHR>(stg, tid, mrows, [&](int row, int ch) -> uint16_t* {
+      const int col = n0 + ch * 8;
+      return col < F ? Hout + static_cast<int64_t>(row) * F + col : nullptr;
+    });
+  }
+  if constexpr (PHASE == 3 || PHASE == 4) {
+    // the gate and up products apart: columns n0.. and F + n0.. of a
+    // [rows, 2F] matrix (tile columns 0..127 gate, 128..255 up)
+    uint16_t* Gout = static_cast<uint16_t*>(PHASE == 4 ? a.ab : a.H) +
+                     static_cast<int64_t>(hrow0) * 2 * a.F;
+    __syncthreads();
+#pragma unroll
+    for (int ni = 0; ni < NB; ++ni)
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int row = wm * WR + mi * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+          const int col = (ni / (NB / 2)) * 128 + wn * (128 / WN) + (ni % (NB / 2)) * 32 + (lane & 31);
+          stage_put<256>(stg, row, col, acc[mi][ni][v]);
+        }
+    __syncthreads();
+    const int F = a.F;
+    stage_copy_out<BMT, 256, NTHR>(stg, tid, mrows, [&](int row, int ch) -> uint16_t* {
+      const int half = ch >> 4;
+      const int col = n0 + (ch & 15) * 8;
+      return col < F ? Gout + static_cast<int64_t>(row) * 2 * F + half * F + col : nullptr;
+    });
+  }
+  if constexpr (PHASE == 2 || PHASE == 5) {
     uint16_t* Yout = routed ? static_cast<uint16_t*>(a.y_perm) + static_cast<int64_t>(arow0) * a.d
                             : static_cast<uint16_t*>(a.y_shared) +
                                   static_cast<int64_t>(hrow0 - a.T * a.k) * a.d;
+    __syncthreads();
 #pragma unroll
-    for (int ni = 0; ni < NB; ++ni) {
-      const int col = n0 + wn * (kBN2 / WN) + ni * 32 + (lane & 31);
-      if (col >= N) continue;
+    for (int ni = 0; ni < NB; ++ni)
 #pragma unroll
       for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int row = wm * WR + mi * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-          if (row < mrows) Yout[static_cast<int64_t>(row) * a.d + col] = f32_to_bf16(acc[mi][ni][v]);
+          const int col = wn * (kBN2 / WN) + ni * 32 + (lane & 31);
+          stage_put<256>(stg, row, col, acc[mi][ni][v]);
         }
-    }
+    __syncthreads();
+    const int ld = a.d;
+    stage_copy_out<BMT, 256, NTHR>(stg, tid, mrows, [&](int row, int ch) -> uint16_t* {
+      const int col = n0 + ch * 8;
+      return col < N ? Yout + static_cast<int64_t>(row) * ld + col : nullptr;
+    });
   }
 }
 
