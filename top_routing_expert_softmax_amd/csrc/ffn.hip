@@ -510,6 +510,137 @@ __device__ __forceinline__ void gemm_mainloop(
 #undef MOE_BK
 }
 
+// The loop of the four-wave tiles (one wave per SIMD, 128 x 128 outputs
+// each, K-contiguous operands through buffer resources): slices of 64 in a
+// ring of two, with the barrier in the middle of a slice.  The fragments
+// are read one half-slice (two 16-wide K steps) ahead into the other of two
+// register sets, so the MFMAs do not wait on the LDS at the barrier:
+//   phase A of slice s: the MFMAs of its first half (in registers) and the
+//     reads of its second half;
+//   boundary: slice s+1 has landed, and every wave is done reading slice
+//     s (its last reads belong to phase A);
+//   phase B: the DMA of slice s+2 into slice s's slot, the MFMAs of the
+//     second half and the reads of slice s+1's first half.
+// The MFMAs, fragment reads and DMA issues are interleaved evenly by
+// scheduling groups.
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+template <int BKT, int BMT, int NIA, int NIB, int MI, int NB, int MIA>
+__device__ __forceinline__ void gemm_mainloop_mid(
+    f32x16_t (&acc)[MI][NB], char* lds_bytes, int a_dst, int b_dst,
+    const int (&a_off)[MI], const int (&b_off)[NB], int lane, int nk, const BufOperands& bo,
+    const uint32_t (&aoff)[NIA], const uint32_t (&boff)[NIB]) {
+  using G = SliceGeom<BKT, BMT>;
+  static_assert(BKT == 64, "a slice is two halves of two 16-wide K steps");
+  constexpr int NDMA = NIA + NIB;
+  constexpr int MA = MIA > 0 ? MIA : 1;
+  constexpr int NMF = 2 * MIA * NB;                 // MFMAs per half-slice
+  constexpr int NRD = MIA > 0 ? 2 * (MIA + NB) : 0; // fragment reads per half-slice
+  const int key = ((lane & 31) / G::RPL) % G::CH;
+  const int khalf = lane >> 5;
+  bf16x8_t ra[2][2][MA], rb[2][2][NB];              // [set][k16 step of the half][block]
+
+#define MOE_DMA(slot, k0, d)                                                                    \
+  do {                                                                                          \
+    if ((d) < NIA)                                                                              \
+      lds_dma16_buf(bo.ra, aoff[(d) < NIA ? (d) : 0] + 2u * static_cast<uint32_t>(k0),          \
+                    lds_bytes + (slot) * G::STAGE + a_dst + ((d) < NIA ? (d) : 0) * G::RPI * G::ROW); \
+    else                                                                                        \
+      lds_dma16_buf(bo.rb, boff[(d) >= NIA ? (d) - NIA : 0] + 2u * static_cast<uint32_t>(k0),   \
+                    lds_bytes + (slot) * G::STAGE + b_dst + ((d) >= NIA ? (d) - NIA : 0) * 1024); \
+  } while (0)
+  // read r of half h: k16 step j = r / (MIA + NB), then A block q < MIA or B block
+#define MOE_RD(set, slot, h, r)                                                                 \
+  do {                                                                                          \
+    const int j_ = (r) / (MIA + NB), q_ = (r) % (MIA + NB);                                     \
+    const int pc_ = ((2 * (2 * (h) + j_) + khalf) ^ key) * 16;                                  \
+    const char* sb_ = lds_bytes + (slot) * G::STAGE;                                            \
+    if (q_ < MIA)                                                                               \
+      ra[set][j_][q_ < MIA ? q_ : 0] =                                                          \
+          *reinterpret_cast<const bf16x8_t*>(sb_ + a_off[q_ < MIA ? q_ : 0] + pc_);             \
+    else                                                                                        \
+      rb[set][j_][q_ >= MIA ? q_ - MIA : 0] =                                                   \
+          *reinterpret_cast<const bf16x8_t*>(sb_ + b_off[q_ >= MIA ? q_ - MIA : 0] + pc_);      \
+  } while (0)
+#define MOE_MF(set, m)                                                                          \
+  do {                                                                                          \
+    const int j_ = (m) / (MIA * NB), t_ = (m) % (MIA * NB);                                     \
+    const int mi_ = t_ / NB, ni_ = t_ % NB;                                                     \
+    acc[mi_][ni_] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[set][j_][mi_], rb[set][j_][ni_], \
+                                                            acc[mi_][ni_], 0, 0, 0);            \
+  } while (0)
+
+  // prologue: slices 0 and 1 in flight; slice 0 landed and its first half read
+#pragma unroll
+  for (int d = 0; d < NDMA; ++d) MOE_DMA(0, 0, d);
+#pragma unroll
+  for (int d = 0; d < NDMA; ++d) MOE_DMA(1, min(1, nk - 1) * BKT, d);
+  wait_vmcnt<NDMA>();
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  if constexpr (MIA > 0) {
+#pragma unroll
+    for (int r = 0; r < NRD; ++r) MOE_RD(0, 0, 0, r);
+  }
+  for (int s = 0; s < nk; ++s) {
+    const int slot = s & 1;
+    // phase A
+    if constexpr (MIA > 0) {
+#pragma unroll
+      for (int m = 0; m < NMF; ++m) {
+        MOE_MF(0, m);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+#pragma unroll
+        for (int r = 0; r < NRD; ++r) {
+          const int at = ((r + 1) * NMF) / NRD - 1;
+          if ((at < 0 ? 0 : at) == m) {
+            MOE_RD(1, slot, 1, r);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          }
+        }
+      }
+    }
+    wait_lgkm0();
+    wait_vmcnt<0>();
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    // phase B
+    const int kn = min(s + 2, nk - 1) * BKT;
+    if constexpr (MIA > 0) {
+#pragma unroll
+      for (int m = 0; m < NMF; ++m) {
+        MOE_MF(1, m);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+#pragma unroll
+        for (int d = 0; d < NDMA; ++d) {
+          if ((d * NMF) / NDMA == m) {
+            MOE_DMA(slot, kn, d);
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+          }
+        }
+#pragma unroll
+        for (int r = 0; r < NRD; ++r) {
+          const int at = ((r + 1) * NMF) / NRD - 1;
+          if ((at < 0 ? 0 : at) == m) {
+            MOE_RD(0, slot ^ 1, 0, r);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int d = 0; d < NDMA; ++d) MOE_DMA(slot, kn, d);
+    }
+  }
+  wait_vmcnt<0>();
+  wait_lgkm0();
+#undef MOE_DMA
+#undef MOE_RD
+#undef MOE_MF
+}
+
 // ---- epilogue through the LDS.  The block's bf16 output tile (BMT rows x
 // COLS columns) is first written into the idle LDS ring, its 16-byte chunks
 // XOR-swizzled by row (chunk c of row r at c ^ (r % NCH)), so that the two
@@ -575,6 +706,8 @@ void gemm_big_kernel(FfnArgs a, int NT, int ncu) {
   // dH = dO W2 and dX = [dA dB] [W1; W3] on the weights as stored)
   constexpr bool P1 = PHASE == 1 || PHASE == 3 || PHASE == 4;
   constexpr bool BMN = PHASE == 5;
+  // four waves of 128 x 128 run the mid-slice-barrier loop
+  constexpr bool kMidLoop = WAVES == 4 && !BMN && BKT == 64 && NST == 2;
   const int K = P1 ? a.d : a.F;
   const int nk_all = K / BKT;
   const int r = L % ncu;
@@ -761,9 +894,14 @@ void gemm_big_kernel(FfnArgs a, int NT, int ncu) {
   const int mia = __builtin_amdgcn_readfirstlane(
       rows_w <= 0 ? 0 : (rows_w >= WR ? MI : (rows_w + 31) / 32));
 #define MOE_MAINLOOP(X)                                                                    \
-  gemm_mainloop<BKT, BMT, NST, NIA, NIB, MI, NB, (X), BMN, !BMN>(                           \
-      acc, asrc, bsrc, lds_bytes, a_dst, b_dst, a_off, b_off, lane, nk, b_kstride, b_kjump,  \
-      b_jump, bo, aoff, boff)
+  if constexpr (kMidLoop) {                                                                 \
+    gemm_mainloop_mid<BKT, BMT, NIA, NIB, MI, NB, (X)>(acc, lds_bytes, a_dst, b_dst, a_off,  \
+                                                       b_off, lane, nk, bo, aoff, boff);     \
+  } else {                                                                                  \
+    gemm_mainloop<BKT, BMT, NST, NIA, NIB, MI, NB, (X), BMN, !BMN>(                         \
+        acc, asrc, bsrc, lds_bytes, a_dst, b_dst, a_off, b_off, lane, nk, b_kstride,         \
+        b_kjump, b_jump, bo, aoff, boff);                                                   \
+  }
   switch (mia) {
     case 4: if constexpr (MI >= 4) MOE_MAINLOOP(MI >= 4 ? 4 : 0); break;
     case 3: if constexpr (MI >= 3) MOE_MAINLOOP(MI >= 3 ? 3 : 0); break;
@@ -898,10 +1036,14 @@ void gemm_big_kernel(FfnArgs a, int NT, int ncu) {
 }
 
 // The configuration the library launches: K slices of 64, a ring of two
-// slices in LDS, eight wavefronts.
+// slices in LDS; four wavefronts of 128 x 128 for the K-contiguous forms
+// (phases 1-4), eight of 128 x 64 for the MN-contiguous one (phase 5) and
+// the weight gradients.
 constexpr int kBKsel = 64;
 constexpr int kNSTsel = 2;
 constexpr int kWavesSel = 8;
+template <int PHASE>
+constexpr int big_waves() { return PHASE == 5 ? 8 : 4; }
 
 // The dynamic LDS above the default limit is a per-device setting of a
 // kernel: set it once for each (kernel, device) the process launches on.
@@ -927,10 +1069,11 @@ hipError_t launch_gemm_big(const FfnArgs& a, int nt, int64_t mt, int ncu, hipStr
   const unsigned g = static_cast<unsigned>(kXcds * ((lmax + kXcds - 1) / kXcds) + ncu);
   constexpr size_t lds = static_cast<size_t>(kNSTsel) * SliceGeom<kBKsel, kBM2>::STAGE;
   static_assert(lds <= 160 * 1024, "LDS ring exceeds the 160 KB of a CU");
-  constexpr auto kern = &gemm_big_kernel<PHASE, kBKsel, kNSTsel, kWavesSel, kBM2, kWM>;
+  constexpr int kWaves = big_waves<PHASE>();
+  constexpr auto kern = &gemm_big_kernel<PHASE, kBKsel, kNSTsel, kWaves, kBM2, kWM>;
   const hipError_t attr = allow_dynamic_lds<kern>(static_cast<int>(lds));
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL(kern, dim3(g), dim3(kWavesSel * kWave), lds, s, a, nt, ncu);
+  hipLaunchKernelGGL(kern, dim3(g), dim3(kWaves * kWave), lds, s, a, nt, ncu);
   return hipGetLastError();
 }
 
