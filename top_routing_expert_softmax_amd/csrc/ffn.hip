@@ -1195,9 +1195,13 @@ struct WgradArgs {
   int M, N, E, NT;
 };
 
+// WAVES = 4 runs the mid-slice-barrier loop through buffer resources (the
+// tile's rows then lie within 2^31 bytes: ld < 2^22); WAVES = 8 the
+// barrier-per-slice loop on 64-bit addresses.
 template <int BKT, int NST, int WAVES>
 __global__ __launch_bounds__(WAVES * kWave) __attribute__((amdgpu_waves_per_eu(WAVES / 4, WAVES / 4)))
 void gemm_wgrad_kernel(WgradArgs a) {
+  constexpr bool kMid = WAVES == 4;
   constexpr int BMT = 256;
   using G = SliceGeom<BKT, BMT>;
   constexpr int WN = WAVES / 2;
@@ -1256,9 +1260,27 @@ void gemm_wgrad_kernel(WgradArgs a) {
 #pragma unroll
   for (int ni = 0; ni < NB; ++ni)
     b_off[ni] = BMT * G::ROW + (wn * (kBN2 / WN) + ni * 32 + (lane & 31)) * G::ROW;
-  if (nk > 0)
-    gemm_mainloop<BKT, BMT, NST, NIA, NIB, MI, NB, MI, false>(acc, asrc, bsrc, lds_bytes, a_dst, b_dst,
-                                                       a_off, b_off, lane, nk, 1, 1 << 30, 0);
+  if constexpr (kMid) {
+    static_assert(BKT == 64 && NST == 2, "the mid-slice loop's ring");
+    BufOperands bo;
+    bo.ra = buffer_rsrc(a.A + static_cast<int64_t>(m0) * a.ld + k0);
+    bo.rb = buffer_rsrc(a.B + static_cast<int64_t>(n0) * a.ld + k0);
+    uint32_t aoff[NIA], boff[NIB];
+#pragma unroll
+    for (int i = 0; i < NIA; ++i)
+      aoff[i] = static_cast<uint32_t>((asrc[i] - (a.A + static_cast<int64_t>(m0) * a.ld + k0)) * 2);
+#pragma unroll
+    for (int i = 0; i < NIB; ++i)
+      boff[i] = static_cast<uint32_t>((bsrc[i] - (a.B + static_cast<int64_t>(n0) * a.ld + k0)) * 2);
+    if (nk > 0)
+      gemm_mainloop_mid<BKT, BMT, NIA, NIB, MI, NB, MI>(acc, lds_bytes, a_dst, b_dst, a_off, b_off,
+                                                         lane, nk, bo, aoff, boff);
+  } else {
+    if (nk > 0)
+      gemm_mainloop<BKT, BMT, NST, NIA, NIB, MI, NB, MI, false>(acc, asrc, bsrc, lds_bytes, a_dst,
+                                                                b_dst, a_off, b_off, lane, nk, 1,
+                                                                1 << 30, 0);
+  }
   // (a segment with no rows stores zeros)
 #pragma unroll
   for (int ni = 0; ni < NB; ++ni) {
@@ -1282,11 +1304,19 @@ hipError_t launch_wgrad(const WgradArgs& a0, int nseg, hipStream_t s) {
   a.NT = (a.N + kBN2 - 1) / kBN2;
   const int MT = (a.M + 255) / 256;
   constexpr size_t lds = static_cast<size_t>(kNSTsel) * SliceGeom<kBKsel, 256>::STAGE;
-  constexpr auto kern = &gemm_wgrad_kernel<kBKsel, kNSTsel, kWavesSel>;
-  const hipError_t attr = allow_dynamic_lds<kern>(static_cast<int>(lds));
-  if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(MT * a.NT), static_cast<unsigned>(nseg)),
-                     dim3(kWavesSel * kWave), lds, s, a);
+  const dim3 grid(static_cast<unsigned>(MT * a.NT), static_cast<unsigned>(nseg));
+  if (a.ld < (int64_t(1) << 22)) {
+    // a tile's 256 rows of ld bf16 fit the 32-bit offsets of a buffer load
+    constexpr auto kern = &gemm_wgrad_kernel<kBKsel, kNSTsel, 4>;
+    const hipError_t attr = allow_dynamic_lds<kern>(static_cast<int>(lds));
+    if (attr != hipSuccess) return attr;
+    hipLaunchKernelGGL(kern, grid, dim3(4 * kWave), lds, s, a);
+  } else {
+    constexpr auto kern = &gemm_wgrad_kernel<kBKsel, kNSTsel, kWavesSel>;
+    const hipError_t attr = allow_dynamic_lds<kern>(static_cast<int>(lds));
+    if (attr != hipSuccess) return attr;
+    hipLaunchKernelGGL(kern, grid, dim3(kWavesSel * kWave), lds, s, a);
+  }
   return hipGetLastError();
 }
 
