@@ -894,6 +894,7 @@ void gemm_big_kernel(FfnArgs a, int NT, int ncu) {
   const int mia = __builtin_amdgcn_readfirstlane(
       rows_w <= 0 ? 0 : (rows_w >= WR ? MI : (rows_w + 31) / 32));
 #define MOE_MAINLOOP(X)                                                                    \
+  {                                                                                         \
   if constexpr (kMidLoop) {                                                                 \
     gemm_mainloop_mid<BKT, BMT, NIA, NIB, MI, NB, (X)>(acc, lds_bytes, a_dst, b_dst, a_off,  \
                                                        b_off, lane, nk, bo, aoff, boff);     \
@@ -901,6 +902,7 @@ void gemm_big_kernel(FfnArgs a, int NT, int ncu) {
     gemm_mainloop<BKT, BMT, NST, NIA, NIB, MI, NB, (X), BMN, !BMN>(                         \
         acc, asrc, bsrc, lds_bytes, a_dst, b_dst, a_off, b_off, lane, nk, b_kstride,         \
         b_kjump, b_jump, bo, aoff, boff);                                                   \
+  }                                                                                         \
   }
   switch (mia) {
     case 4: if constexpr (MI >= 4) MOE_MAINLOOP(MI >= 4 ? 4 : 0); break;
