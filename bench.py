@@ -31,17 +31,20 @@ PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3        # MI355X fp32 vector
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 
-# HBM bytes per moe_expert_ffn call, as measured by separate rocprofv3 runs
-# (FETCH_SIZE, then WRITE_SIZE, scaled by a plain copy of known size), keyed
-# by the workload and the sha256 prefix of the expert-FFN sources (ffn.hip,
+# HBM bytes per expert-FFN call (moe_expert_ffn, or moe_expert_ffn_fp8 for
+# FP8 weights), as measured by separate rocprofv3 runs (FETCH_SIZE, then
+# WRITE_SIZE, scaled by a plain copy of known size), keyed by the workload,
+# the weight type and the sha256 prefix of the expert-FFN sources (ffn.hip,
 # ffn_stream.hip) they were taken with (softmax router), with the profile
 # summary that holds the counts.  The bench line reports the stored figure
 # and names that summary ("traffic_from"); a changed kernel reports null
 # until it is profiled again.
 MEASURED_TRAFFIC = {
-    ("skewed_train", "7be7a51ef5d3d080"): (3.6371e10, "profiles/moe_layer_skewed_train.md"),
-    ("dsmoe16b_prefill", "7be7a51ef5d3d080"): (3.2549e9, "profiles/moe_layer_dsmoe16b_prefill.md"),
-    ("mixtral_prefill", "7be7a51ef5d3d080"): (9.7518e9, "profiles/moe_layer_mixtral_prefill.md"),
+    ("skewed_train", "bf16", "e80735e819952909"): (3.3062e10, "profiles/moe_layer_skewed_train.md"),
+    ("dsmoe16b_prefill", "bf16", "e80735e819952909"): (3.1441e9, "profiles/moe_layer_dsmoe16b_prefill.md"),
+    ("mixtral_prefill", "bf16", "e80735e819952909"): (6.4243e9, "profiles/moe_layer_mixtral_prefill.md"),
+    ("dsv3_decode", "bf16", "e80735e819952909"): (1.9664e10, "profiles/moe_layer_dsv3_decode.md"),
+    ("dsv3_decode", "fp8", "e80735e819952909"): (1.0109e10, "profiles/moe_layer_dsv3_decode_fp8_weights.md"),
 }
 
 
@@ -468,8 +471,8 @@ def main():
             h.update(fh.read())
     src_hash = h.hexdigest()[:16]
     # counters were taken with the softmax router (the routing decides the rows)
-    measured = (MEASURED_TRAFFIC.get((cfg.name, src_hash))
-                if args.router == "softmax" and fp8 is None else None)
+    measured = (MEASURED_TRAFFIC.get((cfg.name, args.weights, src_hash))
+                if args.router == "softmax" else None)
     roof["traffic"] = measured[0] if measured else None
     roof["traffic_from"] = (f"{measured[1]} (rocprofv3 FETCH_SIZE/WRITE_SIZE, sources "
                             f"{src_hash})" if measured else None)
