@@ -288,10 +288,15 @@ __device__ __forceinline__ void stream_block_fp8(const StreamArgs& a, int seg, i
 #pragma unroll
     for (int b = 0; b < NB; ++b) acc[tg][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
+  // The K steps go to the waves in batches of U, round robin: wave w takes
+  // batches w, w + 4, ..., so the four waves of a block read adjacent
+  // pieces of every weight row at the same moment (rows of d = 7168 codes
+  // are read front to back once, not in four far-apart streams); the steps
+  // past the whole batches go to wave (whole batches) % 4.
   const int nsteps = K / 64;
-  const int s0 = wave * nsteps / kSWaves;
-  const int s1 = (wave + 1) * nsteps / kSWaves;
-  int s = s0;
+  const int nbt = nsteps / U;
+  const int nbw = nbt > wave ? (nbt - wave + kSWaves - 1) / kSWaves : 0;
+  constexpr int SST = kSWaves * U;          // steps from one of a wave's batches to the next
 #define MOE_FLOAD(FQ, FA, S0)                                                              \
   _Pragma("unroll") for (int u = 0; u < U; ++u) {                                         \
     const int kk = ((S0) + u) * 64 + kq;                                                  \
@@ -314,47 +319,51 @@ __device__ __forceinline__ void stream_block_fp8(const StreamArgs& a, int seg, i
                                                               0, 0, 0);                    \
       }                                                                                    \
     }
-  if (s + 2 * U <= s1) {
+  int j = 0;
+  if (nbw >= 2) {
+    // two batches in flight: load batch j+1, then use batch j
     u32x4_t q0[U][NB], q1[U][NB];
     bf16x8_t x0[U][TG][2], x1[U][TG][2];
-    MOE_FLOAD(q0, x0, s);
-    s += U;
-    for (; s + 2 * U <= s1; s += 2 * U) {
-      MOE_FLOAD(q1, x1, s);
+    MOE_FLOAD(q0, x0, wave * U);
+    j = 1;
+    for (; j + 2 <= nbw; j += 2) {
+      MOE_FLOAD(q1, x1, (wave + kSWaves * j) * U);
       MOE_FMFMA(q0, x0);
-      MOE_FLOAD(q0, x0, s + U);
+      MOE_FLOAD(q0, x0, (wave + kSWaves * j) * U + SST);
       MOE_FMFMA(q1, x1);
     }
     MOE_FMFMA(q0, x0);
   }
-  for (; s + U <= s1; s += U) {
+  for (; j < nbw; ++j) {
     u32x4_t q[U][NB];
     bf16x8_t xa[U][TG][2];
-    MOE_FLOAD(q, xa, s);
+    MOE_FLOAD(q, xa, (wave + kSWaves * j) * U);
     MOE_FMFMA(q, xa);
   }
   if constexpr (U > 1) {
-    for (; s < s1; ++s) {
-      u32x4_t q[1][NB];
-      bf16x8_t xa[1][TG][2];
-      {
-        const int kk = s * 64 + kq;
+    if (wave == nbt % kSWaves) {
+      for (int s = nbt * U; s < nsteps; ++s) {
+        u32x4_t q[1][NB];
+        bf16x8_t xa[1][TG][2];
+        {
+          const int kk = s * 64 + kq;
 #pragma unroll
-        for (int b = 0; b < NB; ++b) q[0][b] = *reinterpret_cast<const u32x4_t*>(wrow[b] + kk);
+          for (int b = 0; b < NB; ++b) q[0][b] = *reinterpret_cast<const u32x4_t*>(wrow[b] + kk);
 #pragma unroll
-        for (int tg = 0; tg < TG; ++tg) {
-          xa[0][tg][0] = *reinterpret_cast<const bf16x8_t*>(arow[tg] + kk);
-          xa[0][tg][1] = *reinterpret_cast<const bf16x8_t*>(arow[tg] + kk + 8);
+          for (int tg = 0; tg < TG; ++tg) {
+            xa[0][tg][0] = *reinterpret_cast<const bf16x8_t*>(arow[tg] + kk);
+            xa[0][tg][1] = *reinterpret_cast<const bf16x8_t*>(arow[tg] + kk + 8);
+          }
         }
-      }
 #pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        const bf16x8_t lo = e4m3x8_to_bf16(q[0][b][0], q[0][b][1]);
-        const bf16x8_t hi = e4m3x8_to_bf16(q[0][b][2], q[0][b][3]);
+        for (int b = 0; b < NB; ++b) {
+          const bf16x8_t lo = e4m3x8_to_bf16(q[0][b][0], q[0][b][1]);
+          const bf16x8_t hi = e4m3x8_to_bf16(q[0][b][2], q[0][b][3]);
 #pragma unroll
-        for (int tg = 0; tg < TG; ++tg) {
-          acc[tg][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[0][tg][0], lo, acc[tg][b], 0, 0, 0);
-          acc[tg][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[0][tg][1], hi, acc[tg][b], 0, 0, 0);
+          for (int tg = 0; tg < TG; ++tg) {
+            acc[tg][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[0][tg][0], lo, acc[tg][b], 0, 0, 0);
+            acc[tg][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[0][tg][1], hi, acc[tg][b], 0, 0, 0);
+          }
         }
       }
     }
