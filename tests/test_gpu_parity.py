@@ -77,6 +77,16 @@ SMALL_CASES = {
     # phase 1 split in four parts (K = 4096), with a shared expert
     "bf16_split_k4_shared": ("dsmoe16b_prefill", dict(T=300, d_model=4096, E=4, E_shared=1,
                                                       k=2, d_ff=1024, CF=1.25)),
+    # the smallest dimensions the boundary takes (d = F = 64): the grouped
+    # GEMM's K loops run a single 64-wide slice, whose two prologue loads
+    # and the loop's last DMA issues all target that slice; H's one column
+    # tile holds 64 of its 128 columns
+    "bf16_one_slice": ("mixtral_prefill", dict(T=300, d_model=64, E=2, k=1, d_ff=64, CF=None)),
+    # F = 192: H's second column tile holds 64 columns (weight rows past F
+    # read as zeros, their outputs not stored); d = 320: y's second column
+    # tile holds 64 columns
+    "bf16_partial_col_tiles": ("mixtral_prefill", dict(T=600, d_model=320, E=2, k=2, d_ff=192,
+                                                       CF=None)),
 }
 
 
