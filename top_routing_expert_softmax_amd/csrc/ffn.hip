@@ -16,9 +16,12 @@
 // Both operands are K-contiguous in memory ([rows][K] activations and
 // [out][in] weights), which is the layout bf16 MFMA operands want.
 //
-// bf16, large segments: 256 x 256 output tiles, 8 wavefronts, K slices of
-// 64 streamed into a two-slot LDS ring by direct-to-LDS loads,
-// v_mfma_f32_32x32x16_bf16 with fp32 accumulators.  Tiles of the last,
+// bf16, large segments: 256 x 256 output tiles, K slices of 64 streamed
+// into a two-slot LDS ring by direct-to-LDS loads, v_mfma_f32_32x32x16_bf16
+// with fp32 accumulators; four wavefronts of 128 x 128 with the barrier in
+// the middle of each slice (gemm_mainloop_mid) for the K-contiguous
+// phases, eight of 128 x 64 with a barrier per slice for the MN-contiguous
+// backward form.  Tiles of the last,
 // partial wave of the chip are split along K and summed in a fixed order
 // (gemm_big_kernel).  bf16, decode-sized segments: 128-row tiles with
 // register prefetch (gemm_bf16_kernel).  fp32 (small configs): VALU tiles,
@@ -309,12 +312,13 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(FfnArgs a) {
 
 // ---------------------------------------------- bf16 MFMA, BM x 256 tiles --
 //
-// Block tile BM rows x 256 B-rows (BM = kBM2), 8 wavefronts as WM x (8/WM),
-// each owning (BM/WM) x (256*WM/8) outputs in 32 x 32 blocks of
-// v_mfma_f32_32x32x16_bf16 with fp32 accumulators.  Operand tiles move
-// global -> LDS with global_load_lds_dwordx4 (no staging registers)
-// through an NST-stage ring of K-slices of BKT elements: while slice s is
-// multiplied, the loads of slices s+1 .. s+NST-1 are in flight.  Taller
+// Block tile BM rows x 256 B-rows (BM = kBM2), WAVES wavefronts as WM x
+// (WAVES/WM), each owning (BM/WM) x (256*WM/WAVES) outputs in 32 x 32
+// blocks of v_mfma_f32_32x32x16_bf16 with fp32 accumulators.  Operand
+// tiles move global -> LDS with direct-to-LDS loads (buffer loads for the
+// K-contiguous operands; no staging registers) through an NST-stage ring
+// of K-slices of BKT elements: while slice s is multiplied, the loads of
+// slices s+1 .. s+NST-1 are in flight.  Taller
 // tiles carry more rows per weight byte streamed: an expert segment of c
 // rows streams its weights ceil(c / BM) times.
 // LDS rows hold BKT bf16 (ROW bytes = CH chunks of 16 B).  The LDS has 64
