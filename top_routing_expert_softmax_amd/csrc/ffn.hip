@@ -19,9 +19,8 @@
 // bf16, large segments: 256 x 256 output tiles, K slices of 64 streamed
 // into a two-slot LDS ring by direct-to-LDS loads, v_mfma_f32_32x32x16_bf16
 // with fp32 accumulators; four wavefronts of 128 x 128 with the barrier in
-// the middle of each slice (gemm_mainloop_mid) for the K-contiguous
-// phases, eight of 128 x 64 with a barrier per slice for the MN-contiguous
-// backward form.  Tiles of the last,
+// the middle of each slice (gemm_mainloop_mid, and gemm_mainloop_mid_bmn
+// for the MN-contiguous backward form).  Tiles of the last,
 // partial wave of the chip are split along K and summed in a fixed order
 // (gemm_big_kernel).  bf16, decode-sized segments: 128-row tiles with
 // register prefetch (gemm_bf16_kernel).  fp32 (small configs): VALU tiles,
@@ -645,6 +644,140 @@ __device__ __forceinline__ void gemm_mainloop_mid(
 #undef MOE_MF
 }
 
+// The mid-slice-barrier loop for the MN-contiguous form (phase 5, dH and
+// dX on the weights as stored), four waves of 128 x 128.  Its B fragments
+// come from LDS transpose reads, before which the compiler waits for every
+// LDS-DMA load in flight; so a whole slice's B fragments are read at the
+// start of phase B, right after the barrier (when no load is in flight),
+// into the other of two slice-sized register sets, and only the A
+// fragments (ordinary reads) are read a half-slice ahead as in
+// gemm_mainloop_mid.  Operands through 64-bit addresses (asrc, bsrc; B
+// advancing k0 * b_kstride, plus b_jump from K = b_kjump on).
+template <int BKT, int BMT, int NIA, int NIB, int MI, int NB, int MIA>
+__device__ __forceinline__ void gemm_mainloop_mid_bmn(
+    f32x16_t (&acc)[MI][NB], const uint16_t* const (&asrc)[NIA],
+    const uint16_t* const (&bsrc)[NIB], char* lds_bytes, int a_dst, int b_dst,
+    const int (&a_off)[MI], const int (&b_off)[NB], int lane, int nk, int64_t b_kstride,
+    int b_kjump, int64_t b_jump) {
+  using G = SliceGeom<BKT, BMT>;
+  static_assert(BKT == 64, "a slice is two halves of two 16-wide K steps");
+  constexpr int NDMA = NIA + NIB;
+  constexpr int MA = MIA > 0 ? MIA : 1;
+  constexpr int NMF = 2 * MIA * NB;                 // MFMAs per half-slice
+  constexpr int NRA = 2 * MIA;                      // A fragment reads per half-slice
+  const int key = ((lane & 31) / G::RPL) % G::CH;
+  const int khalf = lane >> 5;
+  bf16x8_t ra[2][2][MA];                            // [set][k16 step of the half][mi]
+  bf16x8_t rb[2][4][NB];                            // [set][k16 step of the slice][ni]
+#define MOE_BK(k0) (static_cast<int64_t>(k0) * b_kstride + ((k0) >= b_kjump ? b_jump : 0))
+#define MOE_MDMA(slot, k0, d)                                                                   \
+  do {                                                                                          \
+    if ((d) < NIA)                                                                              \
+      lds_dma16(asrc[(d) < NIA ? (d) : 0] + (k0),                                               \
+                reinterpret_cast<uint32_t*>(lds_bytes + (slot) * G::STAGE + a_dst +             \
+                                            ((d) < NIA ? (d) : 0) * G::RPI * G::ROW));          \
+    else                                                                                        \
+      lds_dma16(bsrc[(d) >= NIA ? (d) - NIA : 0] + MOE_BK(k0),                                  \
+                reinterpret_cast<uint32_t*>(lds_bytes + (slot) * G::STAGE + b_dst +             \
+                                            ((d) >= NIA ? (d) - NIA : 0) * 1024));              \
+  } while (0)
+#define MOE_MRDA(set, slot, h, r)                                                               \
+  do {                                                                                          \
+    const int j_ = (r) / MA, q_ = (r) % MA;                                                     \
+    const int pc_ = ((2 * (2 * (h) + j_) + khalf) ^ key) * 16;                                  \
+    ra[set][j_][q_] = *reinterpret_cast<const bf16x8_t*>(lds_bytes + (slot) * G::STAGE +        \
+                                                         a_off[q_] + pc_);                      \
+  } while (0)
+#define MOE_MRDB(set, slot)                                                                     \
+  _Pragma("unroll") for (int ks_ = 0; ks_ < 4; ++ks_)                                           \
+    _Pragma("unroll") for (int ni_ = 0; ni_ < NB; ++ni_)                                        \
+      rb[set][ks_][ni_] = lds_read_tr_pair(lds_bytes + (slot) * G::STAGE + b_off[ni_] +         \
+                                           ks_ * 16 * kBRowMN, 4 * kBRowMN)
+#define MOE_MMF(aset, bset, h, m)                                                               \
+  do {                                                                                          \
+    const int j_ = (m) / (MIA * NB), t_ = (m) % (MIA * NB);                                     \
+    const int mi_ = t_ / NB, ni_ = t_ % NB;                                                     \
+    acc[mi_][ni_] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(                                    \
+        ra[aset][j_][mi_], rb[bset][2 * (h) + j_][ni_], acc[mi_][ni_], 0, 0, 0);                \
+  } while (0)
+
+  // prologue: slices 0 and 1 in flight; slice 0 landed, its A first half
+  // and all its B fragments read
+#pragma unroll
+  for (int d = 0; d < NDMA; ++d) MOE_MDMA(0, 0, d);
+#pragma unroll
+  for (int d = 0; d < NDMA; ++d) MOE_MDMA(1, min(1, nk - 1) * BKT, d);
+  wait_vmcnt<0>();
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  if constexpr (MIA > 0) {
+#pragma unroll
+    for (int r = 0; r < NRA; ++r) MOE_MRDA(0, 0, 0, r);
+  }
+  MOE_MRDB(0, 0);
+
+  // one iteration on slice S whose B fragments sit in register set BSET
+#define MOE_MITER(S, BSET)                                                                      \
+  do {                                                                                          \
+    const int s_ = (S);                                                                         \
+    const int slot_ = s_ & 1;                                                                   \
+    if constexpr (MIA > 0) {                                                                    \
+      _Pragma("unroll") for (int m = 0; m < NMF; ++m) {                                         \
+        MOE_MMF(0, BSET, 0, m);                                                                 \
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                      \
+        _Pragma("unroll") for (int r = 0; r < NRA; ++r) {                                       \
+          if ((((r + 1) * NMF) / NRA - 1) == m) {                                               \
+            MOE_MRDA(1, slot_, 1, r);                                                           \
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                  \
+          }                                                                                     \
+        }                                                                                       \
+      }                                                                                         \
+    }                                                                                           \
+    wait_lgkm0();                                                                               \
+    wait_vmcnt<0>();                                                                            \
+    __builtin_amdgcn_sched_barrier(0);                                                          \
+    __builtin_amdgcn_s_barrier();                                                               \
+    __builtin_amdgcn_sched_barrier(0);                                                          \
+    /* slice s+1's B fragments, with no load in flight */                                       \
+    MOE_MRDB(1 - (BSET), slot_ ^ 1);                                                            \
+    __builtin_amdgcn_sched_barrier(0);                                                          \
+    const int kn_ = min(s_ + 2, nk - 1) * BKT;                                                  \
+    if constexpr (MIA > 0) {                                                                    \
+      _Pragma("unroll") for (int m = 0; m < NMF; ++m) {                                         \
+        MOE_MMF(1, BSET, 1, m);                                                                 \
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                      \
+        _Pragma("unroll") for (int d = 0; d < NDMA; ++d) {                                      \
+          if ((d * NMF) / NDMA == m) {                                                          \
+            MOE_MDMA(slot_, kn_, d);                                                            \
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);                                  \
+          }                                                                                     \
+        }                                                                                       \
+        _Pragma("unroll") for (int r = 0; r < NRA; ++r) {                                       \
+          if ((((r + 1) * NMF) / NRA - 1) == m) {                                               \
+            MOE_MRDA(0, slot_ ^ 1, 0, r);                                                       \
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                  \
+          }                                                                                     \
+        }                                                                                       \
+      }                                                                                         \
+    } else {                                                                                    \
+      _Pragma("unroll") for (int d = 0; d < NDMA; ++d) MOE_MDMA(slot_, kn_, d);                 \
+    }                                                                                           \
+  } while (0)
+  for (int s = 0; s < nk; s += 2) {
+    MOE_MITER(s, 0);
+    if (s + 1 < nk) MOE_MITER(s + 1, 1);
+  }
+  wait_vmcnt<0>();
+  wait_lgkm0();
+#undef MOE_MITER
+#undef MOE_MMF
+#undef MOE_MRDB
+#undef MOE_MRDA
+#undef MOE_MDMA
+#undef MOE_BK
+}
+
 // ---- epilogue through the LDS.  The block's bf16 output tile (BMT rows x
 // COLS columns) is first written into the idle LDS ring, its 16-byte chunks
 // XOR-swizzled by row (chunk c of row r at c ^ (r % NCH)), so that the two
@@ -710,8 +843,9 @@ void gemm_big_kernel(FfnArgs a, int NT, int ncu) {
   // dH = dO W2 and dX = [dA dB] [W1; W3] on the weights as stored)
   constexpr bool P1 = PHASE == 1 || PHASE == 3 || PHASE == 4;
   constexpr bool BMN = PHASE == 5;
-  // four waves of 128 x 128 run the mid-slice-barrier loop
+  // four waves of 128 x 128 run the mid-slice-barrier loops
   constexpr bool kMidLoop = WAVES == 4 && !BMN && BKT == 64 && NST == 2;
+  constexpr bool kMidBmn = WAVES == 4 && BMN && BKT == 64 && NST == 2;
   const int K = P1 ? a.d : a.F;
   const int nk_all = K / BKT;
   const int r = L % ncu;
@@ -902,6 +1036,10 @@ void gemm_big_kernel(FfnArgs a, int NT, int ncu) {
   if constexpr (kMidLoop) {                                                                 \
     gemm_mainloop_mid<BKT, BMT, NIA, NIB, MI, NB, (X)>(acc, lds_bytes, a_dst, b_dst, a_off,  \
                                                        b_off, lane, nk, bo, aoff, boff);     \
+  } else if constexpr (kMidBmn) {                                                           \
+    gemm_mainloop_mid_bmn<BKT, BMT, NIA, NIB, MI, NB, (X)>(acc, asrc, bsrc, lds_bytes, a_dst, \
+                                                           b_dst, a_off, b_off, lane, nk,    \
+                                                           b_kstride, b_kjump, b_jump);      \
   } else {                                                                                  \
     gemm_mainloop<BKT, BMT, NST, NIA, NIB, MI, NB, (X), BMN, !BMN>(                         \
         acc, asrc, bsrc, lds_bytes, a_dst, b_dst, a_off, b_off, lane, nk, b_kstride,         \
@@ -1042,14 +1180,13 @@ void gemm_big_kernel(FfnArgs a, int NT, int ncu) {
 }
 
 // The configuration the library launches: K slices of 64, a ring of two
-// slices in LDS; four wavefronts of 128 x 128 for the K-contiguous forms
-// (phases 1-4), eight of 128 x 64 for the MN-contiguous one (phase 5) and
-// the weight gradients.
+// slices in LDS, four wavefronts of 128 x 128 with the mid-slice barrier
+// for every phase (the weight gradients too, when their offsets fit 32
+// bits; else eight wavefronts of 128 x 64).
 constexpr int kBKsel = 64;
 constexpr int kNSTsel = 2;
-constexpr int kWavesSel = 8;
-template <int PHASE>
-constexpr int big_waves() { return PHASE == 5 ? 8 : 4; }
+constexpr int kWavesSel = 8;       // wgrad fallback for offsets past 32 bits
+constexpr int kBigWaves = 4;
 
 // The dynamic LDS above the default limit is a per-device setting of a
 // kernel: set it once for each (kernel, device) the process launches on.
@@ -1075,7 +1212,7 @@ hipError_t launch_gemm_big(const FfnArgs& a, int nt, int64_t mt, int ncu, hipStr
   const unsigned g = static_cast<unsigned>(kXcds * ((lmax + kXcds - 1) / kXcds) + ncu);
   constexpr size_t lds = static_cast<size_t>(kNSTsel) * SliceGeom<kBKsel, kBM2>::STAGE;
   static_assert(lds <= 160 * 1024, "LDS ring exceeds the 160 KB of a CU");
-  constexpr int kWaves = big_waves<PHASE>();
+  constexpr int kWaves = kBigWaves;
   constexpr auto kern = &gemm_big_kernel<PHASE, kBKsel, kNSTsel, kWaves, kBM2, kWM>;
   const hipError_t attr = allow_dynamic_lds<kern>(static_cast<int>(lds));
   if (attr != hipSuccess) return attr;
@@ -1313,10 +1450,10 @@ hipError_t launch_wgrad(const WgradArgs& a0, int nseg, hipStream_t s) {
   const dim3 grid(static_cast<unsigned>(MT * a.NT), static_cast<unsigned>(nseg));
   if (a.ld < (int64_t(1) << 22)) {
     // a tile's 256 rows of ld bf16 fit the 32-bit offsets of a buffer load
-    constexpr auto kern = &gemm_wgrad_kernel<kBKsel, kNSTsel, 4>;
+    constexpr auto kern = &gemm_wgrad_kernel<kBKsel, kNSTsel, kBigWaves>;
     const hipError_t attr = allow_dynamic_lds<kern>(static_cast<int>(lds));
     if (attr != hipSuccess) return attr;
-    hipLaunchKernelGGL(kern, grid, dim3(4 * kWave), lds, s, a);
+    hipLaunchKernelGGL(kern, grid, dim3(kBigWaves * kWave), lds, s, a);
   } else {
     constexpr auto kern = &gemm_wgrad_kernel<kBKsel, kNSTsel, kWavesSel>;
     const hipError_t attr = allow_dynamic_lds<kern>(static_cast<int>(lds));
