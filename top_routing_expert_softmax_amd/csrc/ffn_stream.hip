@@ -373,12 +373,15 @@ __device__ __forceinline__ void stream_block_fp8(const StreamArgs& a, int seg, i
   stream_finish<PHASE, TG, true, NB>(a, acc, seg, rows, arow0, hrow0, n0, red);
 }
 
-// Grid: x = weight-row group, y = segment (routed experts, then shared).
+// Grid: x = weight-row group, y = segment (shared experts, then routed).
 // Segments with no rows, or more than kStreamMaxRows rows, exit at once.
 template <int PHASE, bool FP8>
 __global__ __launch_bounds__(kSWaves * kWave) void ffn_stream_kernel(StreamArgs a) {
   __shared__ f32x4_t red[kSWaves * (kSNB8 > kSNB ? kSNB8 : kSNB) * kWave];
-  const int seg = blockIdx.y;
+  // the shared experts first: their blocks carry all T tokens, run longest
+  // and would otherwise form the launch's tail
+  const int y = static_cast<int>(blockIdx.y);
+  const int seg = y < a.Es ? a.E + y : y - a.Es;
   int rows, arow0, hrow0;
   if (seg < a.E) {
     arow0 = a.offsets[seg];
