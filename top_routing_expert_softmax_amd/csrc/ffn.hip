@@ -17,10 +17,11 @@
 // [out][in] weights), which is the layout bf16 MFMA operands want.
 //
 // bf16, large segments: 256 x 256 output tiles, K slices of 64 streamed
-// into a two-slot LDS ring by direct-to-LDS loads, v_mfma_f32_32x32x16_bf16
-// with fp32 accumulators; four wavefronts of 128 x 128 with the barrier in
-// the middle of each slice (gemm_mainloop_mid, and gemm_mainloop_mid_bmn
-// for the MN-contiguous backward form).  Tiles of the last,
+// into LDS by direct-to-LDS loads, v_mfma_f32_32x32x16_bf16 with fp32
+// accumulators; four wavefronts of 128 x 128 with the barrier in the middle
+// of each slice (gemm_mainloop_p5 on a ring of five operand parts, and
+// gemm_mainloop_mid_bmn on a ring of two slices for the MN-contiguous
+// backward form).  Tiles of the last,
 // partial wave of the chip are split along K and summed in a fixed order
 // (gemm_big_kernel).  bf16, decode-sized segments: 128-row tiles with
 // register prefetch (gemm_bf16_kernel).  fp32 (small configs): VALU tiles,
@@ -350,6 +351,13 @@ struct SliceGeom {
   static constexpr int STAGE = (BMT + kBN2) * ROW;      // bytes per slice
 };
 
+// LDS bytes of a ring of NST slices; NST = 5 is the ring of five operand
+// parts (half a slice each) of gemm_mainloop_p5
+template <int BKT, int BMT, int NST>
+constexpr int ring_bytes() {
+  return NST == 5 ? 5 * SliceGeom<BKT, BMT>::STAGE / 2 : NST * SliceGeom<BKT, BMT>::STAGE;
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
@@ -513,146 +521,162 @@ __device__ __forceinline__ void gemm_mainloop(
 #undef MOE_BK
 }
 
-// The loop of the four-wave tiles (one wave per SIMD, 128 x 128 outputs
-// each, K-contiguous operands through buffer resources): slices of 64 in a
-// ring of two, with the barrier in the middle of a slice.  The fragments
-// are read one half-slice (two 16-wide K steps) ahead into the other of two
-// register sets, so the MFMAs do not wait on the LDS at the barrier:
-//   phase A of slice s: the MFMAs of its first half (in registers) and the
-//     reads of its second half;
-//   boundary: slice s+1 has landed, and every wave is done reading slice
-//     s (its last reads belong to phase A);
-//   phase B: the DMA of slice s+2 into slice s's slot, the MFMAs of the
-//     second half and the reads of slice s+1's first half.
-// The MFMAs, fragment reads and DMA issues are interleaved evenly by
-// scheduling groups.
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
+// The loop of the four-wave tiles (one wave per SIMD, 128 x 128 outputs
+// each, K-contiguous operands through buffer resources), on K slices of 64
+// with one barrier in the middle of each slice.  The fragments are read
+// one half-slice (two 16-wide K steps) ahead into the other of two
+// register sets, so the MFMAs do not wait on the LDS at the barrier:
+//   phase A of slice s: the MFMAs of its first half (in registers), the
+//     reads of its second half, the DMA of A(s+2);
+//   barrier: slice s+1 has landed, and every wave is done reading slice s
+//     (its last reads belong to phase A);
+//   phase B: the MFMAs of the second half, the reads of slice s+1's first
+//     half, the DMA of B(s+2).
+// The LDS holds the operands' slice parts (256 rows of A or of B, 32 KB
+// each) in a ring of five part slots, all 160 KB: part q of the sequence
+// A0 B0 A1 B1 ... sits in slot q % 5.  A(s+2) goes to B(s-1)'s slot (free
+// since the previous barrier), B(s+2) to A(s)'s; at the barrier of slice s
+// only A(s+2)'s loads may still be in flight.  With a ring of two slices
+// (no spare slot) both parts of slice s+2 had to load in phase B, and the
+// address unit, busy with them for most of that phase, held up the MFMA
+// issue: spreading the DMA over both phases made the grouped GEMM 1-3%
+// faster.  The MFMAs, fragment reads and DMA issues are interleaved evenly
+// by scheduling groups.
 template <int BKT, int BMT, int NIA, int NIB, int MI, int NB, int MIA>
-__device__ __forceinline__ void gemm_mainloop_mid(
+__device__ __forceinline__ void gemm_mainloop_p5(
     f32x16_t (&acc)[MI][NB], char* lds_bytes, int a_dst, int b_dst,
     const int (&a_off)[MI], const int (&b_off)[NB], int lane, int nk, const BufOperands& bo,
     const uint32_t (&aoff)[NIA], const uint32_t (&boff)[NIB]) {
   using G = SliceGeom<BKT, BMT>;
-  static_assert(BKT == 64, "a slice is two halves of two 16-wide K steps");
-  constexpr int NDMA = NIA + NIB;
-  constexpr int MA = MIA > 0 ? MIA : 1;
+  static_assert(BKT == 64 && BMT == kBN2, "a slice is two halves; A and B parts of equal size");
+  constexpr int PART = BMT * G::ROW;                // bytes of one operand's slice part
+  constexpr int NSLOT = 5;
   constexpr int NMF = 2 * MIA * NB;                 // MFMAs per half-slice
   constexpr int NRD = MIA > 0 ? 2 * (MIA + NB) : 0; // fragment reads per half-slice
+  constexpr int MA = MIA > 0 ? MIA : 1;
   const int key = ((lane & 31) / G::RPL) % G::CH;
   const int khalf = lane >> 5;
   bf16x8_t ra[2][2][MA], rb[2][2][NB];              // [set][k16 step of the half][block]
+  // B rows follow the A rows within a slice in the callers' offsets
+  const int bd = b_dst - PART;
 
-#define MOE_DMA(slot, k0, d)                                                                    \
-  do {                                                                                          \
-    if ((d) < NIA)                                                                              \
-      lds_dma16_buf(bo.ra, aoff[(d) < NIA ? (d) : 0] + 2u * static_cast<uint32_t>(k0),          \
-                    lds_bytes + (slot) * G::STAGE + a_dst + ((d) < NIA ? (d) : 0) * G::RPI * G::ROW); \
-    else                                                                                        \
-      lds_dma16_buf(bo.rb, boff[(d) >= NIA ? (d) - NIA : 0] + 2u * static_cast<uint32_t>(k0),   \
-                    lds_bytes + (slot) * G::STAGE + b_dst + ((d) >= NIA ? (d) - NIA : 0) * 1024); \
-  } while (0)
-  // read r of half h: k16 step j = r / (MIA + NB), then A block q < MIA or B block
-#define MOE_RD(set, slot, h, r)                                                                 \
+#define P5_DMA_A(pslot, k0, d)                                                                  \
+  lds_dma16_buf(bo.ra, aoff[d] + 2u * static_cast<uint32_t>(k0),                                \
+                lds_bytes + (pslot) * PART + a_dst + (d) * G::RPI * G::ROW)
+#define P5_DMA_B(pslot, k0, d)                                                                  \
+  lds_dma16_buf(bo.rb, boff[d] + 2u * static_cast<uint32_t>(k0),                                \
+                lds_bytes + (pslot) * PART + bd + (d) * G::RPI * G::ROW)
+#define P5_RD(set, aslot, bslot, h, r)                                                          \
   do {                                                                                          \
     const int j_ = (r) / (MIA + NB), q_ = (r) % (MIA + NB);                                     \
     const int pc_ = ((2 * (2 * (h) + j_) + khalf) ^ key) * 16;                                  \
-    const char* sb_ = lds_bytes + (slot) * G::STAGE;                                            \
     if (q_ < MIA)                                                                               \
-      ra[set][j_][q_ < MIA ? q_ : 0] =                                                          \
-          *reinterpret_cast<const bf16x8_t*>(sb_ + a_off[q_ < MIA ? q_ : 0] + pc_);             \
+      ra[set][j_][q_ < MIA ? q_ : 0] = *reinterpret_cast<const bf16x8_t*>(                      \
+          lds_bytes + (aslot) * PART + a_off[q_ < MIA ? q_ : 0] + pc_);                         \
     else                                                                                        \
-      rb[set][j_][q_ >= MIA ? q_ - MIA : 0] =                                                   \
-          *reinterpret_cast<const bf16x8_t*>(sb_ + b_off[q_ >= MIA ? q_ - MIA : 0] + pc_);      \
+      rb[set][j_][q_ >= MIA ? q_ - MIA : 0] = *reinterpret_cast<const bf16x8_t*>(               \
+          lds_bytes + (bslot) * PART - PART + b_off[q_ >= MIA ? q_ - MIA : 0] + pc_);           \
   } while (0)
-#define MOE_MF(set, m)                                                                          \
+#define P5_MF(set, m)                                                                           \
   do {                                                                                          \
     const int j_ = (m) / (MIA * NB), t_ = (m) % (MIA * NB);                                     \
     const int mi_ = t_ / NB, ni_ = t_ % NB;                                                     \
     acc[mi_][ni_] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[set][j_][mi_], rb[set][j_][ni_], \
                                                             acc[mi_][ni_], 0, 0, 0);            \
   } while (0)
+  // one half-slice: the MFMAs of register set SET, the reads of half H of
+  // the parts in slots AS, BS into the other set, and NDM DMA issues
+#define P5_PHASE(SET, AS, BS, H, NDM, DMA)                                                      \
+  do {                                                                                          \
+    if constexpr (MIA > 0) {                                                                    \
+      _Pragma("unroll") for (int m = 0; m < NMF; ++m) {                                         \
+        P5_MF(SET, m);                                                                          \
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                      \
+        _Pragma("unroll") for (int d = 0; d < (NDM); ++d) {                                     \
+          if ((d * NMF) / (NDM) == m) {                                                         \
+            DMA(d);                                                                             \
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);                                  \
+          }                                                                                     \
+        }                                                                                       \
+        _Pragma("unroll") for (int r = 0; r < NRD; ++r) {                                       \
+          const int at = ((r + 1) * NMF) / NRD - 1;                                             \
+          if ((at < 0 ? 0 : at) == m) {                                                         \
+            P5_RD(1 - (SET), AS, BS, H, r);                                                     \
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                  \
+          }                                                                                     \
+        }                                                                                       \
+      }                                                                                         \
+    } else {                                                                                    \
+      _Pragma("unroll") for (int d = 0; d < (NDM); ++d) DMA(d);                                 \
+    }                                                                                           \
+  } while (0)
 
-  // prologue: slices 0 and 1 in flight; slice 0 landed and its first half read
+  // prologue: A0 B0 A1 B1 in slots 0 .. 3; slice 0 landed and its first
+  // half read
+  {
+    const int k1 = min(1, nk - 1) * BKT;
 #pragma unroll
-  for (int d = 0; d < NDMA; ++d) MOE_DMA(0, 0, d);
+    for (int d = 0; d < NIA; ++d) P5_DMA_A(0, 0, d);
 #pragma unroll
-  for (int d = 0; d < NDMA; ++d) MOE_DMA(1, min(1, nk - 1) * BKT, d);
-  wait_vmcnt<NDMA>();
+    for (int d = 0; d < NIB; ++d) P5_DMA_B(1, 0, d);
+#pragma unroll
+    for (int d = 0; d < NIA; ++d) P5_DMA_A(2, k1, d);
+#pragma unroll
+    for (int d = 0; d < NIB; ++d) P5_DMA_B(3, k1, d);
+  }
+  wait_vmcnt<NIA + NIB>();
   __builtin_amdgcn_sched_barrier(0);
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_sched_barrier(0);
   if constexpr (MIA > 0) {
 #pragma unroll
-    for (int r = 0; r < NRD; ++r) MOE_RD(0, 0, 0, r);
+    for (int r = 0; r < NRD; ++r) P5_RD(0, 0, 1, 0, r);
   }
+  int qa = 0;                                       // slot of A(s); B(s) in the next
   for (int s = 0; s < nk; ++s) {
-    const int slot = s & 1;
-    // phase A
-    if constexpr (MIA > 0) {
-#pragma unroll
-      for (int m = 0; m < NMF; ++m) {
-        MOE_MF(0, m);
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-#pragma unroll
-        for (int r = 0; r < NRD; ++r) {
-          const int at = ((r + 1) * NMF) / NRD - 1;
-          if ((at < 0 ? 0 : at) == m) {
-            MOE_RD(1, slot, 1, r);
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-          }
-        }
-      }
-    }
+    const int qb = qa + 1 < NSLOT ? qa + 1 : qa + 1 - NSLOT;
+    const int qna = qa + 2 < NSLOT ? qa + 2 : qa + 2 - NSLOT;
+    const int qnb = qa + 3 < NSLOT ? qa + 3 : qa + 3 - NSLOT;
+    const int qda = qa + 4 < NSLOT ? qa + 4 : qa + 4 - NSLOT;
+    const int k2 = min(s + 2, nk - 1) * BKT;
+    // phase A: A(s+2) into B(s-1)'s slot
+#define P5_DA(d) P5_DMA_A(qda, k2, d)
+    P5_PHASE(0, qa, qb, 1, NIA, P5_DA);
+#undef P5_DA
     wait_lgkm0();
-    wait_vmcnt<0>();
+    wait_vmcnt<NIA>();
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    // phase B
-    const int kn = min(s + 2, nk - 1) * BKT;
-    if constexpr (MIA > 0) {
-#pragma unroll
-      for (int m = 0; m < NMF; ++m) {
-        MOE_MF(1, m);
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-#pragma unroll
-        for (int d = 0; d < NDMA; ++d) {
-          if ((d * NMF) / NDMA == m) {
-            MOE_DMA(slot, kn, d);
-            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-          }
-        }
-#pragma unroll
-        for (int r = 0; r < NRD; ++r) {
-          const int at = ((r + 1) * NMF) / NRD - 1;
-          if ((at < 0 ? 0 : at) == m) {
-            MOE_RD(0, slot ^ 1, 0, r);
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-          }
-        }
-      }
-    } else {
-#pragma unroll
-      for (int d = 0; d < NDMA; ++d) MOE_DMA(slot, kn, d);
-    }
+    // phase B: B(s+2) into A(s)'s slot; slice s+1's first half read
+#define P5_DB(d) P5_DMA_B(qa, k2, d)
+    P5_PHASE(1, qna, qnb, 0, NIB, P5_DB);
+#undef P5_DB
+    qa = qna;
   }
   wait_vmcnt<0>();
   wait_lgkm0();
-#undef MOE_DMA
-#undef MOE_RD
-#undef MOE_MF
+#undef P5_PHASE
+#undef P5_DMA_A
+#undef P5_DMA_B
+#undef P5_RD
+#undef P5_MF
 }
 
 // The mid-slice-barrier loop for the MN-contiguous form (phase 5, dH and
-// dX on the weights as stored), four waves of 128 x 128.  Its B fragments
-// come from LDS transpose reads, before which the compiler waits for every
-// LDS-DMA load in flight; so a whole slice's B fragments are read at the
-// start of phase B, right after the barrier (when no load is in flight),
-// into the other of two slice-sized register sets, and only the A
-// fragments (ordinary reads) are read a half-slice ahead as in
-// gemm_mainloop_mid.  Operands through 64-bit addresses (asrc, bsrc; B
-// advancing k0 * b_kstride, plus b_jump from K = b_kjump on).
+// dX on the weights as stored), four waves of 128 x 128, on a ring of two
+// slices.  Its B fragments come from LDS transpose reads, before which the
+// compiler waits for every LDS-DMA load in flight; so a whole slice's B
+// fragments are read at the start of phase B, right after the barrier
+// (when no load is in flight), into the other of two slice-sized register
+// sets, and the DMA of slice s+2 (both operands) follows them in phase B.
+// (The five-part ring of gemm_mainloop_p5 would put loads in flight at
+// that point.)  Only the A fragments (ordinary reads) are read a
+// half-slice ahead as in gemm_mainloop_p5.  Operands through 64-bit
+// addresses (asrc, bsrc; B advancing k0 * b_kstride, plus b_jump from
+// K = b_kjump on).
 template <int BKT, int BMT, int NIA, int NIB, int MI, int NB, int MIA>
 __device__ __forceinline__ void gemm_mainloop_mid_bmn(
     f32x16_t (&acc)[MI][NB], const uint16_t* const (&asrc)[NIA],
@@ -843,9 +867,10 @@ void gemm_big_kernel(FfnArgs a, int NT, int ncu) {
   // dH = dO W2 and dX = [dA dB] [W1; W3] on the weights as stored)
   constexpr bool P1 = PHASE == 1 || PHASE == 3 || PHASE == 4;
   constexpr bool BMN = PHASE == 5;
-  // four waves of 128 x 128 run the mid-slice-barrier loops
-  constexpr bool kMidLoop = WAVES == 4 && !BMN && BKT == 64 && NST == 2;
+  // four waves of 128 x 128 run the mid-slice-barrier loops (NST = 5: the
+  // ring of five operand parts)
   constexpr bool kMidBmn = WAVES == 4 && BMN && BKT == 64 && NST == 2;
+  constexpr bool kPart5 = WAVES == 4 && !BMN && BKT == 64 && NST == 5;
   const int K = P1 ? a.d : a.F;
   const int nk_all = K / BKT;
   const int r = L % ncu;
@@ -1033,9 +1058,9 @@ void gemm_big_kernel(FfnArgs a, int NT, int ncu) {
       rows_w <= 0 ? 0 : (rows_w >= WR ? MI : (rows_w + 31) / 32));
 #define MOE_MAINLOOP(X)                                                                    \
   {                                                                                         \
-  if constexpr (kMidLoop) {                                                                 \
-    gemm_mainloop_mid<BKT, BMT, NIA, NIB, MI, NB, (X)>(acc, lds_bytes, a_dst, b_dst, a_off,  \
-                                                       b_off, lane, nk, bo, aoff, boff);     \
+  if constexpr (kPart5) {                                                            \
+    gemm_mainloop_p5<BKT, BMT, NIA, NIB, MI, NB, (X)>(acc, lds_bytes, a_dst, b_dst, a_off,   \
+                                                      b_off, lane, nk, bo, aoff, boff);      \
   } else if constexpr (kMidBmn) {                                                           \
     gemm_mainloop_mid_bmn<BKT, BMT, NIA, NIB, MI, NB, (X)>(acc, asrc, bsrc, lds_bytes, a_dst, \
                                                            b_dst, a_off, b_off, lane, nk,    \
@@ -1108,7 +1133,7 @@ void gemm_big_kernel(FfnArgs a, int NT, int ncu) {
   // + v%4, column l%32 of its 32 x 32 block), staged through the LDS ring,
   // idle once every wave is past its K loop.
   constexpr int NTHR = WAVES * kWave;
-  static_assert(BMT * 256 * 2 <= NST * G::STAGE, "the staged tile fits the LDS ring");
+  static_assert(BMT * 256 * 2 <= ring_bytes<BKT, BMT, NST>(), "the staged tile fits the LDS ring");
   char* stg = lds_bytes;
   if constexpr (PHASE == 1 || PHASE == 4) {
     // H = SiLU(gate) * up: 128 columns from n0 of a [rows, F] matrix
@@ -1179,10 +1204,12 @@ void gemm_big_kernel(FfnArgs a, int NT, int ncu) {
   }
 }
 
-// The configuration the library launches: K slices of 64, a ring of two
-// slices in LDS, four wavefronts of 128 x 128 with the mid-slice barrier
-// for every phase (the weight gradients too, when their offsets fit 32
-// bits; else eight wavefronts of 128 x 64).
+// The configuration the library launches: K slices of 64, four wavefronts
+// of 128 x 128 with the mid-slice barrier for every phase; the K-contiguous
+// forms (phases 1-4, and the weight gradients when their offsets fit 32
+// bits) on the ring of five operand parts, the MN-contiguous one (phase 5)
+// on a ring of two slices (kNSTsel), as is the weight gradients' fallback
+// of eight wavefronts of 128 x 64.
 constexpr int kBKsel = 64;
 constexpr int kNSTsel = 2;
 constexpr int kWavesSel = 8;       // wgrad fallback for offsets past 32 bits
@@ -1210,10 +1237,11 @@ hipError_t launch_gemm_big(const FfnArgs& a, int nt, int64_t mt, int ncu, hipStr
   // wave of split-K blocks
   const int64_t lmax = mt * nt;
   const unsigned g = static_cast<unsigned>(kXcds * ((lmax + kXcds - 1) / kXcds) + ncu);
-  constexpr size_t lds = static_cast<size_t>(kNSTsel) * SliceGeom<kBKsel, kBM2>::STAGE;
+  constexpr int kBK = kBKsel, kNST = PHASE == 5 ? kNSTsel : 5;
+  constexpr size_t lds = static_cast<size_t>(ring_bytes<kBK, kBM2, kNST>());
   static_assert(lds <= 160 * 1024, "LDS ring exceeds the 160 KB of a CU");
   constexpr int kWaves = kBigWaves;
-  constexpr auto kern = &gemm_big_kernel<PHASE, kBKsel, kNSTsel, kWaves, kBM2, kWM>;
+  constexpr auto kern = &gemm_big_kernel<PHASE, kBK, kNST, kWaves, kBM2, kWM>;
   const hipError_t attr = allow_dynamic_lds<kern>(static_cast<int>(lds));
   if (attr != hipSuccess) return attr;
   hipLaunchKernelGGL(kern, dim3(g), dim3(kWaves * kWave), lds, s, a, nt, ncu);
@@ -1338,9 +1366,9 @@ struct WgradArgs {
   int M, N, E, NT;
 };
 
-// WAVES = 4 runs the mid-slice-barrier loop through buffer resources (the
-// tile's rows then lie within 2^31 bytes: ld < 2^22); WAVES = 8 the
-// barrier-per-slice loop on 64-bit addresses.
+// WAVES = 4 (NST = 5) runs gemm_mainloop_p5 through buffer resources (the
+// tile's rows then lie within 2^31 bytes: ld < 2^22); WAVES = 8 (NST = 2)
+// the barrier-per-slice loop on 64-bit addresses.
 template <int BKT, int NST, int WAVES>
 __global__ __launch_bounds__(WAVES * kWave) __attribute__((amdgpu_waves_per_eu(WAVES / 4, WAVES / 4)))
 void gemm_wgrad_kernel(WgradArgs a) {
@@ -1404,7 +1432,7 @@ void gemm_wgrad_kernel(WgradArgs a) {
   for (int ni = 0; ni < NB; ++ni)
     b_off[ni] = BMT * G::ROW + (wn * (kBN2 / WN) + ni * 32 + (lane & 31)) * G::ROW;
   if constexpr (kMid) {
-    static_assert(BKT == 64 && NST == 2, "the mid-slice loop's ring");
+    static_assert(BKT == 64 && NST == 5, "the five-part ring");
     BufOperands bo;
     bo.ra = buffer_rsrc(a.A + static_cast<int64_t>(m0) * a.ld + k0);
     bo.rb = buffer_rsrc(a.B + static_cast<int64_t>(n0) * a.ld + k0);
@@ -1416,7 +1444,7 @@ void gemm_wgrad_kernel(WgradArgs a) {
     for (int i = 0; i < NIB; ++i)
       boff[i] = static_cast<uint32_t>((bsrc[i] - (a.B + static_cast<int64_t>(n0) * a.ld + k0)) * 2);
     if (nk > 0)
-      gemm_mainloop_mid<BKT, BMT, NIA, NIB, MI, NB, MI>(acc, lds_bytes, a_dst, b_dst, a_off, b_off,
+      gemm_mainloop_p5<BKT, BMT, NIA, NIB, MI, NB, MI>(acc, lds_bytes, a_dst, b_dst, a_off, b_off,
                                                          lane, nk, bo, aoff, boff);
   } else {
     if (nk > 0)
@@ -1450,10 +1478,11 @@ hipError_t launch_wgrad(const WgradArgs& a0, int nseg, hipStream_t s) {
   const dim3 grid(static_cast<unsigned>(MT * a.NT), static_cast<unsigned>(nseg));
   if (a.ld < (int64_t(1) << 22)) {
     // a tile's 256 rows of ld bf16 fit the 32-bit offsets of a buffer load
-    constexpr auto kern = &gemm_wgrad_kernel<kBKsel, kNSTsel, kBigWaves>;
-    const hipError_t attr = allow_dynamic_lds<kern>(static_cast<int>(lds));
+    constexpr auto kern = &gemm_wgrad_kernel<kBKsel, 5, kBigWaves>;
+    constexpr size_t lds5 = ring_bytes<kBKsel, 256, 5>();
+    const hipError_t attr = allow_dynamic_lds<kern>(static_cast<int>(lds5));
     if (attr != hipSuccess) return attr;
-    hipLaunchKernelGGL(kern, grid, dim3(kBigWaves * kWave), lds, s, a);
+    hipLaunchKernelGGL(kern, grid, dim3(kBigWaves * kWave), lds5, s, a);
   } else {
     constexpr auto kern = &gemm_wgrad_kernel<kBKsel, kNSTsel, kWavesSel>;
     const hipError_t attr = allow_dynamic_lds<kern>(static_cast<int>(lds));
