@@ -30,6 +30,9 @@
 // same 16 indices of the token rows.  The row scale multiplies the summed
 // dot product (s * sum_k x_k q_k = sum_k x_k (s q_k)).  Half the bytes of
 // the bf16 weights cross HBM.
+#include <algorithm>
+#include <atomic>
+
 #include "moe_device.h"
 #include "moe_internal.h"
 
@@ -62,6 +65,7 @@ struct StreamArgs {
   const float* ssc3;
   const float* ssc2;
   int T, d, E, Es, k, F;
+  int xs_rows;            // segments of at most this many rows stage them in LDS
 };
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -76,6 +80,31 @@ __device__ __forceinline__ bf16x8_t e4m3x8_to_bf16(uint32_t w0, uint32_t w1) {
 }
 
 __device__ __forceinline__ float silu_s(float g) { return g / (1.0f + __expf(-g)); }
+
+// The segment's token rows (rows x K bf16) copied into the LDS, row r at
+// element r * (K + 8): the 16-byte pad puts the rows of a fragment read on
+// different banks.  A decode segment holds a few tokens, so every lane of
+// an A-operand load addresses one of a few rows; from L2 those loads cost
+// about as many requests as the weight stream, and from LDS none.  Direct-
+// to-LDS loads of 16 bytes, 64 pieces per wave instruction (the pad pieces
+// load the first piece again); every wave waits for its loads, then the
+// block meets at a barrier.
+__device__ __forceinline__ void stage_rows(const uint16_t* A, int rows, int K, uint16_t* xs) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int per_row = (K + 8) / 8;                 // 16-byte pieces per LDS row
+  const int total = rows * per_row;
+  for (int j = wave; j * kWave < total; j += kSWaves) {
+    const int p = j * kWave + lane;
+    const int r = p / per_row, c = p - r * per_row;
+    const uint16_t* src = c < K / 8 ? A + static_cast<int64_t>(r) * K + c * 8 : A;
+    if (p < total)
+      __builtin_amdgcn_global_load_lds(src, reinterpret_cast<uint32_t*>(xs + j * kWave * 8), 16,
+                                       0, 0);
+  }
+  __builtin_amdgcn_s_waitcnt(0xF70);               // vmcnt(0)
+  __syncthreads();
+}
 
 // Sum the four quarters of a block in wave order, one token group at a
 // time (wave tg % 4 finishes group tg), scale (FP8) and store.
@@ -142,9 +171,9 @@ __device__ __forceinline__ void stream_finish(const StreamArgs& a, f32x4_t (&acc
 }
 
 // One block, TG groups of 16 tokens.  U = K steps loaded per batch.
-template <int PHASE, int TG>
+template <int PHASE, int TG, bool XS>
 __device__ __forceinline__ void stream_block(const StreamArgs& a, int seg, int rows, int arow0,
-                                             int hrow0, float* red) {
+                                             int hrow0, float* red, uint16_t* xs) {
   constexpr int U = TG == 1 ? kSU : (TG == 2 ? (kSU + 1) / 2 : 1);
   const bool routed = seg < a.E;
   const int e = routed ? seg : seg - a.E;
@@ -173,10 +202,15 @@ __device__ __forceinline__ void stream_block(const StreamArgs& a, int seg, int r
   const uint16_t* Abase = PHASE == 1
       ? static_cast<const uint16_t*>(routed ? a.x_perm : a.x) + static_cast<int64_t>(arow0) * K
       : static_cast<const uint16_t*>(a.H) + static_cast<int64_t>(hrow0) * K;
+  if constexpr (XS) {
+    stage_rows(Abase, rows, K, xs);
+    arow[0] = xs + min(lane & 15, rows - 1) * (K + 8);
+  } else {
 #pragma unroll
-  for (int tg = 0; tg < TG; ++tg) {
-    const int m = min(tg * 16 + (lane & 15), rows - 1);
-    arow[tg] = Abase + static_cast<int64_t>(m) * K;
+    for (int tg = 0; tg < TG; ++tg) {
+      const int m = min(tg * 16 + (lane & 15), rows - 1);
+      arow[tg] = Abase + static_cast<int64_t>(m) * K;
+    }
   }
   const int kq = 8 * (lane >> 4);
 
@@ -243,9 +277,10 @@ __device__ __forceinline__ void stream_block(const StreamArgs& a, int seg, int r
 }
 
 // FP8 weights: as stream_block, on 64-wide K steps of E4M3 codes.
-template <int PHASE, int TG>
+template <int PHASE, int TG, bool XS>
 __device__ __forceinline__ void stream_block_fp8(const StreamArgs& a, int seg, int rows,
-                                                 int arow0, int hrow0, float* red) {
+                                                 int arow0, int hrow0, float* red,
+                                                 uint16_t* xs) {
   constexpr int NB = kSNB8;
   constexpr int U = TG == 1 ? kSU8 : 1;              // 64-wide K steps per batch
   const bool routed = seg < a.E;
@@ -275,10 +310,15 @@ __device__ __forceinline__ void stream_block_fp8(const StreamArgs& a, int seg, i
   const uint16_t* Abase = PHASE == 1
       ? static_cast<const uint16_t*>(routed ? a.x_perm : a.x) + static_cast<int64_t>(arow0) * K
       : static_cast<const uint16_t*>(a.H) + static_cast<int64_t>(hrow0) * K;
+  if constexpr (XS) {
+    stage_rows(Abase, rows, K, xs);
+    arow[0] = xs + min(lane & 15, rows - 1) * (K + 8);
+  } else {
 #pragma unroll
-  for (int tg = 0; tg < TG; ++tg) {
-    const int m = min(tg * 16 + (lane & 15), rows - 1);
-    arow[tg] = Abase + static_cast<int64_t>(m) * K;
+    for (int tg = 0; tg < TG; ++tg) {
+      const int m = min(tg * 16 + (lane & 15), rows - 1);
+      arow[tg] = Abase + static_cast<int64_t>(m) * K;
+    }
   }
   const int kq = 16 * (lane >> 4);       // the lane's 16 indices of a 64-wide step
 
@@ -377,7 +417,8 @@ __device__ __forceinline__ void stream_block_fp8(const StreamArgs& a, int seg, i
 // Segments with no rows, or more than kStreamMaxRows rows, exit at once.
 template <int PHASE, bool FP8>
 __global__ __launch_bounds__(kSWaves * kWave) void ffn_stream_kernel(StreamArgs a) {
-  __shared__ f32x4_t red[kSWaves * (kSNB8 > kSNB ? kSNB8 : kSNB) * kWave];
+  __shared__ f32x4_t red[kSWaves * (FP8 ? kSNB8 : kSNB) * kWave];
+  extern __shared__ __attribute__((aligned(16))) uint16_t xs[];   // a.xs_rows x (K + 8)
   // the shared experts first: their blocks carry all T tokens, run longest
   // and would otherwise form the launch's tail
   const int y = static_cast<int>(blockIdx.y);
@@ -395,20 +436,46 @@ __global__ __launch_bounds__(kSWaves * kWave) void ffn_stream_kernel(StreamArgs 
   if (rows <= 0 || rows > kStreamMaxRows) return;
   float* r = reinterpret_cast<float*>(red);
   if constexpr (FP8) {
+    if (rows <= a.xs_rows) {
+      stream_block_fp8<PHASE, 1, true>(a, seg, rows, arow0, hrow0, r, xs);
+      return;
+    }
     switch ((rows + 15) / 16) {
-      case 1: stream_block_fp8<PHASE, 1>(a, seg, rows, arow0, hrow0, r); break;
-      case 2: stream_block_fp8<PHASE, 2>(a, seg, rows, arow0, hrow0, r); break;
-      case 3: stream_block_fp8<PHASE, 3>(a, seg, rows, arow0, hrow0, r); break;
-      default: stream_block_fp8<PHASE, 4>(a, seg, rows, arow0, hrow0, r); break;
+      case 1: stream_block_fp8<PHASE, 1, false>(a, seg, rows, arow0, hrow0, r, xs); break;
+      case 2: stream_block_fp8<PHASE, 2, false>(a, seg, rows, arow0, hrow0, r, xs); break;
+      case 3: stream_block_fp8<PHASE, 3, false>(a, seg, rows, arow0, hrow0, r, xs); break;
+      default: stream_block_fp8<PHASE, 4, false>(a, seg, rows, arow0, hrow0, r, xs); break;
     }
   } else {
+    if (rows <= a.xs_rows) {
+      stream_block<PHASE, 1, true>(a, seg, rows, arow0, hrow0, r, xs);
+      return;
+    }
     switch ((rows + 15) / 16) {
-      case 1: stream_block<PHASE, 1>(a, seg, rows, arow0, hrow0, r); break;
-      case 2: stream_block<PHASE, 2>(a, seg, rows, arow0, hrow0, r); break;
-      case 3: stream_block<PHASE, 3>(a, seg, rows, arow0, hrow0, r); break;
-      default: stream_block<PHASE, 4>(a, seg, rows, arow0, hrow0, r); break;
+      case 1: stream_block<PHASE, 1, false>(a, seg, rows, arow0, hrow0, r, xs); break;
+      case 2: stream_block<PHASE, 2, false>(a, seg, rows, arow0, hrow0, r, xs); break;
+      case 3: stream_block<PHASE, 3, false>(a, seg, rows, arow0, hrow0, r, xs); break;
+      default: stream_block<PHASE, 4, false>(a, seg, rows, arow0, hrow0, r, xs); break;
     }
   }
+}
+
+// Dynamic LDS above the default limit is a per-device setting of a
+// kernel: raise it once for each (kernel, device); sizes within the
+// default need nothing.
+template <auto Kern>
+hipError_t allow_stream_lds(size_t bytes) {
+  if (bytes <= 48 * 1024) return hipSuccess;
+  static std::atomic<uint64_t> done{0};        // one bit per device id < 64
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  const uint64_t bit = dev < 64 ? (uint64_t{1} << dev) : 0;
+  if (bit != 0 && (done.load(std::memory_order_acquire) & bit) != 0) return hipSuccess;
+  err = hipFuncSetAttribute(reinterpret_cast<const void*>(Kern),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, 60 * 1024);
+  if (err == hipSuccess && bit != 0) done.fetch_or(bit, std::memory_order_acq_rel);
+  return err;
 }
 
 }  // namespace
@@ -422,22 +489,42 @@ hipError_t launch_ffn_stream(int phase, int64_t T, int64_t d, int E, int E_share
                              const float* ssc3, const float* ssc2) {
   StreamArgs a{x_perm, x, offsets, w1, w3, w2, ws1, ws3, ws2, H, y_perm, y_shared,
                sc1, sc3, sc2, ssc1, ssc3, ssc2,
-               static_cast<int>(T), static_cast<int>(d), E, E_shared, k, static_cast<int>(F)};
+               static_cast<int>(T), static_cast<int>(d), E, E_shared, k, static_cast<int>(F),
+               0};
   const bool fp8 = sc1 != nullptr;
   const unsigned nseg = static_cast<unsigned>(E + E_shared);
   const dim3 block(kSWaves * kWave);
   // H columns per block: 8 * fragments (half gate, half up); output
   // columns per block: 16 * fragments
   const int nb = fp8 ? kSNB8 : kSNB;
+  // Token rows staged in LDS for segments of up to 4 (FP8) or 3 (bf16)
+  // rows, within 60 KB or 45 KB: two FP8 blocks (216 registers a lane) or
+  // three bf16 blocks (144) still fit a compute unit's 160 KB.
+  const int64_t K = phase == 1 ? d : F;
+  const int64_t row_bytes = (K + 8) * 2;
+  a.xs_rows = static_cast<int>(std::min<int64_t>(fp8 ? 4 : 3, (fp8 ? 60 : 45) * 1024 / row_bytes));
+  const size_t lds = static_cast<size_t>(a.xs_rows * row_bytes);
+  hipError_t err = hipSuccess;
   if (phase == 1) {
     const dim3 grid(static_cast<unsigned>(F / (8 * nb)), nseg);
-    if (fp8) hipLaunchKernelGGL((ffn_stream_kernel<1, true>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((ffn_stream_kernel<1, false>), grid, block, 0, s, a);
+    if (fp8) {
+      err = allow_stream_lds<ffn_stream_kernel<1, true>>(lds);
+      if (err == hipSuccess) hipLaunchKernelGGL((ffn_stream_kernel<1, true>), grid, block, lds, s, a);
+    } else {
+      err = allow_stream_lds<ffn_stream_kernel<1, false>>(lds);
+      if (err == hipSuccess) hipLaunchKernelGGL((ffn_stream_kernel<1, false>), grid, block, lds, s, a);
+    }
   } else {
     const dim3 grid(static_cast<unsigned>(d / (16 * nb)), nseg);
-    if (fp8) hipLaunchKernelGGL((ffn_stream_kernel<2, true>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((ffn_stream_kernel<2, false>), grid, block, 0, s, a);
+    if (fp8) {
+      err = allow_stream_lds<ffn_stream_kernel<2, true>>(lds);
+      if (err == hipSuccess) hipLaunchKernelGGL((ffn_stream_kernel<2, true>), grid, block, lds, s, a);
+    } else {
+      err = allow_stream_lds<ffn_stream_kernel<2, false>>(lds);
+      if (err == hipSuccess) hipLaunchKernelGGL((ffn_stream_kernel<2, false>), grid, block, lds, s, a);
+    }
   }
+  if (err != hipSuccess) return err;
   return hipGetLastError();
 }
 
