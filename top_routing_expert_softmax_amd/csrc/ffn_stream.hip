@@ -10,10 +10,13 @@
 //
 // Work split.  A block of 4 wavefronts owns one group of weight rows of one
 // segment: phase 1 takes 16 rows of W1 and the same 16 rows of W3 (16
-// columns of H), phase 2 takes 32 rows of W2 (32 output columns).  Its
-// waves stream the four quarters of the contracted dimension; the four
-// partial sums meet in LDS and are added in wave order (deterministic),
-// then phase 1 applies SiLU(gate) * up and rounds H to bf16.
+// columns of H), phase 2 takes 32 rows of W2 (32 output columns) (FP8:
+// twice as many).  Its waves take the contracted dimension's batches of K
+// steps round robin, so at any moment they read adjacent pieces of every
+// weight row; the four partial sums meet in LDS and are added in wave
+// order (deterministic), then phase 1 applies SiLU(gate) * up and rounds H
+// to bf16.  Segments of a few rows first copy their token rows into the
+// LDS (stage_rows).
 //
 // Fragments (16 x 16 x 32 MFMA, lane l): the A operand holds token
 // l % 16 of a 16-token group and the B operand weight row l % 16 of a
@@ -220,11 +223,13 @@ __device__ __forceinline__ void stream_block(const StreamArgs& a, int seg, int r
 #pragma unroll
     for (int b = 0; b < kSNB; ++b) acc[tg][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  // this wave's quarter of the 32-wide K steps
+  // The 32-wide K steps go to the waves in batches of U, round robin (as in
+  // stream_block_fp8); the steps past the whole batches go to wave
+  // (whole batches) % 4.
   const int nsteps = K / 32;
-  const int s0 = wave * nsteps / kSWaves;
-  const int s1 = (wave + 1) * nsteps / kSWaves;
-  int s = s0;
+  const int nbt = nsteps / U;
+  const int nbw = nbt > wave ? (nbt - wave + kSWaves - 1) / kSWaves : 0;
+  constexpr int SST = kSWaves * U;
 #define MOE_SLOAD(FA, FB, S0)                                                              \
   _Pragma("unroll") for (int u = 0; u < U; ++u) {                                         \
     const int kk = ((S0) + u) * 32 + kq;                                                  \
@@ -238,27 +243,29 @@ __device__ __forceinline__ void stream_block(const StreamArgs& a, int seg, int r
     _Pragma("unroll") for (int tg = 0; tg < TG; ++tg)                                     \
       _Pragma("unroll") for (int b = 0; b < kSNB; ++b)                                    \
         acc[tg][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(FA[u][tg], FB[u][b], acc[tg][b], 0, 0, 0);
-  if (s + 2 * U <= s1) {
-    // two batches in flight: load batch i+1, then use batch i
+  int j = 0;
+  if (nbw >= 2) {
     bf16x8_t fa0[U][TG], fb0[U][kSNB], fa1[U][TG], fb1[U][kSNB];
-    MOE_SLOAD(fa0, fb0, s);
-    s += U;
-    for (; s + 2 * U <= s1; s += 2 * U) {
-      MOE_SLOAD(fa1, fb1, s);
+    MOE_SLOAD(fa0, fb0, wave * U);
+    j = 1;
+    for (; j + 2 <= nbw; j += 2) {
+      MOE_SLOAD(fa1, fb1, (wave + kSWaves * j) * U);
       MOE_SMFMA(fa0, fb0);
-      MOE_SLOAD(fa0, fb0, s + U);
+      MOE_SLOAD(fa0, fb0, (wave + kSWaves * j) * U + SST);
       MOE_SMFMA(fa1, fb1);
     }
     MOE_SMFMA(fa0, fb0);
   }
-  for (; s + U <= s1; s += U) {
+  for (; j < nbw; ++j) {
     bf16x8_t fa[U][TG], fb[U][kSNB];
-    MOE_SLOAD(fa, fb, s);
+    MOE_SLOAD(fa, fb, (wave + kSWaves * j) * U);
     MOE_SMFMA(fa, fb);
   }
 #undef MOE_SLOAD
 #undef MOE_SMFMA
-  for (; s < s1; ++s) {
+  const bool tailw = wave == nbt % kSWaves;
+  const int s1 = tailw ? nsteps : 0;
+  for (int s = nbt * U; s < s1; ++s) {
     const int kk = s * 32 + kq;
     bf16x8_t fb[kSNB], fa[TG];
 #pragma unroll
