@@ -111,3 +111,59 @@ def test_fp8_decode_layer_full_size():
     y on two tokens, codes checked on their experts and the shared one."""
     cfg = get_config("dsv3_decode")
     _fp8_layer(cfg, tokens=[0, 37])
+
+
+@pytest.mark.parametrize("counts,T,k", [
+    # 1 .. 4 rows read the token rows from LDS (FP8 limit 4), 5 from L2,
+    # 16 and 17 rows one and two token groups, 64 the largest streamed
+    ([0, 1, 2, 3, 4, 5, 16, 17, 64, 0, 7], 64, 4),
+    # T = 4: the shared expert's all-token segment is staged too
+    ([0, 1, 4, 2, 3], 4, 3),
+])
+def test_fp8_stream_segments_at_the_staging_limits(counts, T, k):
+    """moe_expert_ffn_fp8 on chosen decode-sized segments around the LDS
+    staging of token rows, d = 320 and F = 192 (rows of 640 and 384 bytes;
+    K loops of 5 and 3 steps of 64: whole batches and a remainder), against
+    the oracle computing with the dequantised weights."""
+    import top_routing_expert_softmax_amd as M
+    d_model, d_ff = 320, 192
+    cfg = get_config("dsv3_decode", T=T, d_model=d_model, E=len(counts), E_shared=1, k=k,
+                     d_ff=d_ff, CF=None)
+    H.log(f"fp8 staging limits: counts={counts} T={T} k={k}")
+    inp = H.LayerInputs(cfg)
+    dd = inp.dev
+    q = {kind: _quantize_dev(dd[kind]) for kind in dd}
+    R = sum(counts)
+    src = np.arange(R) % T
+    xp = torch.zeros((T * k, d_model), dtype=torch.bfloat16, device="cuda")
+    xp[:R] = inp.x_dev[torch.from_numpy(src).cuda()]
+    offs = torch.tensor(np.concatenate([[0], np.cumsum(counts)]), dtype=torch.int32,
+                        device="cuda")
+    E = len(counts)
+    ws = torch.empty(M.moe_workspace_size(T, d_model, E, 1, k, d_ff, torch.bfloat16),
+                     dtype=torch.uint8, device="cuda")
+    yp = torch.empty((T * k, d_model), dtype=torch.bfloat16, device="cuda")
+    ysh = torch.empty((1, T, d_model), dtype=torch.bfloat16, device="cuda")
+    M.moe_expert_ffn_fp8(T, k, xp, offs, inp.x_dev, q["w1"][0], q["w3"][0], q["w2"][0],
+                         q["w1"][1], q["w3"][1], q["w2"][1], yp, ws, sq1=q["ws1"][0],
+                         sq3=q["ws3"][0], sq2=q["ws2"][0], ss1=q["ws1"][1], ss3=q["ws3"][1],
+                         ss2=q["ws2"][1], y_shared=ysh)
+    torch.cuda.synchronize()
+
+    def deq(name, e):
+        c, s = O.quantize_fp8_rows(inp.host_expert(name, e))
+        return O.dequantize_fp8_rows(c, s)
+
+    x64 = inp.x.astype(np.float64)
+    o = np.concatenate([[0], np.cumsum(counts)])
+    got, ref = [], []
+    for e in range(E):
+        if counts[e] == 0:
+            continue
+        got.append(yp[o[e]:o[e + 1]].float().cpu().numpy())
+        ref.append(O.swiglu_expert(x64[src[o[e]:o[e + 1]]], deq("w1", e), deq("w3", e),
+                                   deq("w2", e)))
+    got.append(ysh[0].float().cpu().numpy())
+    ref.append(O.swiglu_expert(x64, deq("ws1", 0), deq("ws3", 0), deq("ws2", 0)))
+    mx, mr = H.check_y(cfg, np.concatenate(got), np.concatenate(ref))
+    H.log(f"  y: max_err={mx:.2e} mean_rel={mr:.2e}")

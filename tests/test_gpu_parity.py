@@ -230,3 +230,61 @@ def test_expert_ffn_segments_with_short_remainders(d_model, d_ff):
     H.log(f"  y: max_err={mx:.2e} mean_rel={mr:.2e}")
     mx, mr = H.check_y(cfg, np.concatenate(got_ab), np.concatenate(ref_ab))
     H.log(f"  A, B: max_err={mx:.2e} mean_rel={mr:.2e}")
+
+
+def _stream_segments(counts, T, k, d_model, d_ff, E_shared):
+    """Explicit segment offsets for the weight-streaming kernels: x_perm row r
+    copies token r mod T; every segment of at most 64 rows streams."""
+    cfg = get_config("dsv3_decode", T=T, d_model=d_model, E=len(counts), E_shared=E_shared,
+                     k=k, d_ff=d_ff, CF=None)
+    inp = H.LayerInputs(cfg)
+    R = sum(counts)
+    src = np.arange(R) % T
+    xp = torch.zeros((T * k, d_model), dtype=torch.bfloat16, device="cuda")
+    xp[:R] = inp.x_dev[torch.from_numpy(src).cuda()]
+    offs = torch.tensor(np.concatenate([[0], np.cumsum(counts)]), dtype=torch.int32,
+                        device="cuda")
+    return cfg, inp, src, xp, offs
+
+
+@pytest.mark.parametrize("counts,T,k,E_shared", [
+    # 1 .. 3 rows read the token rows from LDS (bf16 limit 3), 4 and 5 from
+    # L2, 16 and 17 rows one and two token groups, 64 the largest streamed
+    ([0, 1, 2, 3, 4, 5, 16, 17, 64, 0, 7], 64, 4, 1),
+    # T = 3: the shared expert's all-token segment is staged too
+    ([0, 1, 2, 3, 3], 3, 3, 1),
+])
+def test_stream_segments_at_the_staging_limits(counts, T, k, E_shared):
+    """moe_expert_ffn on decode-sized segments with chosen row counts around
+    the streaming kernels' LDS staging of token rows, with d = 320 and
+    F = 192: rows of 640 and 384 bytes (no whole 1 KB pieces), K loops of 10
+    and 6 steps of 32 (whole batches and a remainder).  Every row against
+    the oracle's SwiGLU expert."""
+    import top_routing_expert_softmax_amd as M
+    from oracle import moe_oracle as O
+    d_model, d_ff = 320, 192
+    cfg, inp, src, xp, offs = _stream_segments(counts, T, k, d_model, d_ff, E_shared)
+    H.log(f"stream staging limits: counts={counts} T={T} k={k}")
+    dd = inp.dev
+    E, F = len(counts), d_ff
+    ws = torch.empty(M.moe_workspace_size(T, d_model, E, E_shared, k, F, torch.bfloat16),
+                     dtype=torch.uint8, device="cuda")
+    yp = torch.empty((T * k, d_model), dtype=torch.bfloat16, device="cuda")
+    ysh = torch.empty((E_shared, T, d_model), dtype=torch.bfloat16, device="cuda")
+    M.moe_expert_ffn(T, k, xp, offs, inp.x_dev, dd["w1"], dd["w3"], dd["w2"], dd["ws1"],
+                     dd["ws3"], dd["ws2"], yp, ysh, ws)
+    torch.cuda.synchronize()
+    x64 = inp.x.astype(np.float64)
+    o = np.concatenate([[0], np.cumsum(counts)])
+    got, ref = [], []
+    for e in range(E):
+        if counts[e] == 0:
+            continue
+        w1, w3, w2 = inp.load_routed(e)
+        got.append(yp[o[e]:o[e + 1]].float().cpu().numpy())
+        ref.append(O.swiglu_expert(x64[src[o[e]:o[e + 1]]], w1, w3, w2))
+    s1, s3, s2 = (a.astype(np.float64) for a in inp.load_shared(0))
+    got.append(ysh[0].float().cpu().numpy())
+    ref.append(O.swiglu_expert(x64, s1, s3, s2))
+    mx, mr = H.check_y(cfg, np.concatenate(got), np.concatenate(ref))
+    H.log(f"  y: max_err={mx:.2e} mean_rel={mr:.2e}")
