@@ -24,7 +24,8 @@
  *     allocates, frees or keeps a pointer after the call returns.
  *   - State the library keeps: the last error message, per calling thread
  *     (thread-local); a per-device record of the large-LDS launch attribute
- *     it has set on its GEMM kernels (set once, under an atomic); and the
+ *     it has set on its GEMM and weight-streaming kernels (set once, under
+ *     an atomic); and the
  *     per-device address of the scratch array of moe_expert_ffn_noalloc.
  *     Device state lives only in the caller's workspace (and in that
  *     scratch array): moe_expert_ffn keeps split-K arrival counters and
