@@ -10,8 +10,8 @@
 //
 // Work split.  A block of 4 wavefronts owns one group of weight rows of one
 // segment: phase 1 takes 16 rows of W1 and the same 16 rows of W3 (16
-// columns of H), phase 2 takes 32 rows of W2 (32 output columns) (FP8:
-// twice as many).  Its waves take the contracted dimension's batches of K
+// columns of H), phase 2 takes 32 rows of W2 (32 output columns; FP8: 64).
+// Its waves take the contracted dimension's batches of K
 // steps round robin, so at any moment they read adjacent pieces of every
 // weight row, starting at a per-block rotation of the batch order so that
 // concurrent blocks read different parts of their rows; the four partial
@@ -46,9 +46,11 @@ namespace {
 
 constexpr int kSWaves = 4;               // waves per block (K quarters)
 constexpr int kSNB = 2;                  // 16-row weight fragments per K step (bf16)
-constexpr int kSNB8 = 4;                 // fragments per K step (FP8): half gate, half up
+constexpr int kSNB8 = 4;                 // fragments per K step (FP8, phase 2)
+constexpr int kSNB8P1 = 2;               // fragments per K step (FP8, phase 1): gate, up
 constexpr int kSU = 4;                   // 32-wide K steps per load batch (bf16, 16 tokens)
-constexpr int kSU8 = 2;                  // 64-wide K steps per load batch (FP8, 16 tokens)
+constexpr int kSU8 = 2;                  // 64-wide K steps per load batch (FP8 phase 2, 16 tokens)
+constexpr int kSU8P1 = 4;                // the same, FP8 phase 1
 
 struct StreamArgs {
   const void* x_perm;
@@ -310,8 +312,15 @@ template <int PHASE, int TG, bool XS>
 __device__ __forceinline__ void stream_block_fp8(const StreamArgs& a, int seg, int rows,
                                                  int arow0, int hrow0, float* red,
                                                  uint16_t* xs) {
-  constexpr int NB = kSNB8;
-  constexpr int U = TG == 1 ? kSU8 : 1;              // 64-wide K steps per batch
+  // Phase 1 (rows of d codes): a wave's batch covers 256 bytes of each of
+  // 32 weight rows (two fragments, four 64-wide steps), the shape of the
+  // bf16 kernel's batches.  Four fragments of two steps (128 bytes of each
+  // of 64 rows, the same registers) measured 1.707 ms against 1.622 ms on
+  // the DeepSeek-V3 decode step: longer pieces of fewer rows at a time
+  // stream faster.  Phase 2 (rows of F = 2048 codes) keeps four fragments
+  // of two steps, which leaves each wave four batches to pipeline.
+  constexpr int NB = PHASE == 1 ? kSNB8P1 : kSNB8;
+  constexpr int U = TG == 1 ? (PHASE == 1 ? kSU8P1 : kSU8) : 1;   // 64-wide K steps per batch
   const bool routed = seg < a.E;
   const int e = routed ? seg : seg - a.E;
   const int lane = threadIdx.x & (kWave - 1);
@@ -447,6 +456,7 @@ __device__ __forceinline__ void stream_block_fp8(const StreamArgs& a, int seg, i
 // Segments with no rows, or more than kStreamMaxRows rows, exit at once.
 template <int PHASE, bool FP8>
 __global__ __launch_bounds__(kSWaves * kWave) void ffn_stream_kernel(StreamArgs a) {
+  static_assert(kSNB8 >= kSNB8P1, "the reduction buffer holds the larger FP8 block");
   __shared__ f32x4_t red[kSWaves * (FP8 ? kSNB8 : kSNB) * kWave];
   extern __shared__ __attribute__((aligned(16))) uint16_t xs[];   // a.xs_rows x (K + 8)
   // the shared experts first: their blocks carry all T tokens, run longest
@@ -526,7 +536,7 @@ hipError_t launch_ffn_stream(int phase, int64_t T, int64_t d, int E, int E_share
   const dim3 block(kSWaves * kWave);
   // H columns per block: 8 * fragments (half gate, half up); output
   // columns per block: 16 * fragments
-  const int nb = fp8 ? kSNB8 : kSNB;
+  const int nb = fp8 ? (phase == 1 ? kSNB8P1 : kSNB8) : kSNB;
   // Token rows staged in LDS for segments of up to 4 (FP8) or 3 (bf16)
   // rows, within 60 KB or 45 KB: two FP8 blocks (216 registers a lane) or
   // three bf16 blocks (144) still fit a compute unit's 160 KB.
