@@ -86,7 +86,10 @@ __device__ __forceinline__ bf16x8_t e4m3x8_to_bf16(uint32_t w0, uint32_t w1) {
   return bf16x8_t{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
-__device__ __forceinline__ float silu_s(float g) { return g / (1.0f + __expf(-g)); }
+// SiLU with the hardware reciprocal, as in the grouped GEMM's epilogue.
+__device__ __forceinline__ float silu_s(float g) {
+  return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g));
+}
 
 // Each block walks its K batches from a rotated start: batch b of the
 // round-robin order reads physical batch (b + rot) mod nbt, rot a hash of
