@@ -816,11 +816,13 @@ __device__ __forceinline__ void gemm_mainloop_mid_bmn(
 // different banks; then consecutive threads copy consecutive chunks of a
 // row to memory, so every store instruction writes whole 16-byte pieces of
 // full rows instead of 2 bytes per lane.
-template <int COLS>
+// HW: round with the hardware conversion (the inference phases 1 and 2,
+// 0.5-1% faster there), else with integer arithmetic (same bits).
+template <int COLS, bool HW>
 __device__ __forceinline__ void stage_put(char* lds, int row, int col, float v) {
   constexpr int NCH = COLS / 8;
   const int off = row * (COLS * 2) + (((col >> 3) ^ (row & (NCH - 1))) << 4) + ((col & 7) << 1);
-  *reinterpret_cast<uint16_t*>(lds + off) = f32_to_bf16(v);
+  *reinterpret_cast<uint16_t*>(lds + off) = HW ? f32_to_bf16_hw(v) : f32_to_bf16(v);
 }
 
 // dst(row, chunk) gives the destination of 16-byte chunk `chunk` of tile row
@@ -1154,7 +1156,7 @@ void gemm_big_kernel(FfnArgs a, int NT, int ncu) {
         for (int v = 0; v < 16; ++v) {
           const int row = wm * WR + mi * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
           const int col = wn * (128 / WN) + ni * 32 + (lane & 31);
-          stage_put<128>(stg, row, col, silu_f(acc[mi][ni][v]) * acc[mi][ni + NB / 2][v]);
+          stage_put<128, PHASE == 1>(stg, row, col, silu_f(acc[mi][ni][v]) * acc[mi][ni + NB / 2][v]);
         }
     __syncthreads();
     const int F = a.F;
@@ -1177,7 +1179,7 @@ void gemm_big_kernel(FfnArgs a, int NT, int ncu) {
         for (int v = 0; v < 16; ++v) {
           const int row = wm * WR + mi * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
           const int col = (ni / (NB / 2)) * 128 + wn * (128 / WN) + (ni % (NB / 2)) * 32 + (lane & 31);
-          stage_put<256>(stg, row, col, acc[mi][ni][v]);
+          stage_put<256, false>(stg, row, col, acc[mi][ni][v]);
         }
     __syncthreads();
     const int F = a.F;
@@ -1200,7 +1202,7 @@ void gemm_big_kernel(FfnArgs a, int NT, int ncu) {
         for (int v = 0; v < 16; ++v) {
           const int row = wm * WR + mi * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
           const int col = wn * (kBN2 / WN) + ni * 32 + (lane & 31);
-          stage_put<256>(stg, row, col, acc[mi][ni][v]);
+          stage_put<256, PHASE == 2>(stg, row, col, acc[mi][ni][v]);
         }
     __syncthreads();
     const int ld = a.d;

@@ -20,10 +20,18 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
   return __uint_as_float(static_cast<uint32_t>(h) << 16);
 }
 
-// Round to nearest even (gfx950's v_cvt_pk_bf16_f32, one instruction; the
-// same bits as adding 0x7FFF plus the kept lowest bit for every finite
-// input).
+// Round to nearest even; inputs here are finite.
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+// The same rounding by gfx950's v_cvt_pk_bf16_f32 (one instruction, the
+// same bits for finite inputs).  Used only where it was measured to help:
+// in the grouped GEMM's dH / dX epilogue it made the compiler spill
+// registers (that kernel 60% slower).
+__device__ __forceinline__ uint16_t f32_to_bf16_hw(float f) {
   return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
 
