@@ -86,76 +86,108 @@ __device__ __forceinline__ int tile_seg(int x) { return x & 0xFFFF; }
 __device__ __forceinline__ int tile_gsize(int x) { return (x >> 16) & 15; }
 __device__ __forceinline__ int tile_goff(int x) { return (x >> 20) & 15; }
 
-__global__ __launch_bounds__(kWave) void tile_table_kernel(const int32_t* __restrict__ offsets,
-                                                          int4* __restrict__ tiles,
-                                                          int* __restrict__ ntiles, int E,
-                                                          int Es, int T, int k, int BM,
-                                                          unsigned* __restrict__ sk_count) {
-  // One wavefront; each lane owns up to 5 segments (E + Es <= 272 < 320).
-  const int lane = threadIdx.x;
+constexpr int kTableThreads = 256;
+constexpr int kTableSegs = 5 * kWave;     // E + Es <= 272 segments, five per lane of wave 0
+
+__global__ __launch_bounds__(kTableThreads) void tile_table_kernel(
+    const int32_t* __restrict__ offsets, int4* __restrict__ tiles, int* __restrict__ ntiles,
+    int E, int Es, int T, int k, int BM, unsigned* __restrict__ sk_count) {
+  // Wave 0 counts each segment's tiles (five segments a lane) and scans
+  // them into the segments' first tile indices; then every thread writes
+  // tiles t, t + 256, ..., finding its segment by binary search.  (One
+  // lane writing all the tiles of its segments took 10-15 us.)
+  __shared__ int s_first[kTableSegs + 1];
+  __shared__ int s_row0[kTableSegs], s_row1[kTableSegs];
+  const int tid = threadIdx.x;
   // arrival counters of the split tiles start at zero in every call
   if (sk_count != nullptr)
-    for (int i = lane; i < 2 * kMaxCUs; i += kWave) sk_count[i] = 0u;
+    for (int i = tid; i < 2 * kMaxCUs; i += kTableThreads) sk_count[i] = 0u;
   const int nseg = E + Es;
-  // the lane's segment bounds, loaded together (indices clamped to E, so
-  // every load is in bounds and none waits behind a branch)
-  int o0[5], o1[5];
+  if (tid < kWave) {
+    const int lane = tid;
+    // the lane's segment bounds, loaded together (indices clamped to E, so
+    // every load is in bounds and none waits behind a branch)
+    int o0[5], o1[5];
 #pragma unroll
-  for (int q = 0; q < 5; ++q) {
-    const int s = lane * 5 + q;
-    o0[q] = offsets[min(s, E)];
-    o1[q] = offsets[min(s + 1, E)];
+    for (int q = 0; q < 5; ++q) {
+      const int s = lane * 5 + q;
+      o0[q] = offsets[min(s, E)];
+      o1[q] = offsets[min(s + 1, E)];
+    }
+    int cnt[5];
+    int tot = 0;
+#pragma unroll
+    for (int q = 0; q < 5; ++q) {
+      const int s = lane * 5 + q;
+      int rows = 0;
+      if (s < E) rows = o1[q] - o0[q];
+      else if (s < nseg) rows = T;
+      cnt[q] = (rows + BM - 1) / BM;
+      tot += cnt[q];
+    }
+    int incl = tot;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      const int n = __shfl_up(incl, off, kWave);
+      if (lane >= off) incl += n;
+    }
+    int base = incl - tot;
+#pragma unroll
+    for (int q = 0; q < 5; ++q) {
+      const int s = lane * 5 + q;
+      if (s < nseg) {
+        s_first[s] = base;
+        s_row0[s] = o0[q];
+        s_row1[s] = o1[q];
+      }
+      base += cnt[q];
+    }
+    if (lane == kWave - 1) {
+      s_first[nseg] = incl;
+      *ntiles = incl;
+    }
   }
-  int cnt[5];
-  int tot = 0;
-#pragma unroll
-  for (int q = 0; q < 5; ++q) {
-    const int s = lane * 5 + q;
-    int rows = 0;
-    if (s < E) rows = o1[q] - o0[q];
-    else if (s < nseg) rows = T;
-    cnt[q] = (rows + BM - 1) / BM;
-    tot += cnt[q];
-  }
-  int incl = tot;
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    const int n = __shfl_up(incl, off, kWave);
-    if (lane >= off) incl += n;
-  }
-  int base = incl - tot;
-#pragma unroll
-  for (int q = 0; q < 5; ++q) {
-    const int s = lane * 5 + q;
+  __syncthreads();
+  const int total = s_first[nseg];
+  for (int t = tid; t < total; t += kTableThreads) {
+    // the segment holding tile t: s_first[s] <= t < s_first[s + 1]
+    int lo = 0, hi = nseg;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (s_first[mid] <= t) lo = mid;
+      else hi = mid;
+    }
+    const int s = lo;
+    const int i = t - s_first[s];
+    const int cnt = s_first[s + 1] - s_first[s];
     // the segment's tiles form ng groups of at most kTileGroup, sizes as
     // even as possible (the first rem groups one larger)
-    const int ng = (cnt[q] + kTileGroup - 1) / kTileGroup;
-    const int gs = ng > 0 ? cnt[q] / ng : 0, rem = ng > 0 ? cnt[q] % ng : 0;
-    int g_first = 0, g_size = gs + (rem > 0 ? 1 : 0), g_idx = 0;
-    for (int i = 0; i < cnt[q]; ++i) {
-      if (i == g_first + g_size) {
-        g_first = i;
-        ++g_idx;
-        g_size = gs + (g_idx < rem ? 1 : 0);
-      }
-      int4 t;
-      t.x = s | (g_size << 16) | ((i - g_first) << 20);
-      if (s < E) {
-        const int r0 = o0[q] + i * BM;
-        t.y = r0;
-        t.z = min(BM, o1[q] - r0);
-        t.w = r0;
-      } else {
-        const int m0 = i * BM;
-        t.y = m0;
-        t.z = min(BM, T - m0);
-        t.w = T * k + (s - E) * T + m0;
-      }
-      tiles[base + i] = t;
+    const int ng = (cnt + kTileGroup - 1) / kTileGroup;
+    const int gs = cnt / ng, rem = cnt % ng;
+    const int big = rem * (gs + 1);
+    int g_first, g_size;
+    if (i < big) {
+      g_size = gs + 1;
+      g_first = i / g_size * g_size;
+    } else {
+      g_size = gs;
+      g_first = big + (i - big) / gs * gs;
     }
-    base += cnt[q];
+    int4 tl;
+    tl.x = s | (g_size << 16) | ((i - g_first) << 20);
+    if (s < E) {
+      const int r0 = s_row0[s] + i * BM;
+      tl.y = r0;
+      tl.z = min(BM, s_row1[s] - r0);
+      tl.w = r0;
+    } else {
+      const int m0 = i * BM;
+      tl.y = m0;
+      tl.z = min(BM, T - m0);
+      tl.w = T * k + (s - E) * T + m0;
+    }
+    tiles[t] = tl;
   }
-  if (lane == kWave - 1) *ntiles = incl;
 }
 
 // ------------------------------------------------------------- bf16 MFMA --
@@ -1593,7 +1625,7 @@ hipError_t launch_expert_ffn_train(int64_t T, int64_t d, int E, int E_shared, in
   unsigned* sk_count =
       reinterpret_cast<unsigned*>(sk + static_cast<size_t>(kMaxCUs) * kBM2 * kBN2 * 4);
   void* H = sk + ffn_sk_bytes(2);
-  hipLaunchKernelGGL(tile_table_kernel, dim3(1), dim3(kWave), 0, s, offsets, tiles, ntiles, E,
+  hipLaunchKernelGGL(tile_table_kernel, dim3(1), dim3(kTableThreads), 0, s, offsets, tiles, ntiles, E,
                      E_shared, static_cast<int>(T), k, kBM2, sk_count);
   FfnArgs a{x_perm, x, offsets, w1, w3, w2, ws1, ws3, ws2, H, y_perm, y_shared, tiles, ntiles,
             sk_partial, sk_count,
@@ -1627,7 +1659,7 @@ hipError_t launch_expert_ffn(int64_t T, int64_t d, int E, int E_shared, int k, i
   // decode-sized calls with T <= kStreamMaxRows only stream (no tiles)
   const bool stream_only = bf16 && BM == kBM && T <= kStreamMaxRows;
   if (!stream_only)
-    hipLaunchKernelGGL(tile_table_kernel, dim3(1), dim3(kWave), 0, s, offsets, tiles, ntiles, E,
+    hipLaunchKernelGGL(tile_table_kernel, dim3(1), dim3(kTableThreads), 0, s, offsets, tiles, ntiles, E,
                        E_shared, static_cast<int>(T), k, BM, sk_count);
   FfnArgs a{x_perm, x, offsets, w1, w3, w2, ws1, ws3, ws2, H, y_perm, y_shared, tiles, ntiles,
             sk_partial, sk_count,
@@ -1728,7 +1760,7 @@ hipError_t launch_expert_ffn_backward(int64_t T, int64_t d, int E, int E_shared,
   hipError_t err = hipSuccess;
   auto ok = [&](hipError_t e) { if (err == hipSuccess) err = e; return err == hipSuccess; };
   // tiles of the large-tile kernel (and zeroed split-K counters), segment info
-  hipLaunchKernelGGL(tile_table_kernel, dim3(1), dim3(kWave), 0, s, offsets, tiles, ntiles, E,
+  hipLaunchKernelGGL(tile_table_kernel, dim3(1), dim3(kTableThreads), 0, s, offsets, tiles, ntiles, E,
                      E_shared, static_cast<int>(T), k, kBM2, sk_count);
   ok(launch_seg_info(offsets, poff, hstart, nrows, E, E_shared, T, k, s));
   int ncu = 0;
