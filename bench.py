@@ -40,11 +40,11 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 # and names that summary ("traffic_from"); a changed kernel reports null
 # until it is profiled again.
 MEASURED_TRAFFIC = {
-    ("skewed_train", "bf16", "3c44b6840db72b13"): (3.0962e10, "profiles/moe_layer_skewed_train.md"),
-    ("dsmoe16b_prefill", "bf16", "3c44b6840db72b13"): (2.9426e9, "profiles/moe_layer_dsmoe16b_prefill.md"),
-    ("mixtral_prefill", "bf16", "3c44b6840db72b13"): (8.8912e9, "profiles/moe_layer_mixtral_prefill.md"),
-    ("dsv3_decode", "bf16", "3c44b6840db72b13"): (1.9671e10, "profiles/moe_layer_dsv3_decode.md"),
-    ("dsv3_decode", "fp8", "3c44b6840db72b13"): (9.8259e9, "profiles/moe_layer_dsv3_decode_fp8_weights.md"),
+    ("skewed_train", "bf16", "af12e33b88fb188c"): (3.1008e10, "profiles/moe_layer_skewed_train.md"),
+    ("dsmoe16b_prefill", "bf16", "af12e33b88fb188c"): (2.9193e9, "profiles/moe_layer_dsmoe16b_prefill.md"),
+    ("mixtral_prefill", "bf16", "af12e33b88fb188c"): (8.8628e9, "profiles/moe_layer_mixtral_prefill.md"),
+    ("dsv3_decode", "bf16", "af12e33b88fb188c"): (1.9671e10, "profiles/moe_layer_dsv3_decode.md"),
+    ("dsv3_decode", "fp8", "af12e33b88fb188c"): (9.8258e9, "profiles/moe_layer_dsv3_decode_fp8_weights.md"),
 }
 
 
