@@ -40,11 +40,11 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 # and names that summary ("traffic_from"); a changed kernel reports null
 # until it is profiled again.
 MEASURED_TRAFFIC = {
-    ("skewed_train", "bf16", "af12e33b88fb188c"): (3.1008e10, "profiles/moe_layer_skewed_train.md"),
-    ("dsmoe16b_prefill", "bf16", "af12e33b88fb188c"): (2.9193e9, "profiles/moe_layer_dsmoe16b_prefill.md"),
-    ("mixtral_prefill", "bf16", "af12e33b88fb188c"): (8.8628e9, "profiles/moe_layer_mixtral_prefill.md"),
-    ("dsv3_decode", "bf16", "af12e33b88fb188c"): (1.9671e10, "profiles/moe_layer_dsv3_decode.md"),
-    ("dsv3_decode", "fp8", "af12e33b88fb188c"): (9.8258e9, "profiles/moe_layer_dsv3_decode_fp8_weights.md"),
+    ("skewed_train", "bf16", "a9dfe14a8f4d0ed0"): (3.1008e10, "profiles/moe_layer_skewed_train.md"),
+    ("dsmoe16b_prefill", "bf16", "a9dfe14a8f4d0ed0"): (2.9193e9, "profiles/moe_layer_dsmoe16b_prefill.md"),
+    ("mixtral_prefill", "bf16", "a9dfe14a8f4d0ed0"): (8.8628e9, "profiles/moe_layer_mixtral_prefill.md"),
+    ("dsv3_decode", "bf16", "a9dfe14a8f4d0ed0"): (1.9671e10, "profiles/moe_layer_dsv3_decode.md"),
+    ("dsv3_decode", "fp8", "a9dfe14a8f4d0ed0"): (9.8258e9, "profiles/moe_layer_dsv3_decode_fp8_weights.md"),
 }
 
 

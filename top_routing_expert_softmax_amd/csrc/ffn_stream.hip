@@ -15,9 +15,8 @@
 // steps round robin, so at any moment they read adjacent pieces of every
 // weight row, starting at a per-block rotation of the batch order so that
 // concurrent blocks read different parts of their rows; the four partial
-// sums meet in LDS and are added in wave
-// order (deterministic), then phase 1 applies SiLU(gate) * up and rounds H
-// to bf16.  Segments of a few rows first copy their token rows into the
+// sums meet in LDS and are added in wave order (deterministic), then phase
+// 1 applies SiLU(gate) * up and rounds H to bf16.  Segments of a few rows first copy their token rows into the
 // LDS (stage_rows).
 //
 // Fragments (16 x 16 x 32 MFMA, lane l): the A operand holds token
@@ -96,9 +95,8 @@ __device__ __forceinline__ float silu_s(float g) {
 // the block's indices.  In unrotated order every block of a launch starts
 // at K = 0 and they move through K at about the same pace, so the blocks in
 // flight all read the same narrow column range of their weight rows at
-// once, and their requests pile onto the same memory channels; the rotation
-// spreads them over the whole row (DeepSeek-V3 decode step: bf16 weights
-// 3.31 -> 3.18 ms, FP8 1.733 -> 1.707 ms).  The per-block sum order
+// once; the rotation spreads them over the whole row (DeepSeek-V3 decode
+// step: bf16 weights 3.31 -> 3.18 ms, FP8 1.733 -> 1.707 ms).  The per-block sum order
 // changes with it, fixed for a given launch shape, so results stay
 // deterministic.
 __device__ __forceinline__ int batch_rotation(int nbt) {
