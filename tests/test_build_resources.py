@@ -1,4 +1,4 @@
-"""The hot kernels compile without register spills (CPU only: hipcc
+"""Every kernel compiles without register spills (CPU only: hipcc
 cross-compiles for gfx950 and reports each kernel's resources).
 
 A spill puts scratch loads and stores into a kernel; in the grouped GEMM's
@@ -14,12 +14,10 @@ import pytest
 
 from top_routing_expert_softmax_amd import build as B
 
-# kernel name pattern -> largest scratch (bytes per lane) allowed
+# kernel name pattern -> largest scratch (bytes per lane) allowed; every
+# other kernel: none
 LIMITS = [
     (r"gemm_big_kernelILi4E", 8),
-    (r"gemm_big_kernelILi\dE", 0),
-    (r"gemm_wgrad_kernelILi64ELi5ELi4E", 0),
-    (r"ffn_stream_kernel", 0),
 ]
 
 
@@ -40,14 +38,13 @@ def resources(src):
 
 
 @pytest.mark.skipif(not os.path.exists(B.HIPCC), reason="hipcc not installed")
-@pytest.mark.parametrize("src", ["ffn.hip", "ffn_stream.hip"])
-def test_hot_kernels_do_not_spill(src):
+@pytest.mark.parametrize("src", [os.path.basename(p) for p in B.sources()])
+def test_kernels_do_not_spill(src):
+    with open(os.path.join(B.CSRC, src)) as fh:
+        if "__global__" not in fh.read():
+            pytest.skip("no kernels in this source")
     res = resources(src)
-    checked = 0
+    assert res, f"no kernels reported for {src}"
     for name, scratch in res.items():
-        for pat, limit in LIMITS:
-            if re.search(pat, name):
-                assert scratch <= limit, f"{name}: {scratch} bytes of scratch a lane"
-                checked += 1
-                break
-    assert checked >= (6 if src == "ffn.hip" else 4), res
+        limit = next((lim for pat, lim in LIMITS if re.search(pat, name)), 0)
+        assert scratch <= limit, f"{name}: {scratch} bytes of scratch a lane"
