@@ -87,6 +87,14 @@ SMALL_CASES = {
     # tile holds 64 columns
     "bf16_partial_col_tiles": ("mixtral_prefill", dict(T=600, d_model=320, E=2, k=2, d_ff=192,
                                                        CF=None)),
+    # the most segments the boundary takes (256 routed + 16 shared): the tile
+    # table's per-tile segment search on the 256 x 256 tiles (T k = 64 E:
+    # every routed expert a tail tile, 384 tiles) and on the 128-row tiles
+    # beside the streaming kernels (T = 100: shared segments of 100 rows)
+    "bf16_max_segments_big": ("dsmoe16b_prefill", dict(T=2048, d_model=64, E=256, E_shared=16,
+                                                       k=8, d_ff=64, CF=1.25)),
+    "bf16_max_segments_mixed": ("dsmoe16b_prefill", dict(T=100, d_model=64, E=256, E_shared=16,
+                                                         k=8, d_ff=64, CF=None)),
 }
 
 
